@@ -1,0 +1,206 @@
+// C entry points of libkvq: argument checks on the host, then kernel
+// launches on the caller's stream.  Nothing here allocates device memory or
+// synchronises.
+#include <cmath>
+#include <cstdio>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+
+float fwht_norm(int d) { return (float)(1.0 / std::sqrt((double)d)); }
+
+namespace {
+
+thread_local hipError_t g_last_hip = hipSuccess;
+thread_local char g_msg[256];
+
+bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+// Validate a description; fills geometry.  Pointers are checked by callers
+// that use them.
+int check_desc(const kvq_cache_desc* d, CacheGeom* g) {
+  if (!d) return KVQ_ERR_NULL;
+  if (d->format != KVQ_FMT_FP4_E2M1 && d->format != KVQ_FMT_FP8_E4M3) return KVQ_ERR_FORMAT;
+  if (d->num_kv_heads <= 0 || d->num_pages <= 0 || d->head_dim <= 0 || d->page_size <= 0)
+    return KVQ_ERR_SHAPE;
+  if (!pow2(d->head_dim) || d->head_dim < 32 || d->head_dim > 1024) return KVQ_ERR_SHAPE;
+  if (d->page_size != 16 && d->page_size != 32 && d->page_size != 64) return KVQ_ERR_UNSUPPORTED;
+  if (d->rotate != 0 && d->rotate != 1) return KVQ_ERR_SHAPE;
+  if (d->kv_shared != 0 && d->kv_shared != 1) return KVQ_ERR_SHAPE;
+  g->fmt = d->format;
+  g->rotate = d->rotate;
+  g->kv_shared = d->kv_shared;
+  g->hkv = d->num_kv_heads;
+  g->d = d->head_dim;
+  g->g = d->head_dim / 32;
+  g->p = d->page_size;
+  g->num_pages = d->num_pages;
+  g->cb = (d->format == KVQ_FMT_FP4_E2M1) ? 16 : 32;
+  g->c_head = (int64_t)g->g * g->p * g->cb;
+  g->c_page = (int64_t)g->hkv * g->c_head;
+  g->s_head = (int64_t)g->g * g->p;
+  g->s_page = (int64_t)g->hkv * g->s_head;
+  g->kc = (const uint8_t*)d->k_codes;
+  g->ks = (const uint8_t*)d->k_scales;
+  g->vc = (const uint8_t*)d->v_codes;
+  g->vs = (const uint8_t*)d->v_scales;
+  return KVQ_OK;
+}
+
+int check_cache_ptrs(const kvq_cache_desc* d) {
+  if (!d->k_codes || !d->k_scales) return KVQ_ERR_NULL;
+  if (!d->kv_shared && (!d->v_codes || !d->v_scales)) return KVQ_ERR_NULL;
+  return KVQ_OK;
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return KVQ_OK;
+  g_last_hip = e;
+  return KVQ_ERR_HIP;
+}
+
+int decode_common(int want_fmt, const kvq_cache_desc* desc, const void* q, int32_t batch,
+                  int32_t num_q_heads, int32_t n_q, const int32_t* block_tables,
+                  int32_t max_pages_per_seq, const int32_t* context_lens, int32_t max_context_len,
+                  float sm_scale, uint32_t flags, float* out, void* workspace,
+                  size_t workspace_bytes, kvq_stream_t stream) {
+  CacheGeom g;
+  int st = check_desc(desc, &g);
+  if (st != KVQ_OK) return st;
+  if (g.fmt != want_fmt) return KVQ_ERR_FORMAT;
+  st = check_cache_ptrs(desc);
+  if (st != KVQ_OK) return st;
+  if (!q || !block_tables || !context_lens || !out) return KVQ_ERR_NULL;
+  if (batch < 0 || num_q_heads <= 0 || n_q < 1 || max_pages_per_seq <= 0 || max_context_len < 0)
+    return KVQ_ERR_SHAPE;
+  if (num_q_heads % g.hkv != 0) return KVQ_ERR_SHAPE;
+  if ((int64_t)max_pages_per_seq * g.p < (int64_t)max_context_len) return KVQ_ERR_SHAPE;
+  if (!std::isfinite(sm_scale)) return KVQ_ERR_SHAPE;
+  if (flags & ~(KVQ_Q_PREROTATED | KVQ_OUT_ROTATED | KVQ_SPLITS_MASK)) return KVQ_ERR_SHAPE;
+  if (batch == 0 || max_context_len == 0) {
+    // Nothing to attend to: every position sees no token and gets zeros.
+    if (batch == 0) return KVQ_OK;
+  }
+  DecodePlan plan;
+  st = plan_decode(g, batch, num_q_heads, n_q, max_context_len > 0 ? max_context_len : 1, flags, &plan);
+  if (st != KVQ_OK) return st;
+  if (plan.workspace > 0 && (!workspace || workspace_bytes < plan.workspace)) return KVQ_ERR_WORKSPACE;
+  DecodeArgs a;
+  a.c = g;
+  a.plan = plan;
+  a.q = (const uint16_t*)q;
+  a.batch = batch;
+  a.hq = num_q_heads;
+  a.n_q = n_q;
+  a.group = num_q_heads / g.hkv;
+  a.block_tables = block_tables;
+  a.max_pages = max_pages_per_seq;
+  a.context_lens = context_lens;
+  a.qscale = (float)((double)sm_scale * 1.4426950408889634);  // log2(e)
+  a.rotate_q = g.rotate && !(flags & KVQ_Q_PREROTATED);
+  a.rotate_out = g.rotate && !(flags & KVQ_OUT_ROTATED);
+  a.out = out;
+  a.workspace = (float*)workspace;
+  return hip_status(launch_decode(a, (hipStream_t)stream));
+}
+
+}  // namespace
+}  // namespace kvq
+
+using namespace kvq;
+
+extern "C" {
+
+size_t kvq_cache_code_bytes(const kvq_cache_desc* desc) {
+  CacheGeom g;
+  if (check_desc(desc, &g) != KVQ_OK) return 0;
+  return (size_t)g.c_page * (size_t)g.num_pages;
+}
+
+size_t kvq_cache_scale_bytes(const kvq_cache_desc* desc) {
+  CacheGeom g;
+  if (check_desc(desc, &g) != KVQ_OK) return 0;
+  return (size_t)g.s_page * (size_t)g.num_pages;
+}
+
+int kvq_rotate_quantize_append(const kvq_cache_desc* desc, const void* k_new, const void* v_new,
+                               const int32_t* slot_mapping, int32_t n_tokens, kvq_stream_t stream) {
+  CacheGeom g;
+  int st = check_desc(desc, &g);
+  if (st != KVQ_OK) return st;
+  st = check_cache_ptrs(desc);
+  if (st != KVQ_OK) return st;
+  if (n_tokens < 0) return KVQ_ERR_SHAPE;
+  if (n_tokens == 0) return KVQ_OK;
+  if (!k_new || !slot_mapping) return KVQ_ERR_NULL;
+  if (!g.kv_shared && !v_new) return KVQ_ERR_NULL;
+  return hip_status(launch_append(g, (uint8_t*)desc->k_codes, (uint8_t*)desc->k_scales,
+                                  (uint8_t*)desc->v_codes, (uint8_t*)desc->v_scales,
+                                  (const uint16_t*)k_new, (const uint16_t*)v_new, slot_mapping,
+                                  n_tokens, (hipStream_t)stream));
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_cache_desc* desc, int32_t batch, int32_t num_q_heads,
+                                  int32_t n_q, int32_t max_context_len, uint32_t flags) {
+  CacheGeom g;
+  if (check_desc(desc, &g) != KVQ_OK) return 0;
+  if (batch <= 0 || num_q_heads <= 0 || n_q < 1 || max_context_len <= 0) return 0;
+  if (num_q_heads % g.hkv != 0) return 0;
+  DecodePlan plan;
+  if (plan_decode(g, batch, num_q_heads, n_q, max_context_len, flags, &plan) != KVQ_OK) return 0;
+  return plan.workspace;
+}
+
+int kvq_decode_attn_fp4(const kvq_cache_desc* desc, const void* q, int32_t batch,
+                        int32_t num_q_heads, int32_t n_q, const int32_t* block_tables,
+                        int32_t max_pages_per_seq, const int32_t* context_lens,
+                        int32_t max_context_len, float sm_scale, uint32_t flags, float* out,
+                        void* workspace, size_t workspace_bytes, kvq_stream_t stream) {
+  return decode_common(KVQ_FMT_FP4_E2M1, desc, q, batch, num_q_heads, n_q, block_tables,
+                       max_pages_per_seq, context_lens, max_context_len, sm_scale, flags, out,
+                       workspace, workspace_bytes, stream);
+}
+
+int kvq_decode_attn_fp8(const kvq_cache_desc* desc, const void* q, int32_t batch,
+                        int32_t num_q_heads, int32_t n_q, const int32_t* block_tables,
+                        int32_t max_pages_per_seq, const int32_t* context_lens,
+                        int32_t max_context_len, float sm_scale, uint32_t flags, float* out,
+                        void* workspace, size_t workspace_bytes, kvq_stream_t stream) {
+  return decode_common(KVQ_FMT_FP8_E4M3, desc, q, batch, num_q_heads, n_q, block_tables,
+                       max_pages_per_seq, context_lens, max_context_len, sm_scale, flags, out,
+                       workspace, workspace_bytes, stream);
+}
+
+int kvq_dequant(const kvq_cache_desc* desc, const int32_t* slots, int32_t n, float* k_out,
+                float* v_out, kvq_stream_t stream) {
+  CacheGeom g;
+  int st = check_desc(desc, &g);
+  if (st != KVQ_OK) return st;
+  st = check_cache_ptrs(desc);
+  if (st != KVQ_OK) return st;
+  if (n < 0) return KVQ_ERR_SHAPE;
+  if (n == 0) return KVQ_OK;
+  if (!slots || !k_out) return KVQ_ERR_NULL;
+  if (!g.kv_shared && !v_out) return KVQ_ERR_NULL;
+  return hip_status(launch_dequant(g, slots, n, k_out, v_out, (hipStream_t)stream));
+}
+
+const char* kvq_strerror(int status) {
+  switch (status) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_NULL: return "a required pointer is NULL";
+    case KVQ_ERR_SHAPE: return "a size is non-positive or inconsistent";
+    case KVQ_ERR_FORMAT: return "cache format does not match the call";
+    case KVQ_ERR_UNSUPPORTED: return "no kernel is built for this shape";
+    case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case KVQ_ERR_HIP:
+      snprintf(g_msg, sizeof g_msg, "HIP error: %s", hipGetErrorString(g_last_hip));
+      return g_msg;
+    default: return "unknown status";
+  }
+}
+
+int kvq_version(void) { return KVQ_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,75 @@
+// Internal declarations shared by the translation units of libkvq.
+// Host-side launchers take already-validated arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "kvq.h"
+
+namespace kvq {
+
+// Geometry of one paged cache, derived from kvq_cache_desc (byte strides).
+struct CacheGeom {
+  const uint8_t* kc;
+  const uint8_t* ks;
+  const uint8_t* vc;
+  const uint8_t* vs;
+  int fmt;          // KVQ_FMT_*
+  int rotate;
+  int kv_shared;
+  int hkv;
+  int d;            // head_dim
+  int g;            // head_dim / 32
+  int p;            // page_size
+  int num_pages;
+  int cb;           // code bytes per (token, group): 16 (FP4) or 32 (FP8)
+  int64_t c_head;   // code bytes per (page, head)  = g * p * cb
+  int64_t c_page;   // code bytes per page          = hkv * c_head
+  int64_t s_head;   // scale bytes per (page, head) = g * p
+  int64_t s_page;   // scale bytes per page         = hkv * s_head
+};
+
+// fp32 rounding of 1/sqrt(d): the single multiply after the butterfly.
+float fwht_norm(int d);
+
+hipError_t launch_append(const CacheGeom& c, uint8_t* kc, uint8_t* ks,
+                         uint8_t* vc, uint8_t* vs, const uint16_t* k_new,
+                         const uint16_t* v_new, const int32_t* slots,
+                         int n_tokens, hipStream_t stream);
+
+hipError_t launch_dequant(const CacheGeom& c, const int32_t* slots, int n,
+                          float* k_out, float* v_out, hipStream_t stream);
+
+struct DecodePlan {
+  int rows;              // query rows per KV head = n_q * group
+  int row_tiles;         // 8-row tiles (hi/lo split fills a 16-wide MFMA)
+  int splits;            // context splits per (sequence, KV head)
+  int tiles_per_split;   // 16-token tiles per split (even)
+  size_t workspace;      // bytes
+};
+
+// Decide split count and workspace size; returns KVQ_OK or an error code.
+int plan_decode(const CacheGeom& c, int batch, int hq, int n_q,
+                int max_context_len, uint32_t flags, DecodePlan* plan);
+
+struct DecodeArgs {
+  CacheGeom c;
+  DecodePlan plan;
+  const uint16_t* q;
+  int batch, hq, n_q, group;
+  const int32_t* block_tables;
+  int max_pages;
+  const int32_t* context_lens;
+  float qscale;      // sm_scale * log2(e)
+  int rotate_q;      // rotate the query inside the kernel
+  int rotate_out;    // rotate the output back inside the kernel
+  float* out;
+  float* workspace;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace kvq

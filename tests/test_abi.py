@@ -1,0 +1,136 @@
+"""libkvq's C interface on the host: the library loads, exports every
+function include/kvq.h declares, sizes its buffers as documented, and rejects
+bad arguments with the documented status before any HIP call.  No GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import bit_quantized_kv_rotate_amd as kvq
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "kvq.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert declared_functions() == sorted(kvq.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    L = kvq.library()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+    assert L.kvq_version() == 1
+
+
+def _desc(fmt=1, hkv=8, d=128, p=16, pages=10, rotate=1, shared=0, ptrs=True):
+    x = ctypes.c_void_p(0x1000) if ptrs else None
+    return kvq.CacheDesc(fmt, rotate, shared, hkv, d, p, pages, x, x, x, x)
+
+
+def test_cache_sizes_match_documented_layout():
+    L = kvq.library()
+    d = _desc(fmt=1, hkv=8, d=128, p=16, pages=10)
+    # FP4: 16 code bytes + 1 scale byte per (token, group): 17 per 32 values
+    assert L.kvq_cache_code_bytes(ctypes.byref(d)) == 10 * 8 * 4 * 16 * 16
+    assert L.kvq_cache_scale_bytes(ctypes.byref(d)) == 10 * 8 * 4 * 16
+    d8 = _desc(fmt=2, hkv=1, d=512, p=64, pages=3)
+    assert L.kvq_cache_code_bytes(ctypes.byref(d8)) == 3 * 1 * 16 * 64 * 32
+    assert L.kvq_cache_scale_bytes(ctypes.byref(d8)) == 3 * 16 * 64
+    per_group = (L.kvq_cache_code_bytes(ctypes.byref(d)) + L.kvq_cache_scale_bytes(ctypes.byref(d))) \
+        / (10 * 8 * 16 * 4)
+    assert per_group == 17
+
+
+@pytest.mark.parametrize("kw", [dict(d=96), dict(d=16), dict(d=2048), dict(hkv=0), dict(pages=0)])
+def test_bad_geometry_sizes_zero(kw):
+    d = _desc(**kw)
+    assert kvq.library().kvq_cache_code_bytes(ctypes.byref(d)) == 0
+
+
+def test_strerror_texts():
+    for st in (0, -1, -2, -3, -4, -5, -6):
+        assert kvq.strerror(st)
+    assert "HIP" in kvq.strerror(-6)
+
+
+def _append(desc, k=0x2000, v=0x3000, slots=0x4000, n=4):
+    return kvq.library().kvq_rotate_quantize_append(ctypes.byref(desc) if desc is not None else None,
+                                                    k, v, slots, n, None)
+
+
+def test_append_argument_errors():
+    assert _append(None) == -1
+    assert _append(_desc(ptrs=False)) == -1
+    assert _append(_desc(), k=None) == -1
+    assert _append(_desc(), v=None) == -1
+    assert _append(_desc(), slots=None) == -1
+    assert _append(_desc(), n=-1) == -2
+    assert _append(_desc(), n=0) == 0            # nothing to do, no HIP call
+    assert _append(_desc(d=96)) == -2
+    assert _append(_desc(p=24)) == -4
+    assert _append(_desc(fmt=7)) == -3
+    assert _append(_desc(rotate=2)) == -2
+
+
+def _decode(fn="kvq_decode_attn_fp4", desc=None, q=0x10, B=2, hq=16, n_q=1, bt=0x20, maxp=8,
+            cl=0x30, maxl=128, sm=0.1, flags=0, out=0x40, ws=0x50, wsb=1 << 30):
+    if desc is None:
+        desc = _desc(fmt=1 if fn.endswith("fp4") else 2)
+    return getattr(kvq.library(), fn)(ctypes.byref(desc), q, B, hq, n_q, bt, maxp, cl, maxl,
+                                      sm, flags, out, ws, wsb, None)
+
+
+def test_decode_argument_errors():
+    assert _decode(q=None) == -1
+    assert _decode(bt=None) == -1
+    assert _decode(cl=None) == -1
+    assert _decode(out=None) == -1
+    assert _decode(desc=_desc(ptrs=False)) == -1
+    assert _decode(hq=12) == -2                  # not a multiple of num_kv_heads
+    assert _decode(n_q=0) == -2
+    assert _decode(maxp=4, maxl=128) == -2       # 4 pages of 16 cannot hold 128 tokens
+    assert _decode(sm=float("inf")) == -2
+    assert _decode(flags=0x4) == -2
+    assert _decode(desc=_desc(fmt=2)) == -3      # FP4 entry point, FP8 cache
+    assert _decode(fn="kvq_decode_attn_fp8", desc=_desc(fmt=1)) == -3
+    assert _decode(desc=_desc(d=64)) == -4       # no kernel for head_dim 64 yet
+    assert _decode(hq=8 * 32) == -4              # 32 rows per KV head: not built
+    assert _decode(B=0) == 0                     # empty batch: nothing enqueued
+
+
+def test_decode_workspace_checks():
+    L = kvq.library()
+    d = _desc()
+    need = L.kvq_decode_workspace_bytes(ctypes.byref(d), 32, 64, 1, 32768, 0)
+    assert need > 0
+    assert _decode(B=32, hq=64, maxp=2048, maxl=32768, ws=None, wsb=0) == -5
+    assert _decode(B=32, hq=64, maxp=2048, maxl=32768, ws=0x50, wsb=need - 1) == -5
+    # one forced split needs no workspace
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 32, 64, 1, 32768, kvq.splits_flag(1)) == 0
+
+
+def test_dequant_argument_errors():
+    L = kvq.library()
+    d = _desc()
+    assert L.kvq_dequant(ctypes.byref(d), None, 3, 0x10, 0x20, None) == -1
+    assert L.kvq_dequant(ctypes.byref(d), 0x10, 3, None, 0x20, None) == -1
+    assert L.kvq_dequant(ctypes.byref(d), 0x10, 3, 0x10, None, None) == -1
+    assert L.kvq_dequant(ctypes.byref(d), 0x10, -1, 0x10, 0x20, None) == -2
+    assert L.kvq_dequant(ctypes.byref(d), 0x10, 0, 0x10, 0x20, None) == 0
+
+
+def test_binding_has_no_oracle_dependency():
+    """The product package must not import or call the test oracle."""
+    pkg = os.path.dirname(kvq.__file__)
+    for root, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(root, f)).read()
+                assert "oracle" not in text.lower().replace("no cpu fallback", ""), f

@@ -1,0 +1,155 @@
+"""Decode attention on the GPU against the oracle (fp64 attention over the
+oracle's own quantisation of the same bf16 inputs): max |err| <= 2e-3 and
+relative L2 <= 1e-3 over every output, plus invariances that hold at any
+size (split count, page permutation, flags)."""
+import dataclasses
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_kv_rotate_amd as kvq
+import kvq_synth as syn
+import oracle
+from kvq_gpu_util import Filled, assert_close, oracle_decode_batch, to_dev_i32
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(wl, fmt, flags=0, gen_device="cpu", rotate=None):
+    f = Filled(wl, fmt, gen_device=gen_device, rotate=rotate)
+    q = syn.queries(wl, gen_device)
+    out = f.decode(q.cuda(), flags=flags).cpu().numpy()
+    return f, syn.bf16_bits(q), out
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "fp8"])
+def test_decode_tiny(gpu, fmt):
+    wl = syn.WORKLOADS["tiny_b1_l256"]
+    f, qh, out = _run(wl, fmt)
+    want = oracle_decode_batch(f, qh)
+    print("tiny", fmt, assert_close(out[0], want[0], "tiny %s" % fmt))
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "fp8"])
+def test_decode_b8_l8k(gpu, fmt):
+    wl = syn.WORKLOADS["b8_l8k"]
+    f, qh, out = _run(wl, fmt)
+    want = oracle_decode_batch(f, qh)
+    got = np.stack([out[b] for b in range(wl.batch)])
+    ref = np.stack([want[b] for b in range(wl.batch)])
+    print("b8_l8k", fmt, assert_close(got, ref, "b8_l8k %s" % fmt))
+
+
+@pytest.mark.parametrize("group,n_q", [(1, 1), (2, 1), (4, 1), (8, 1), (16, 1), (1, 3), (4, 3), (8, 3), (2, 5)])
+def test_decode_query_groups_and_mtp(gpu, group, n_q):
+    wl = syn.Workload("grp%d_nq%d" % (group, n_q), batch=3, num_kv_heads=2, num_q_heads=2 * group,
+                      head_dim=128, page_size=16, context=0, n_q=n_q, ctx_range=(40, 700))
+    f, qh, out = _run(wl, "fp4")
+    want = oracle_decode_batch(f, qh)
+    for b in range(wl.batch):
+        assert_close(out[b], want[b], "g%d n_q%d seq %d" % (group, n_q, b))
+
+
+def test_decode_ragged_contexts(gpu):
+    """Contexts that end anywhere inside a tile, tile pair or page, and a
+    single token."""
+    lens = [1, 2, 15, 16, 17, 31, 32, 33, 47, 100, 129, 255]
+    wl = syn.Workload("ragged", batch=len(lens), num_kv_heads=2, num_q_heads=16, head_dim=128,
+                      page_size=16, context=1)
+    plan = syn.page_plan(dataclasses.replace(wl, context=256))
+    plan.context_lens = np.array(lens, dtype=np.int32)
+    f = Filled(wl, "fp4", plan=plan)
+    q = syn.queries(wl)
+    out = f.decode(q.cuda()).cpu().numpy()
+    want = oracle_decode_batch(f, syn.bf16_bits(q))
+    for b in range(wl.batch):
+        assert_close(out[b], want[b], "len %d" % lens[b])
+
+
+def test_decode_shared_prefix_mtp_small(gpu):
+    """Shared-prefix block tables and 3 verify positions (a scaled-down
+    version of the agentic mix)."""
+    wl = syn.Workload("mtp_small", batch=6, num_kv_heads=2, num_q_heads=16, head_dim=128,
+                      page_size=16, context=0, n_q=3, ctx_range=(64, 2048), n_prefixes=2,
+                      shared_frac=0.92)
+    f, qh, out = _run(wl, "fp4")
+    want = oracle_decode_batch(f, qh)
+    for b in range(wl.batch):
+        assert_close(out[b], want[b], "seq %d" % b)
+
+
+@pytest.mark.parametrize("page_size", [32, 64])
+def test_decode_page_sizes(gpu, page_size):
+    wl = syn.Workload("pages%d" % page_size, batch=2, num_kv_heads=2, num_q_heads=16, head_dim=128,
+                      page_size=page_size, context=0, ctx_range=(100, 900))
+    f, qh, out = _run(wl, "fp4")
+    want = oracle_decode_batch(f, qh)
+    for b in range(wl.batch):
+        assert_close(out[b], want[b], "P%d seq %d" % (page_size, b))
+
+
+def test_decode_split_count_invariance(gpu):
+    wl = syn.WORKLOADS["tiny_b1_l256"]
+    f = Filled(wl, "fp4")
+    q = syn.queries(wl).cuda()
+    ref = f.decode(q, flags=kvq.splits_flag(1)).cpu().numpy()
+    for s in (2, 3, 5, 8, 16):
+        got = f.decode(q, flags=kvq.splits_flag(s)).cpu().numpy()
+        np.testing.assert_allclose(got, ref, rtol=0, atol=2e-5)
+    want = oracle_decode_batch(f, syn.bf16_bits(q))
+    assert_close(ref[0], want[0], "one split")
+
+
+def test_decode_page_permutation_invariance(gpu):
+    wl = syn.WORKLOADS["tiny_b1_l256"]
+    a = Filled(wl, "fp4")
+    b = Filled(dataclasses.replace(wl, permute_pages=True), "fp4")
+    q = syn.queries(wl).cuda()
+    assert not np.array_equal(a.plan.block_tables, b.plan.block_tables)
+    np.testing.assert_array_equal(a.decode(q).cpu().numpy(), b.decode(q).cpu().numpy())
+
+
+def test_decode_rotation_flags(gpu):
+    """KVQ_Q_PREROTATED and KVQ_OUT_ROTATED: the caller folds H into q or
+    the output; the fp32 transform of the oracle supplies the reference."""
+    wl = syn.WORKLOADS["tiny_b1_l256"]
+    f = Filled(wl, "fp4")
+    q = syn.queries(wl)
+    qh = syn.bf16_bits(q)
+    base = f.decode(q.cuda()).cpu().numpy()
+    out_rot = f.decode(q.cuda(), flags=kvq.OUT_ROTATED).cpu().numpy()
+    assert_close(oracle.fwht_f64(out_rot.astype(np.float64)), base, "OUT_ROTATED")
+    # a pre-rotated query: rotate in fp32, round to bf16 (the caller's choice)
+    qf = q.float().numpy()
+    qrot = torch.from_numpy(oracle.fwht_f32(qf)).to(torch.bfloat16)
+    got = f.decode(qrot.cuda(), flags=kvq.Q_PREROTATED).cpu().numpy()
+    sm = 1 / math.sqrt(128)
+    kc, ks = oracle.quantize_fp4(f.host["k"][0], True)
+    vc, vs = oracle.quantize_fp4(f.host["v"][0], True)
+    khat, vhat = oracle.dequant_fp4(kc, ks), oracle.dequant_fp4(vc, vs)
+    qr = syn.bf16_bits(qrot)[0].astype(np.uint32)
+    qr64 = (qr << 16).astype(np.uint32).view(np.float32).astype(np.float64)
+    want = oracle.fwht_f64(oracle.attend(qr64, khat, vhat, sm))
+    assert_close(got[0], want, "Q_PREROTATED")
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "fp8"])
+def test_decode_empty_context_gives_zeros(gpu, fmt):
+    wl = syn.WORKLOADS["tiny_b1_l256"]
+    f = Filled(wl, fmt)
+    q = syn.queries(wl).cuda()
+    zero = to_dev_i32([0])
+    fn = kvq.decode_attn_fp4 if fmt == "fp4" else kvq.decode_attn_fp8
+    out = fn(f.cache, q, f.block_tables, zero, 0)
+    assert torch.count_nonzero(out).item() == 0
+
+
+def test_decode_repeatable(gpu):
+    wl = syn.WORKLOADS["b8_l8k"]
+    f = Filled(wl, "fp4", keep_host=False)
+    q = syn.queries(wl).cuda()
+    a = f.decode(q)
+    b = f.decode(q)
+    assert torch.equal(a, b)

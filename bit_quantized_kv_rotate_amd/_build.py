@@ -28,7 +28,9 @@ COMMON = [
 SOURCES = {
     "kvq_api.hip": [],
     "kvq_append.hip": ["-ffp-contract=off"],
-    "kvq_decode.hip": [],
+    # keep MFMA accumulators in VGPRs: the softmax rescale touches them with
+    # VALU ops, and AGPR placement costs a copy per access
+    "kvq_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -86,6 +86,7 @@ int decode_common(int want_fmt, const kvq_cache_desc* desc, const void* q, int32
   st = plan_decode(g, batch, num_q_heads, n_q, max_context_len > 0 ? max_context_len : 1, flags, &plan);
   if (st != KVQ_OK) return st;
   if (plan.workspace > 0 && (!workspace || workspace_bytes < plan.workspace)) return KVQ_ERR_WORKSPACE;
+  if ((uintptr_t)workspace & 15u) return KVQ_ERR_WORKSPACE;
   DecodeArgs a;
   a.c = g;
   a.plan = plan;
@@ -145,10 +146,12 @@ size_t kvq_decode_workspace_bytes(const kvq_cache_desc* desc, int32_t batch, int
                                   int32_t n_q, int32_t max_context_len, uint32_t flags) {
   CacheGeom g;
   if (check_desc(desc, &g) != KVQ_OK) return 0;
-  if (batch <= 0 || num_q_heads <= 0 || n_q < 1 || max_context_len <= 0) return 0;
+  if (batch <= 0 || num_q_heads <= 0 || n_q < 1 || max_context_len < 0) return 0;
   if (num_q_heads % g.hkv != 0) return 0;
   DecodePlan plan;
-  if (plan_decode(g, batch, num_q_heads, n_q, max_context_len, flags, &plan) != KVQ_OK) return 0;
+  // the decode call plans a context of at least one token, as here
+  if (plan_decode(g, batch, num_q_heads, n_q, max_context_len > 0 ? max_context_len : 1, flags, &plan) != KVQ_OK)
+    return 0;
   return plan.workspace;
 }
 

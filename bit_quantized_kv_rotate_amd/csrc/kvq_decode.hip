@@ -66,8 +66,9 @@ struct DecodeParams {
   int rotate_q, rotate_out;
   int splits, tiles_per_split;
   float* out;
-  float* ws_o;   // [B][hkv][splits][8*NT][kD]
-  float* ws_ml;  // [B][hkv][splits][8*NT][2]
+  float* ws_o;       // [B][hkv][splits][8*NT][kD]
+  float* ws_ml;      // [B][hkv][splits][8*NT][2]
+  uint32_t* qops;    // [B][hkv][NT][QOpsLayout::kSlots][64 lanes][kDwords]
 };
 
 template <int FMT>
@@ -89,6 +90,15 @@ struct QOps<KVQ_FMT_FP4_E2M1, NT> {
 template <int NT>
 struct QOps<KVQ_FMT_FP8_E4M3, NT> {
   bf16x8_t b[NT][4];
+};
+
+// Workspace image of the query operands: per (sequence, KV head, row tile)
+// kSlots operands of kDwords per lane (FP4: 6 packed FP6 dwords + scale +
+// pad; FP8: one bf16x8 = 4 dwords).
+template <int FMT>
+struct QOpsLayout {
+  static constexpr int kSlots = (FMT == KVQ_FMT_FP4_E2M1) ? kQMfma : 4;
+  static constexpr int kDwords = (FMT == KVQ_FMT_FP4_E2M1) ? 8 : 4;
 };
 
 // Dequantise one (token, 32-channel group) into 16 packed bf16x2 words
@@ -176,35 +186,53 @@ struct RawTile {
   uint32_t ksc, vsc;
 };
 
+// Per-lane byte offsets inside one (page, KV head) block, fixed for the
+// whole scan: lane l reads token l%16 (of a 16-token tile) in group l/16.
+struct LaneOffsets {
+  uint32_t code;   // into the code block
+  uint32_t scale;  // into the scale block
+};
+
+template <int FMT>
+__device__ __forceinline__ LaneOffsets lane_offsets(const DecodeParams& p, int lane) {
+  constexpr int kBytes = Fmt<FMT>::kWords * 4;
+  const uint32_t idx = (uint32_t)((lane >> 4) * p.P + (lane & 15));
+  return LaneOffsets{idx * kBytes, idx};
+}
+
+// Buffer resource over one (page, KV head) block: loads through it take a
+// scalar base, a scalar in-page offset and the lane's constant offset, and
+// reads past the block return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t* base, int64_t off,
+                                                             int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(base + off), 0, (int)bytes, 0x00020000);
+}
+
+// Loads of one 16-token tile (all addressing scalar except the lane offset).
 template <int FMT>
 __device__ __forceinline__ void load_tile(const DecodeParams& p, const int32_t* bt_row, int kvh,
-                                          int tile, int lane, RawTile<FMT>& t) {
+                                          int tile, const LaneOffsets& lo, RawTile<FMT>& t) {
+  constexpr int kBytes = Fmt<FMT>::kWords * 4;
   const int tok = tile * 16;
-  const int page = bt_row[tok >> p.p_shift];
-  const int off = (tok & (p.P - 1)) + (lane & 15);
-  const int grp = lane >> 4;
-  const int64_t head = (int64_t)page * p.c_page + (int64_t)kvh * p.c_head;
-  const int64_t sidx = (int64_t)page * p.s_page + (int64_t)kvh * p.s_head + (int64_t)grp * p.P + off;
-  if constexpr (Fmt<FMT>::kFP4) {
-    const int64_t cidx = head + ((int64_t)grp * p.P + off) * 16;
-    const u32x4_t a = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p.kc + cidx));
-    const u32x4_t c = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p.vc + cidx));
+  const int page = __builtin_amdgcn_readfirstlane(bt_row[tok >> p.p_shift]);
+  const int in_page = tok & (p.P - 1);
+  const int64_t cb = (int64_t)page * p.c_page + (int64_t)kvh * p.c_head;
+  const int64_t sb = (int64_t)page * p.s_page + (int64_t)kvh * p.s_head;
+  const __amdgpu_buffer_rsrc_t rk = block_rsrc(p.kc, cb, p.c_head);
+  const __amdgpu_buffer_rsrc_t rv = block_rsrc(p.vc, cb, p.c_head);
+  const __amdgpu_buffer_rsrc_t rks = block_rsrc(p.ks, sb, p.s_head);
+  const __amdgpu_buffer_rsrc_t rvs = block_rsrc(p.vs, sb, p.s_head);
+  const int coff = in_page * kBytes;
+  // slc (bit 1 of aux): streaming, the codes are read once per step
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { t.k[i] = a[i]; t.v[i] = c[i]; }
-  } else {
-    const int64_t cidx = head + ((int64_t)grp * p.P + off) * 32;
-    const u32x4_t a0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p.kc + cidx));
-    const u32x4_t a1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p.kc + cidx + 16));
-    const u32x4_t c0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p.vc + cidx));
-    const u32x4_t c1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p.vc + cidx + 16));
+  for (int i = 0; i < kBytes / 16; ++i) {
+    const u32x4_t a = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)lo.code + 16 * i, coff, 2));
+    const u32x4_t c = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)lo.code + 16 * i, coff, 2));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      t.k[i] = a0[i]; t.k[4 + i] = a1[i];
-      t.v[i] = c0[i]; t.v[4 + i] = c1[i];
-    }
+    for (int w = 0; w < 4; ++w) { t.k[4 * i + w] = a[w]; t.v[4 * i + w] = c[w]; }
   }
-  t.ksc = p.ks[sidx];
-  t.vsc = p.vs[sidx];
+  t.ksc = __builtin_amdgcn_raw_buffer_load_b8(rks, (int)lo.scale, in_page, 0);
+  t.vsc = __builtin_amdgcn_raw_buffer_load_b8(rvs, (int)lo.scale, in_page, 0);
 }
 
 // Per-wave softmax / accumulator state.
@@ -217,21 +245,25 @@ struct WaveState {
 
 template <int FMT>
 __device__ __forceinline__ void issue_pair(const DecodeParams& p, const int32_t* bt_row, int kvh,
-                                           int tile, int t_end, int lane, RawTile<FMT> (&r)[2]) {
-  load_tile<FMT>(p, bt_row, kvh, min(tile, t_end - 1), lane, r[0]);
-  load_tile<FMT>(p, bt_row, kvh, min(tile + 1, t_end - 1), lane, r[1]);
+                                           int tile, int t_end, const LaneOffsets& lo,
+                                           RawTile<FMT> (&r)[2]) {
+  load_tile<FMT>(p, bt_row, kvh, min(tile, t_end - 1), lo, r[0]);
+  load_tile<FMT>(p, bt_row, kvh, min(tile + 1, t_end - 1), lo, r[1]);
 }
 
 // One pair of 16-token tiles: scores, V staging, softmax update, PV.
 // Once the codes of `r` are consumed, the loads of tile pair `refill` are
 // issued into the same registers (clamped to the split's last tile).
-template <int FMT, int NT>
+// Boundary pairs (the split's last tokens, padding pairs, MTP verify
+// tokens) mask scores and clear values of tokens past the end; interior
+// pairs skip all of that.
+template <int FMT, int NT, bool Boundary>
 __device__ __forceinline__ void compute_pair(const DecodeParams& p, const int32_t* bt_row, int kvh,
                                              int tile, int t_end, int refill, int tok_limit,
                                              int interior_limit, const int (&row_last)[NT],
                                              const QOps<FMT, NT>& q, RawTile<FMT> (&r)[2],
                                              uint8_t (*s_v)[16][kVRow], int lane,
-                                             WaveState<NT>& st) {
+                                             const LaneOffsets& lo, WaveState<NT>& st) {
   const int col = lane & 15;
   const int quad = lane >> 4;
   const bool hi_col = col < 8;
@@ -271,44 +303,33 @@ __device__ __forceinline__ void compute_pair(const DecodeParams& p, const int32_
     }
   }
 
-  // ---- V tiles -> LDS as bf16 token rows
-  const bool interior = (tile * 16 + 32) <= interior_limit;
+  // ---- V tiles -> LDS as bf16 token rows.  Past the end of the context the
+  // cache may hold anything: clear those codes and use the smallest scale so
+  // the (zero-weighted) values are exactly zero.
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
-    uint32_t vb[16];
-    dequant_group<FMT>(r[s].v, scale_operand(r[s].vsc), vb);
-    if (!interior) {
-      const int tok = (tile + s) * 16 + col;
-      if (tok >= tok_limit) {
+    uint32_t vw[Fmt<FMT>::kWords];
+    uint32_t vsc = r[s].vsc;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) vb[i] = 0u;
-      }
+    for (int i = 0; i < Fmt<FMT>::kWords; ++i) vw[i] = r[s].v[i];
+    if constexpr (Boundary) {
+      const bool dead = (tile + s) * 16 + col >= tok_limit;
+#pragma unroll
+      for (int i = 0; i < Fmt<FMT>::kWords; ++i) vw[i] = dead ? 0u : vw[i];
+      vsc = dead ? 0u : vsc;
     }
+    uint32_t vb[16];
+    dequant_group<FMT>(vw, scale_operand(vsc), vb);
     u32x4_t* dst = reinterpret_cast<u32x4_t*>(&s_v[s][col][64 * quad]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dst[i] = u32x4_t{vb[4 * i], vb[4 * i + 1], vb[4 * i + 2], vb[4 * i + 3]};
   }
 
   // the raw codes are consumed: start the next loads into the same registers
-  issue_pair<FMT>(p, bt_row, kvh, refill, t_end, lane, r);
+  issue_pair<FMT>(p, bt_row, kvh, refill, t_end, lo, r);
 
-  // ---- B operands of PV (transposed LDS reads)
-  bf16x8_t Bv[8];
-  {
-    const int rr = col >> 2;
-    const int c4 = (col & 3) * 4;
-    typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-      lds_bf16x4* a0 = (lds_bf16x4*)((__attribute__((address_space(3))) uint8_t*)&s_v[0][4 * quad + rr][2 * (16 * n + c4)]);
-      lds_bf16x4* a1 = (lds_bf16x4*)((__attribute__((address_space(3))) uint8_t*)&s_v[1][4 * quad + rr][2 * (16 * n + c4)]);
-      const u32x2_t w0 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(a0));
-      const u32x2_t w1 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(a1));
-      Bv[n] = __builtin_bit_cast(bf16x8_t, u32x4_t{w0[0], w0[1], w1[0], w1[1]});
-    }
-  }
-
-  // ---- softmax update and P (bf16 hi/lo) per row tile, then PV
+  // ---- softmax update and P (bf16 hi/lo) per row tile
+  bf16x8_t A[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     float sc[8];
@@ -320,7 +341,7 @@ __device__ __forceinline__ void compute_pair(const DecodeParams& p, const int32_
         sc[4 * s + i] = x + dpp_ror8(x);
       }
     }
-    if (!interior) {
+    if constexpr (Boundary) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
 #pragma unroll
@@ -345,8 +366,11 @@ __device__ __forceinline__ void compute_pair(const DecodeParams& p, const int32_
       const float p0 = __builtin_amdgcn_exp2f(sc[2 * e] - m_use);
       const float p1 = __builtin_amdgcn_exp2f(sc[2 * e + 1] - m_use);
       psum += p0 + p1;
-      const uint32_t h = pack_bf16x2(p0, p1);
-      const uint32_t l = pack_bf16x2(p0 - as_f32(h << 16), p1 - as_f32(h & 0xFFFF0000u));
+      // hi: the upper halves of p0, p1 (bf16 by truncation, one byte permute);
+      // lo: the exact remainders rounded to bf16.  |p - hi - lo| <= 2^-16 |p|.
+      const uint32_t u0 = as_u32(p0), u1 = as_u32(p1);
+      const uint32_t h = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+      const uint32_t l = pack_bf16x2(p0 - as_f32(u0 & 0xFFFF0000u), p1 - as_f32(u1 & 0xFFFF0000u));
       pw[e] = hi_col ? h : l;
     }
     if (__builtin_amdgcn_ballot_w64(m_new != m_old)) {
@@ -363,51 +387,50 @@ __device__ __forceinline__ void compute_pair(const DecodeParams& p, const int32_
       }
     }
     st.l_run[t] += psum;
-    const bf16x8_t A = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[0], pw[1], pw[2], pw[3]});
+    A[t] = __builtin_bit_cast(bf16x8_t, u32x4_t{pw[0], pw[1], pw[2], pw[3]});
+  }
+
+  // ---- PV: B operands read transposed from the LDS V tiles, one n-tile
+  // ahead of the MFMA that consumes it
+  {
+    const int rr = col >> 2;
+    const int c4 = (col & 3) * 4;
+    typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+    auto read_b = [&](int n) {
+      lds_bf16x4* a0 = (lds_bf16x4*)((__attribute__((address_space(3))) uint8_t*)&s_v[0][4 * quad + rr][2 * (16 * n + c4)]);
+      lds_bf16x4* a1 = (lds_bf16x4*)((__attribute__((address_space(3))) uint8_t*)&s_v[1][4 * quad + rr][2 * (16 * n + c4)]);
+      const u32x2_t w0 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(a0));
+      const u32x2_t w1 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(a1));
+      return __builtin_bit_cast(bf16x8_t, u32x4_t{w0[0], w0[1], w1[0], w1[1]});
+    };
+    bf16x8_t B0 = read_b(0);
 #pragma unroll
-    for (int n = 0; n < 8; ++n)
-      st.O[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, Bv[n], st.O[t][n], 0, 0, 0);
+    for (int n = 0; n < 8; ++n) {
+      const bf16x8_t C0 = (n + 1 < 8) ? read_b(n + 1) : B0;
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        st.O[t][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[t], B0, st.O[t][n], 0, 0, 0);
+      B0 = C0;
+    }
   }
 }
 
+// Query prologue, once per (sequence, KV head): load the rows of the query
+// group, rotate them with the fp32 transform, pre-scale by sm_scale * log2 e,
+// and store every lane's score-MFMA operands (FP6 terms for the FP4 cache,
+// bf16 hi/lo for the FP8 cache) in the workspace for all context splits.
 template <int FMT, int NT>
-__global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(64) void qprep_kernel(const DecodeParams p) {
   constexpr int ROWS = 8 * NT;
-  // s_rows: query rows (prologue) and output rows (epilogue); s_work: packed
-  // FP6 query terms (prologue, FP4 cache), then the V tiles of the page scan.
-  constexpr int kQpBytes = kQTerms * ROWS * 4 * 24;
-  constexpr int kVBytes = 2 * 16 * kVRow;
-  constexpr int kWorkBytes = kQpBytes > kVBytes ? kQpBytes : kVBytes;
   __shared__ __attribute__((aligned(16))) float s_rows[ROWS * kD];
-  __shared__ __attribute__((aligned(16))) uint8_t s_work[kWorkBytes];
+  __shared__ __attribute__((aligned(16))) uint32_t s_qp[kQTerms * ROWS * 4 * 6];
   __shared__ uint8_t s_qsc[kQTerms][ROWS][4];
-  uint8_t (*s_v)[16][kVRow] = reinterpret_cast<uint8_t (*)[16][kVRow]>(s_work);
-  uint32_t* s_qp = reinterpret_cast<uint32_t*>(s_work);  // [kQTerms][ROWS][4 blocks][6 dwords]
-
   const int lane = threadIdx.x;
-  const int split = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
-  const int L = p.context_lens[b];
-  const int n_tiles = (L + 15) >> 4;
-  const int t_begin = split * p.tiles_per_split;
-  const int t_end = min(n_tiles, t_begin + p.tiles_per_split);
-  const int tok_limit = min(L, t_end * 16);
+  const int kvh = blockIdx.x;
+  const int b = blockIdx.y;
   const int col = lane & 15;
   const int quad = lane >> 4;
-  const int32_t* bt_row = p.block_tables + (size_t)b * p.max_pages;
-  const bool has_work = t_end > t_begin;
-  const int n_pairs = has_work ? ((t_end - t_begin + 1) >> 1) : 0;
-  const int n_iter = (n_pairs + kRing - 1) / kRing;
 
-  // ---- start streaming the first tile pairs before the query prologue
-  RawTile<FMT> ring[kRing][2];
-  if (has_work) {
-#pragma unroll
-    for (int u = 0; u < kRing; ++u) issue_pair<FMT>(p, bt_row, kvh, t_begin + 2 * u, t_end, lane, ring[u]);
-  }
-
-  // ---- query prologue: load, rotate, pre-scale
   for (int i = lane; i < ROWS * kD; i += 64) {
     const int r = i / kD;
     const int ch = i % kD;
@@ -422,7 +445,9 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
   __syncthreads();
   if (p.rotate_q) fwht_rows_lds(s_rows, ROWS, kD, p.norm, lane, 64);
 
-  QOps<FMT, NT> q;
+  constexpr int kS = QOpsLayout<FMT>::kSlots;
+  constexpr int kW = QOpsLayout<FMT>::kDwords;
+  uint32_t* dst = p.qops + ((size_t)(b * p.hkv + kvh) * NT * kS * 64 + lane) * kW;
   if constexpr (Fmt<FMT>::kFP4) {
     // ---- split each (row, 32-channel block) of the pre-scaled query into
     // kQTerms FP6 (E2M3) terms, each with its own UE8M0 scale and carrying
@@ -453,10 +478,10 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
           w[bit >> 5] |= c << (bit & 31);
           if ((bit & 31) > 26) w[(bit >> 5) + 1] |= c >> (32 - (bit & 31));
         }
-        uint32_t* dst = s_qp + (((size_t)t * ROWS + row) * 4 + blk) * 6 + 3 * half;
-        dst[0] = w[0];
-        dst[1] = w[1];
-        dst[2] = w[2];
+        uint32_t* pk = s_qp + (((size_t)t * ROWS + row) * 4 + blk) * 6 + 3 * half;
+        pk[0] = w[0];
+        pk[1] = w[1];
+        pk[2] = w[2];
         if (half == 0) s_qsc[t][row][blk] = (uint8_t)byte;
       }
     }
@@ -470,11 +495,11 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
         const int row = 8 * t + (col & 7);
         const int term = 2 * m + (col >> 3);
         const uint32_t* src = s_qp + (((size_t)term * ROWS + row) * 4 + quad) * 6;
-        q.b[t][m] = i32x8_t{(int)src[0], (int)src[1], (int)src[2], (int)src[3], (int)src[4], (int)src[5], 0, 0};
-        q.sc[t][m] = s_qsc[term][row][quad];
+        uint32_t* w = dst + (size_t)(t * kS + m) * 64 * kW;
+        *reinterpret_cast<u32x4_t*>(w) = u32x4_t{src[0], src[1], src[2], src[3]};
+        *reinterpret_cast<u32x4_t*>(w + 4) = u32x4_t{src[4], src[5], (uint32_t)s_qsc[term][row][quad], 0u};
       }
     }
-    __syncthreads();  // s_work becomes the V tile buffer
   } else {
     // ---- bf16 hi + lo parts of the pre-scaled query; lane group j covers
     // channels 32j + 8s .. 32j + 8s + 7 in k-step s (the K operand order)
@@ -496,7 +521,62 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
           }
           w[e] = h0 | (h1 << 16);
         }
-        q.b[t][s] = __builtin_bit_cast(bf16x8_t, w);
+        *reinterpret_cast<u32x4_t*>(dst + (size_t)(t * kS + s) * 64 * kW) = w;
+      }
+    }
+  }
+}
+
+template <int FMT, int NT>
+__global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
+  constexpr int ROWS = 8 * NT;
+  // s_rows: output rows (epilogue); s_v: the V tiles of the page scan
+  __shared__ __attribute__((aligned(16))) float s_rows[ROWS * kD];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[2][16][kVRow];
+
+  const int lane = threadIdx.x;
+  const int split = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  const int L = p.context_lens[b];
+  const int n_tiles = (L + 15) >> 4;
+  const int t_begin = split * p.tiles_per_split;
+  const int t_end = min(n_tiles, t_begin + p.tiles_per_split);
+  const int tok_limit = min(L, t_end * 16);
+  const int col = lane & 15;
+  const int quad = lane >> 4;
+  const int32_t* bt_row = p.block_tables + (size_t)b * p.max_pages;
+  const bool has_work = t_end > t_begin;
+  const int n_pairs = has_work ? ((t_end - t_begin + 1) >> 1) : 0;
+  const int n_iter = (n_pairs + kRing - 1) / kRing;
+
+  // ---- start streaming the first tile pairs
+  const LaneOffsets lo = lane_offsets<FMT>(p, lane);
+  RawTile<FMT> ring[kRing][2];
+  if (has_work) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) issue_pair<FMT>(p, bt_row, kvh, t_begin + 2 * u, t_end, lo, ring[u]);
+  }
+
+  // ---- this lane's query operands, prepared once per (sequence, KV head)
+  QOps<FMT, NT> q;
+  {
+    constexpr int kS = QOpsLayout<FMT>::kSlots;
+    constexpr int kW = QOpsLayout<FMT>::kDwords;
+    const uint32_t* src = p.qops + ((size_t)(b * p.hkv + kvh) * NT * kS * 64 + lane) * kW;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int m = 0; m < kS; ++m) {
+        const uint32_t* w = src + (size_t)(t * kS + m) * 64 * kW;
+        const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(w);
+        if constexpr (Fmt<FMT>::kFP4) {
+          const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(w + 4);
+          q.b[t][m] = i32x8_t{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], 0, 0};
+          q.sc[t][m] = (int)a1[2];
+        } else {
+          q.b[t][m] = __builtin_bit_cast(bf16x8_t, a0);
+        }
       }
     }
   }
@@ -523,8 +603,13 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
 #pragma unroll
     for (int u = 0; u < kRing; ++u) {
       const int pi = it * kRing + u;
-      compute_pair<FMT, NT>(p, bt_row, kvh, t_begin + 2 * pi, t_end, t_begin + 2 * (pi + kRing),
-                            tok_limit, interior_limit, row_last, q, ring[u], s_v, lane, st);
+      const int tile = t_begin + 2 * pi;
+      if (tile * 16 + 32 <= interior_limit)
+        compute_pair<FMT, NT, false>(p, bt_row, kvh, tile, t_end, tile + 2 * kRing, tok_limit,
+                                     interior_limit, row_last, q, ring[u], s_v, lane, lo, st);
+      else
+        compute_pair<FMT, NT, true>(p, bt_row, kvh, tile, t_end, tile + 2 * kRing, tok_limit,
+                                    interior_limit, row_last, q, ring[u], s_v, lane, lo, st);
     }
   }
 
@@ -591,41 +676,41 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
 }
 
 // Combine the split partials of one (sequence, KV head): weights 2^(m_s - M),
-// normalise by the combined sum, rotate back, store.
+// normalise by the combined sum, rotate back, store.  256 threads: 32 per
+// row, 4 channels each; all split loads are issued before any arithmetic.
+constexpr int kMaxSplits = 64;
+
 template <int NT>
 __global__ __launch_bounds__(256) void merge_kernel(const DecodeParams p) {
   constexpr int ROWS = 8 * NT;
-  __shared__ float s_rows[ROWS * kD];
-  __shared__ float s_w[ROWS][64];
-  __shared__ float s_inv[ROWS];
+  __shared__ __attribute__((aligned(16))) float s_rows[ROWS * kD];
   const int tid = threadIdx.x;
   const int kvh = blockIdx.x;
   const int b = blockIdx.y;
-  const size_t base = ((size_t)b * p.hkv + kvh) * p.splits * ROWS;
   const int S = p.splits;
-  // per-row weights (S <= 64 enforced by the planner)
-  for (int r = tid; r < ROWS; r += blockDim.x) {
+  const size_t base = ((size_t)b * p.hkv + kvh) * S * ROWS;
+  const int c4 = (tid & 31) * 4;
+  for (int r = tid >> 5; r < ROWS; r += 8) {
     float M = -INFINITY;
     for (int s = 0; s < S; ++s) M = fmaxf(M, p.ws_ml[(base + (size_t)s * ROWS + r) * 2]);
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     float lsum = 0.0f;
-    for (int s = 0; s < S; ++s) {
-      const float m = p.ws_ml[(base + (size_t)s * ROWS + r) * 2];
-      const float w = (M == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m - M);
-      s_w[r][s] = w;
-      lsum += w * p.ws_ml[(base + (size_t)s * ROWS + r) * 2 + 1];
+    if (M != -INFINITY) {
+#pragma unroll 8
+      for (int s = 0; s < S; ++s) {
+        const size_t row = base + (size_t)s * ROWS + r;
+        const float w = __builtin_amdgcn_exp2f(p.ws_ml[row * 2] - M);
+        lsum += w * p.ws_ml[row * 2 + 1];
+        const f32x4_t o = *reinterpret_cast<const f32x4_t*>(p.ws_o + row * kD + c4);
+        acc += w * o;
+      }
     }
-    s_inv[r] = (lsum > 0.0f) ? 1.0f / lsum : 0.0f;
+    const float inv = (lsum > 0.0f) ? 1.0f / lsum : 0.0f;
+    *reinterpret_cast<f32x4_t*>(s_rows + r * kD + c4) = acc * inv;
   }
   __syncthreads();
-  for (int i = tid; i < ROWS * kD; i += blockDim.x) {
-    const int r = i / kD;
-    float acc = 0.0f;
-    for (int s = 0; s < S; ++s) acc += s_w[r][s] * p.ws_o[(base + (size_t)s * ROWS) * kD + i];
-    s_rows[i] = acc * s_inv[r];
-  }
-  __syncthreads();
-  if (p.rotate_out) fwht_rows_lds(s_rows, ROWS, kD, p.norm, tid, blockDim.x);
-  for (int i = tid; i < p.rows * kD; i += blockDim.x) {
+  if (p.rotate_out) fwht_rows_lds(s_rows, p.rows, kD, p.norm, tid, 256);
+  for (int i = tid; i < p.rows * kD; i += 256) {
     const int r = i / kD;
     const int ch = i % kD;
     const int j = r / p.group;
@@ -636,6 +721,9 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeParams p) {
 
 template <int FMT, int NT>
 hipError_t launch_nt(const DecodeParams& p, int batch, hipStream_t stream) {
+  hipLaunchKernelGGL((qprep_kernel<FMT, NT>), dim3((unsigned)p.hkv, (unsigned)batch), dim3(64), 0, stream, p);
+  hipError_t e0 = hipGetLastError();
+  if (e0 != hipSuccess) return e0;
   dim3 grid((unsigned)p.splits, (unsigned)p.hkv, (unsigned)batch);
   hipLaunchKernelGGL((decode_kernel<FMT, NT>), grid, dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
@@ -673,7 +761,7 @@ int plan_decode(const CacheGeom& c, int batch, int hq, int n_q, int max_context_
     splits = (int)((n_tiles + per - 1) / per);
   }
   if (splits < 1) splits = 1;
-  if (splits > 64) splits = 64;
+  if (splits > kMaxSplits) splits = kMaxSplits;
   int per = (n_tiles + splits - 1) / splits;
   per = (per + 1) & ~1;  // tiles are processed in pairs
   if (per < 2) per = 2;
@@ -683,9 +771,14 @@ int plan_decode(const CacheGeom& c, int batch, int hq, int n_q, int max_context_
   plan->row_tiles = row_tiles;
   plan->splits = splits;
   plan->tiles_per_split = per;
-  plan->workspace = (splits > 1)
-                        ? (size_t)batch * c.hkv * splits * (8 * row_tiles) * (kD + 2) * sizeof(float)
-                        : 0;
+  const size_t qops = (size_t)batch * c.hkv * row_tiles * 64 * sizeof(uint32_t) *
+                      ((c.fmt == KVQ_FMT_FP4_E2M1) ? QOpsLayout<KVQ_FMT_FP4_E2M1>::kSlots *
+                                                         QOpsLayout<KVQ_FMT_FP4_E2M1>::kDwords
+                                                   : QOpsLayout<KVQ_FMT_FP8_E4M3>::kSlots *
+                                                         QOpsLayout<KVQ_FMT_FP8_E4M3>::kDwords);
+  plan->qops_bytes = qops;
+  plan->workspace =
+      qops + ((splits > 1) ? (size_t)batch * c.hkv * splits * (8 * row_tiles) * (kD + 2) * sizeof(float) : 0);
   return KVQ_OK;
 }
 
@@ -718,8 +811,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   p.tiles_per_split = a.plan.tiles_per_split;
   p.out = a.out;
   const size_t n_o = (size_t)a.batch * a.c.hkv * a.plan.splits * (8 * a.plan.row_tiles) * kD;
-  p.ws_o = a.workspace;
-  p.ws_ml = a.workspace ? a.workspace + n_o : nullptr;
+  uint8_t* ws = reinterpret_cast<uint8_t*>(a.workspace);
+  p.qops = reinterpret_cast<uint32_t*>(ws);
+  p.ws_o = reinterpret_cast<float*>(ws + a.plan.qops_bytes);
+  p.ws_ml = p.ws_o + n_o;
   if (a.c.fmt == KVQ_FMT_FP4_E2M1) return launch_fmt<KVQ_FMT_FP4_E2M1>(p, a.plan.row_tiles, a.batch, stream);
   return launch_fmt<KVQ_FMT_FP8_E4M3>(p, a.plan.row_tiles, a.batch, stream);
 }

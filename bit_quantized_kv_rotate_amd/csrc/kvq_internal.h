@@ -48,6 +48,7 @@ struct DecodePlan {
   int row_tiles;         // 8-row tiles (hi/lo split fills a 16-wide MFMA)
   int splits;            // context splits per (sequence, KV head)
   int tiles_per_split;   // 16-token tiles per split (even)
+  size_t qops_bytes;     // query operands (first part of the workspace)
   size_t workspace;      // bytes
 };
 

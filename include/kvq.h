@@ -128,9 +128,12 @@ int kvq_rotate_quantize_append(const kvq_cache_desc *desc, const void *k_new,
                                const void *v_new, const int32_t *slot_mapping,
                                int32_t n_tokens, kvq_stream_t stream);
 
-/* Workspace bytes a decode call with these sizes needs (0: none).  The
- * caller passes at least this much device memory to the decode call; its
- * contents need no initialisation.  Host-only. */
+/* Workspace bytes a decode call with these sizes needs (0 when the sizes are
+ * invalid): the rotated, pre-scaled query operands, prepared once per
+ * (sequence, KV head), and the partial results of the context splits.  The
+ * caller passes at least this much device memory, 16-byte aligned, to the
+ * decode call; its contents need no initialisation.  Calls that overlap in
+ * time must not share a workspace.  Host-only. */
 size_t kvq_decode_workspace_bytes(const kvq_cache_desc *desc, int32_t batch,
                                   int32_t num_q_heads, int32_t n_q,
                                   int32_t max_context_len, uint32_t flags);

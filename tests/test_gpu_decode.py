@@ -97,7 +97,9 @@ def test_decode_split_count_invariance(gpu):
     ref = f.decode(q, flags=kvq.splits_flag(1)).cpu().numpy()
     for s in (2, 3, 5, 8, 16):
         got = f.decode(q, flags=kvq.splits_flag(s)).cpu().numpy()
-        np.testing.assert_allclose(got, ref, rtol=0, atol=2e-5)
+        # only the fp32 summation order changes (per-split partial sums and
+        # their merge): a few ulp of the larger outputs
+        np.testing.assert_allclose(got, ref, rtol=1e-5, atol=2e-5)
     want = oracle_decode_batch(f, syn.bf16_bits(q))
     assert_close(ref[0], want[0], "one split")
 

@@ -5,15 +5,19 @@ context 32768 tokens per sequence, page size 16 with randomly permuted block
 tables; keys/values/queries bf16 N(0,1) with 2 outlier channels x20 per KV
 head.  One step = append one new token per sequence to the FP4 cache
 (rotate + quantise + store) and one FP4 decode-attention pass over the whole
-cache.  The FP8 (E4M3 + per-32 scale) comparator cache is built from the
-same bf16 inputs and timed in ABBA order against FP4.
+cache.  The cache is replicated (as the layers of a model would be) and the
+steps rotate over the replicas, so no step finds its cache in the 256 MB
+last-level cache.  The FP8 (E4M3 + per-32 scale) comparator cache is built
+from the same bf16 inputs and timed in ABBA order against FP4.
 
 Prints ONE JSON line.  `value` is KV-cache bytes streamed per second by the
-whole step (GB/s, inputs resident in HBM); `roofline` is the FP4 decode
-kernel's algorithmic bytes per launch over its HIP-event duration against
-the 8 TB/s HBM peak; `cpu_baseline` times the CPU oracle on a bounded sample.
+whole step (GB/s, inputs resident in HBM); `roofline` is one FP4 decode call
+(query-prep, page-scan and split-merge kernels) - algorithmic bytes per call
+over its mean HIP-event duration - against the 8 TB/s HBM peak;
+`cpu_baseline` times the CPU oracle on a bounded sample.
 """
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -26,20 +30,30 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 WORKLOAD = "b32_l32k"
+# HBM traffic of one decode call, measured with rocprofv3 counters and
+# scaled by a plain copy kernel; valid only for the kernel source it names.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_fp4_b32_l32k_hbm_traffic.md")
+KERNEL_SOURCES = [os.path.join(ROOT, "bit_quantized_kv_rotate_amd", "csrc", f)
+                  for f in ("kvq_decode.hip", "kvq_device.h")]
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=WORKLOAD)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--replicas", type=int, default=3,
+                    help="cache copies the steps rotate over (defeats last-level-cache reuse)")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="target CPU time of each oracle baseline sample")
+    ap.add_argument("--cpu-threads", type=int, default=0,
+                    help="threads of the parallel oracle sample (0: host cores, at most 16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run one 1 GiB device copy (reference for HBM counters)")
+                    help="also run a plain fp32 elementwise kernel over 2 x 512 MiB "
+                         "(reference for the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -47,10 +61,82 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per decode call from the committed counter summary, or None
+    when there is none or it was taken on another version of the kernel."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        line = line.strip().strip("`")
+        if ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(float(fields["traffic_bytes_per_call"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def build_cache(kvq, syn, wl, plan, fmt, dev):
+    """One cache of format `fmt` holding every sequence's tokens; returns the
+    cache and, per sequence, the last tokens (re-appended by every step)."""
+    P, H, D = wl.page_size, wl.num_kv_heads, wl.head_dim
+    c = kvq.KVCache(fmt, H, D, P, plan.num_pages, kv_shared=wl.kv_shared)
+    n_app = max(wl.append_tokens, 1)
+    for p in range(wl.n_prefixes):
+        pages = plan.prefix_pages[p]
+        kv = {t: syn.full_prefix(wl, plan, t, p, dev) for t in syn.tensor_names(wl)}
+        slots = torch_from(syn.slots_for(pages, len(pages) * P, P), dev)
+        kvq.rotate_quantize_append(c, kv["k"], kv.get("v"), slots)
+    last = {}
+    for b in range(wl.batch):
+        L = int(plan.context_lens[b])
+        n_sh = plan.n_shared_pages[b] * P
+        kv = {t: syn.private_tokens(wl, t, b, L - n_sh, dev) for t in syn.tensor_names(wl)}
+        slots = torch_from(syn.slots_for(plan.private_pages[b], L - n_sh, P), dev)
+        kvq.rotate_quantize_append(c, kv["k"], kv.get("v"), slots)
+        last[b] = ({t: x[-n_app:].contiguous() for t, x in kv.items()}, slots[-n_app:])
+    return c, last
+
+
+def torch_from(a, dev):
+    import torch
+    return torch.from_numpy(a).to(dev)
+
+
+def replicate(kvq, c, n):
+    """n caches with identical contents (the first is `c` itself)."""
+    reps = [c]
+    for _ in range(n - 1):
+        r = kvq.KVCache(c.fmt, c.num_kv_heads, c.head_dim, c.page_size, c.num_pages,
+                        rotate=c.rotate, kv_shared=c.kv_shared)
+        r.k_codes.copy_(c.k_codes)
+        r.k_scales.copy_(c.k_scales)
+        if not c.kv_shared:
+            r.v_codes.copy_(c.v_codes)
+            r.v_scales.copy_(c.v_scales)
+        reps.append(r)
+    return reps
+
+
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
@@ -65,88 +151,72 @@ def main():
     plan = syn.page_plan(wl)
     P, H, D = wl.page_size, wl.num_kv_heads, wl.head_dim
     B, HQ, NQ = wl.batch, wl.num_q_heads, wl.n_q
+    R = max(1, args.replicas)
     dev = torch.device("cuda", 0)
 
-    # ---------------- build both caches from identical bf16 inputs
+    # ---------------- caches (FP4 and FP8 from identical bf16 inputs)
     t0 = time.time()
-    c4 = kvq.KVCache(kvq.FMT_FP4_E2M1, H, D, P, plan.num_pages, kv_shared=wl.kv_shared)
-    c8 = None if args.no_fp8 else kvq.KVCache(kvq.FMT_FP8_E4M3, H, D, P, plan.num_pages,
-                                              kv_shared=wl.kv_shared)
-    n_app = max(wl.append_tokens, 1)
-    last_tok = {}
-    for p in range(wl.n_prefixes):
-        pages = plan.prefix_pages[p]
-        kv = {t: syn.full_prefix(wl, plan, t, p, dev) for t in syn.tensor_names(wl)}
-        slots = torch.from_numpy(syn.slots_for(pages, len(pages) * P, P)).to(dev)
-        for c in (c4, c8):
-            if c is not None:
-                kvq.rotate_quantize_append(c, kv["k"], kv.get("v"), slots)
-    for b in range(B):
-        L = int(plan.context_lens[b])
-        n_sh = plan.n_shared_pages[b] * P
-        kv = {t: syn.private_tokens(wl, t, b, L - n_sh, dev) for t in syn.tensor_names(wl)}
-        slots = torch.from_numpy(syn.slots_for(plan.private_pages[b], L - n_sh, P)).to(dev)
-        for c in (c4, c8):
-            if c is not None:
-                kvq.rotate_quantize_append(c, kv["k"], kv.get("v"), slots)
-        # the last n_app tokens are re-appended by every step
-        last_tok[b] = ({t: x[-n_app:].contiguous() for t, x in kv.items()}, slots[-n_app:])
-        del kv
+    c4, last = build_cache(kvq, syn, wl, plan, kvq.FMT_FP4_E2M1, dev)
+    c8 = None
+    if not args.no_fp8:
+        c8, _ = build_cache(kvq, syn, wl, plan, kvq.FMT_FP8_E4M3, dev)
     torch.cuda.synchronize()
-    build_s = time.time() - t0
-    log("cache build %.1fs: fp4 %.3f GB" % (build_s, c4.nbytes / 1e9))
+    c4s = replicate(kvq, c4, R)
+    c8s = None if c8 is None else replicate(kvq, c8, R)
+    torch.cuda.synchronize()
+    log("caches built in %.1fs: fp4 %.3f GB x %d%s" % (
+        time.time() - t0, c4.nbytes / 1e9, R,
+        "" if c8 is None else ", fp8 %.3f GB x %d" % (c8.nbytes / 1e9, R)))
 
-    step_k = torch.cat([last_tok[b][0]["k"] for b in range(B)], 0)
-    step_v = None if wl.kv_shared else torch.cat([last_tok[b][0]["v"] for b in range(B)], 0)
-    step_slots = torch.cat([last_tok[b][1] for b in range(B)], 0)
+    step_k = torch.cat([last[b][0]["k"] for b in range(B)], 0)
+    step_v = None if wl.kv_shared else torch.cat([last[b][0]["v"] for b in range(B)], 0)
+    step_slots = torch.cat([last[b][1] for b in range(B)], 0)
     q = syn.queries(wl, dev)
-    bt = torch.from_numpy(plan.block_tables).to(dev)
-    cl = torch.from_numpy(plan.context_lens).to(dev)
+    bt = torch_from(plan.block_tables, dev)
+    cl = torch_from(plan.context_lens, dev)
     maxL = int(plan.context_lens.max())
     out4 = torch.empty((B, NQ, HQ, D), dtype=torch.float32, device=dev)
     out8 = torch.empty_like(out4)
-    ws_bytes = kvq.decode_workspace_bytes(c4, B, HQ, NQ, maxL)
-    ws = torch.zeros(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
-
+    ws_bytes = max(kvq.decode_workspace_bytes(c4, B, HQ, NQ, maxL),
+                   0 if c8 is None else kvq.decode_workspace_bytes(c8, B, HQ, NQ, maxL))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step():
-        kvq.rotate_quantize_append(c4, step_k, step_v, step_slots, stream=stream)
-        kvq.decode_attn_fp4(c4, q, bt, cl, maxL, out=out4, workspace=ws, stream=stream)
+    def append(i):
+        kvq.rotate_quantize_append(c4s[i % R], step_k, step_v, step_slots, stream=stream)
 
-    def dec4():
-        kvq.decode_attn_fp4(c4, q, bt, cl, maxL, out=out4, workspace=ws, stream=stream)
+    def dec4(i):
+        kvq.decode_attn_fp4(c4s[i % R], q, bt, cl, maxL, out=out4, workspace=ws, stream=stream)
 
-    def dec8():
-        kvq.decode_attn_fp8(c8, q, bt, cl, maxL, out=out8, workspace=ws, stream=stream)
+    def dec8(i):
+        kvq.decode_attn_fp8(c8s[i % R], q, bt, cl, maxL, out=out8, workspace=ws, stream=stream)
 
-    # ---------------- timed steps
-    for _ in range(args.warmup):
-        step()
+    # ---------------- W untimed steps, then exactly K timed steps
+    for i in range(args.warmup):
+        append(i)
+        dec4(i)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    evd = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
-        ev[i][0].record(stream)
-        kvq.rotate_quantize_append(c4, step_k, step_v, step_slots, stream=stream)
-        evd[i][0].record(stream)
-        kvq.decode_attn_fp4(c4, q, bt, cl, maxL, out=out4, workspace=ws, stream=stream)
-        evd[i][1].record(stream)
-        ev[i][1].record(stream)
+        e = ev[i]
+        e[0].record(stream)
+        append(i)
+        e[1].record(stream)
+        dec4(i)
+        e[2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    step_ms = [a.elapsed_time(b) for a, b in ev]
-    dec_ms = [a.elapsed_time(b) for a, b in evd]
+    step_ms = [e[0].elapsed_time(e[2]) for e in ev]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in ev]
     ms_per_step = wall * 1e3 / args.steps
 
     # ---------------- bytes
     Ls = plan.context_lens.astype(np.int64)
-    per_tok_fp4 = (D // 2 + D // 32) * (1 if wl.kv_shared else 2)     # 136 at d128
-    per_tok_fp8 = (D + D // 32) * (1 if wl.kv_shared else 2)          # 264 at d128
+    n_t = 1 if wl.kv_shared else 2
+    per_tok_fp4 = (D // 2 + D // 32) * n_t     # 136 at d128 (K and V)
+    per_tok_fp8 = (D + D // 32) * n_t          # 264 at d128
     kv_fp4 = int(Ls.sum()) * H * per_tok_fp4
     kv_fp8 = int(Ls.sum()) * H * per_tok_fp8
     q_bytes = B * NQ * HQ * D * 2
@@ -154,9 +224,8 @@ def main():
     out_bytes = B * NQ * HQ * D * 4
     dec_alg = kv_fp4 + q_bytes + bt_bytes + out_bytes
     value = kv_fp4 / (ms_per_step * 1e-3) / 1e9
-
-    med_dec = statistics.median(dec_ms)
-    achieved = dec_alg / (med_dec * 1e-3) / 1e9
+    mean_dec = statistics.fmean(dec_ms)
+    achieved = dec_alg / (mean_dec * 1e-3) / 1e9
 
     # ---------------- FP4 vs FP8, ABBA (median of three paired-mean ratios)
     fp8 = None
@@ -164,17 +233,17 @@ def main():
         def timed(fn, n):
             es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                   for _ in range(n)]
-            for a, b in es:
+            for i, (a, b) in enumerate(es):
                 a.record(stream)
-                fn()
+                fn(i)
                 b.record(stream)
             torch.cuda.synchronize()
             return statistics.median([a.elapsed_time(b) for a, b in es])
-        for _ in range(3):
-            dec8()
+        for i in range(5):
+            dec8(i)
         torch.cuda.synchronize()
         ratios, t4s, t8s = [], [], []
-        n = max(args.steps, 10)
+        n = max(args.steps // 2, 24)
         for _ in range(3):
             a1 = timed(dec4, n)
             b1 = timed(dec8, n)
@@ -184,40 +253,31 @@ def main():
             t4s.append(t4)
             t8s.append(t8)
             ratios.append(t8 / t4)
-        t8m = statistics.median(t8s)
+        t8m, t4m = statistics.median(t8s), statistics.median(t4s)
         fp8 = {
             "decode_ms": round(t8m, 4),
             "kv_gbs": round(kv_fp8 / (t8m * 1e-3) / 1e9, 1),
             "hbm_frac": round(kv_fp8 / (t8m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "fp4_decode_ms_abba": round(statistics.median(t4s), 4),
+            "fp4_decode_ms": round(t4m, 4),
+            "fp4_kv_gbs": round(kv_fp4 / (t4m * 1e-3) / 1e9, 1),
             "speedup_fp4_vs_fp8": round(statistics.median(ratios), 3),
             "kv_bytes": kv_fp8,
+            "byte_ratio": round(kv_fp8 / kv_fp4, 4),
         }
 
-    # ---------------- evicted check: a 1 GiB write between decodes
-    evict = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    ev_ms = []
-    for _ in range(5):
-        evict.fill_(1)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        dec4()
-        b.record(stream)
-        torch.cuda.synchronize()
-        ev_ms.append(a.elapsed_time(b))
-    del evict
-
     if args.copy_calibration:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        # torch's elementwise kernel: reads 512 MiB, writes 512 MiB
+        src = torch.ones(1 << 27, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
-        dst.copy_(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
     # ---------------- CPU oracle baseline on a bounded sample
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, plan, args.cpu_seconds)
+        cpu = cpu_baseline(wl, plan, args.cpu_seconds, args.cpu_threads)
 
     res = {
         "metric": "FP4-KV decode attention: KV bytes/s as % of HBM peak; speedup vs FP8-KV kernel",
@@ -230,22 +290,24 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp4 e2m1 cache -> bf16 hi/lo MFMA, f32 accumulate",
+        "dtype": "fp4 e2m1 cache; scaled fp4 x fp6 MFMA scores, bf16 hi/lo MFMA PV, fp32 accumulate",
         "data": "synthetic (seeded bf16 N(0,1) + outlier channels; no trace or dataset)",
         "config": {
             "workload": "%s: %s" % (wl.name, wl.description),
             "batch": B, "kv_heads": H, "q_heads": HQ, "head_dim": D, "context": maxL,
             "page_size": P, "query_positions": NQ, "parallelism": "single GPU",
+            "cache_replicas": R,
         },
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": kv_fp4,
         "step_ms_events_median": round(statistics.median(step_ms), 4),
-        "decode_ms_events_median": round(med_dec, 4),
-        "decode_ms_evicted_median": round(statistics.median(ev_ms), 4),
+        "decode_ms_events_median": round(statistics.median(dec_ms), 4),
+        "decode_ms_events_mean": round(mean_dec, 4),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-            "kernel": "decode_kernel<fp4> + split merge (one decode call)",
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": recorded_traffic(),
+            "kernel": "one FP4 decode call: qprep_kernel + decode_kernel + merge_kernel",
             "bytes_per_launch": dec_alg,
         },
         "fp8_comparator": fp8,
@@ -254,10 +316,14 @@ def main():
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline(wl, plan, target_s):
-    """Time the oracle (dequantise the FP4 cache of one (sequence, KV head)
-    and run fp64 decode attention for its query heads) on (sequence, KV head)
-    pairs until about target_s seconds of CPU work; report KV GB/s."""
+def cpu_baseline(wl, plan, target_s, threads):
+    """Time the oracle - dequantise the FP4 cache of one (sequence, KV head)
+    and run fp64 decode attention for its query heads - over (sequence, KV
+    head) items: first single-threaded until about target_s seconds, then on
+    `threads` host threads (the oracle's C code runs without the GIL) for
+    about target_s seconds of CPU time.  Reports KV GB/s."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
     import torch
     import kvq_synth as syn
@@ -267,35 +333,58 @@ def cpu_baseline(wl, plan, target_s):
     q = syn.bf16_bits(syn.queries(wl, dev))
     g = wl.group
     sm = 1.0 / math.sqrt(wl.head_dim)
-    total_s, total_bytes, pairs = 0.0, 0, []
-    rng = np.random.default_rng(0)
-    order = rng.permutation(wl.batch * wl.num_kv_heads)
-    for idx in order:
-        b, h = int(idx // wl.num_kv_heads), int(idx % wl.num_kv_heads)
-        k = syn.bf16_bits(syn.sequence_kv(wl, plan, "k", b, dev)[:, h:h + 1])
-        v = None if wl.kv_shared else syn.bf16_bits(syn.sequence_kv(wl, plan, "v", b, dev)[:, h:h + 1])
-        kc, ks = oracle.quantize_fp4(k, True)
-        vc, vs = (None, None) if v is None else oracle.quantize_fp4(v, True)
-        t0 = time.perf_counter()
+    if threads <= 0:
+        threads = min(16, os.cpu_count() or 1)
+    # sequence-major, so each sequence's K/V is drawn once per pass
+    order = [(b, h) for b in range(wl.batch) for h in range(wl.num_kv_heads)]
+    seq_cache = {}
+
+    def item(b, h):
+        """Quantised FP4 K/V of one (sequence, KV head) - not timed."""
+        if b not in seq_cache:
+            seq_cache.clear()
+            k = syn.bf16_bits(syn.sequence_kv(wl, plan, "k", b, dev))
+            v = None if wl.kv_shared else syn.bf16_bits(syn.sequence_kv(wl, plan, "v", b, dev))
+            seq_cache[b] = (k, v)
+        k, v = seq_cache[b]
+        kc, ks = oracle.quantize_fp4(np.ascontiguousarray(k[:, h:h + 1]), True)
+        vc, vs = (None, None) if v is None else oracle.quantize_fp4(np.ascontiguousarray(v[:, h:h + 1]), True)
+        return kc, ks, vc, vs
+
+    def work(b, h, kc, ks, vc, vs):
         khat = oracle.dequant_fp4(kc, ks)
-        vhat = None if v is None else oracle.dequant_fp4(vc, vs)
+        vhat = None if vc is None else oracle.dequant_fp4(vc, vs)
         oracle.decode(q[b][:, h * g:(h + 1) * g], khat, vhat, True, sm)
-        dt = time.perf_counter() - t0
-        total_s += dt
-        L = k.shape[0]
-        total_bytes += L * (kc.shape[-1] + ks.shape[-1]) * (1 if v is None else 2)
-        pairs.append((b, h))
-        if total_s >= target_s:
+        return kc.shape[0] * (kc.shape[-1] + ks.shape[-1]) * (1 if vc is None else 2)
+
+    # single thread
+    t1, b1, n1 = 0.0, 0, 0
+    for b, h in order:
+        args = item(b, h)
+        t0 = time.perf_counter()
+        b1 += work(b, h, *args)
+        t1 += time.perf_counter() - t0
+        n1 += 1
+        if t1 >= target_s:
             break
+    per_item = t1 / n1
+    # parallel: enough items for about target_s of CPU time, inputs prepared first
+    n_par = max(threads, int(math.ceil(target_s / per_item / threads)) * threads)
+    items = [(b, h) + item(b, h) for b, h in (order * (n_par // len(order) + 1))[:n_par]]
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        bpar = sum(ex.map(lambda a: work(*a), items))
+    tpar = time.perf_counter() - t0
     return {
-        "value": round(total_bytes / total_s / 1e9, 4),
+        "value": round(bpar / tpar / 1e9, 4),
         "unit": "GB/s",
-        "cores": 1,
+        "cores": threads,
         "kind": "oracle",
-        "sample": "%d (sequence, KV head) pairs of %s: dequantise their FP4 K/V "
-                  "(%d tokens each) and run fp64 decode attention for %d query heads; "
-                  "%.1f s single-threaded" % (len(pairs), wl.name, int(plan.context_lens[0]), g, total_s),
-        "seconds": round(total_s, 2),
+        "sample": "%d (sequence, KV head) items of %s (%d tokens each): dequantise the "
+                  "FP4 K/V and run fp64 decode attention for %d query heads, on %d threads "
+                  "in %.2f s wall" % (n_par, wl.name, int(plan.context_lens[0]), g, threads, tpar),
+        "single_thread": {"value": round(b1 / t1 / 1e9, 4), "unit": "GB/s", "items": n1,
+                          "seconds": round(t1, 2)},
         "cpu": cpu_model(),
     }
 

@@ -415,115 +415,112 @@ __device__ __forceinline__ void compute_pair(const DecodeParams& p, const int32_
   }
 }
 
-// Query prologue, once per (sequence, KV head): load the rows of the query
-// group, rotate them with the fp32 transform, pre-scale by sm_scale * log2 e,
-// and store every lane's score-MFMA operands (FP6 terms for the FP4 cache,
-// bf16 hi/lo for the FP8 cache) in the workspace for all context splits.
-template <int FMT, int NT>
-__global__ __launch_bounds__(64) void qprep_kernel(const DecodeParams p) {
-  constexpr int ROWS = 8 * NT;
-  __shared__ __attribute__((aligned(16))) float s_rows[ROWS * kD];
-  __shared__ __attribute__((aligned(16))) uint32_t s_qp[kQTerms * ROWS * 4 * 6];
-  __shared__ uint8_t s_qsc[kQTerms][ROWS][4];
-  const int lane = threadIdx.x;
-  const int kvh = blockIdx.x;
-  const int b = blockIdx.y;
-  const int col = lane & 15;
-  const int quad = lane >> 4;
-
-  for (int i = lane; i < ROWS * kD; i += 64) {
-    const int r = i / kD;
-    const int ch = i % kD;
-    float v = 0.0f;
-    if (r < p.rows) {
-      const int j = r / p.group;
-      const int hh = r - j * p.group;
-      v = bf16_to_f32(p.q[(((size_t)b * p.n_q + j) * p.hq + (size_t)kvh * p.group + hh) * kD + ch]);
+// Walsh-Hadamard transform of one 128-channel row held by a wave, lane l
+// holding channels 2l and 2l + 1: stage h = 1 in the lane, stage h >= 2
+// between lanes l and l ^ (h / 2); fp32 a + b and a - b in the order of the
+// radix-2 definition, then one multiply by c.
+__device__ __forceinline__ void wave_fwht128(float& x0, float& x1, int lane, float c) {
+  const float a = x0;
+  x0 = a + x1;
+  x1 = a - x1;
+#pragma unroll
+  for (int hs = 1; hs < 64; hs <<= 1) {
+    const float y0 = __shfl_xor(x0, hs, 64);
+    const float y1 = __shfl_xor(x1, hs, 64);
+    if (lane & hs) {
+      x0 = y0 - x0;
+      x1 = y1 - x1;
+    } else {
+      x0 = x0 + y0;
+      x1 = x1 + y1;
     }
-    s_rows[i] = v;
   }
-  __syncthreads();
-  if (p.rotate_q) fwht_rows_lds(s_rows, ROWS, kD, p.norm, lane, 64);
+  x0 = x0 * c;
+  x1 = x1 * c;
+}
 
+// Query prologue, once per query row: load the row, rotate it with the fp32
+// transform, pre-scale by sm_scale * log2 e, and store the score-MFMA
+// operands the page-scan lanes will hold (FP6 terms for the FP4 cache, bf16
+// hi/lo for the FP8 cache) in the workspace, for all context splits.
+// One wave per row (rows of a KV head padded to 8 * NT with zeros); lane l
+// holds channels 2l and 2l + 1, so the butterfly stage of distance h >= 2
+// pairs lane l with lane l ^ (h / 2); every stage is the fp32 add or
+// subtract of the append kernel's transform, in the same order.
+template <int FMT, int NT>
+__global__ __launch_bounds__(256) void qprep_kernel(const DecodeParams p) {
+  constexpr int ROWS = 8 * NT;
   constexpr int kS = QOpsLayout<FMT>::kSlots;
   constexpr int kW = QOpsLayout<FMT>::kDwords;
-  uint32_t* dst = p.qops + ((size_t)(b * p.hkv + kvh) * NT * kS * 64 + lane) * kW;
+  const int lane = threadIdx.x & 63;
+  const int gr = blockIdx.x * 4 + (threadIdx.x >> 6);  // grid covers exactly B * hkv * ROWS
+  const int r = gr % ROWS;
+  const int bh = gr / ROWS;
+  const int kvh = bh % p.hkv;
+  const int b = bh / p.hkv;
+
+  float x0 = 0.0f, x1 = 0.0f;
+  if (r < p.rows) {
+    const int j = r / p.group;
+    const int hh = r - j * p.group;
+    const uint16_t* src = p.q + (((size_t)b * p.n_q + j) * p.hq + (size_t)kvh * p.group + hh) * kD + 2 * lane;
+    x0 = bf16_to_f32(src[0]);
+    x1 = bf16_to_f32(src[1]);
+  }
+  if (p.rotate_q) wave_fwht128(x0, x1, lane, p.norm);
+  x0 = x0 * p.qscale;
+  x1 = x1 * p.qscale;
+
+  const int t = r >> 3;
+  const int c7 = r & 7;
+  uint32_t* base = p.qops + (size_t)bh * NT * kS * 64 * kW;
   if constexpr (Fmt<FMT>::kFP4) {
-    // ---- split each (row, 32-channel block) of the pre-scaled query into
-    // kQTerms FP6 (E2M3) terms, each with its own UE8M0 scale and carrying
-    // the previous residual.  Two lanes per (row, block), 16 channels each;
-    // 16 six-bit codes are exactly 3 dwords of the operand bitstream.
-    for (int pr = lane >> 1; pr < ROWS * 4; pr += 32) {
-      const int row = pr >> 2;
-      const int blk = pr & 3;
-      const int half = lane & 1;
-      float x[16];
+    // kQTerms FP6 (E2M3) terms per 32-channel block (16 lanes), each with its
+    // own UE8M0 scale and carrying the previous residual.  The block's 32
+    // six-bit codes form a 192-bit little-endian stream: lane i of the block
+    // holds bits 12i .. 12i + 11; lanes 0..5 assemble its dwords, lane 6
+    // the scale byte, lane 7 a zero pad.
+    const int blk = lane >> 4;
+    const int li = lane & 15;
+    const int w = min(li, 5);
+    const int src_a = 16 * blk + 8 * (w / 3) + 2 * (w % 3);
+    const int sh = 8 * (w % 3);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = s_rows[row * kD + 32 * blk + 16 * half + i] * p.qscale;
-#pragma unroll 1
-      for (int t = 0; t < kQTerms; ++t) {
-        float am = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(x[i]));
-        am = fmaxf(am, __shfl_xor(am, 1, 64));
-        const int byte = max((int)((as_u32(am) >> 23) & 0xFFu) - 2, 0);
-        const int e = byte - 127;
-        uint32_t w[3] = {0u, 0u, 0u};
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float val;
-          const uint32_t c = e2m3_split(x[i], e, val);
-          x[i] -= val;
-          const int bit = 6 * i;
-          w[bit >> 5] |= c << (bit & 31);
-          if ((bit & 31) > 26) w[(bit >> 5) + 1] |= c >> (32 - (bit & 31));
-        }
-        uint32_t* pk = s_qp + (((size_t)t * ROWS + row) * 4 + blk) * 6 + 3 * half;
-        pk[0] = w[0];
-        pk[1] = w[1];
-        pk[2] = w[2];
-        if (half == 0) s_qsc[t][row][blk] = (uint8_t)byte;
-      }
-    }
-    __syncthreads();
-    // B operands: lane (j = l/16, column n = l%16) holds the 32 codes of block
-    // j for row 8t + (n & 7), term 2m + (n >= 8), with that block's scale.
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-#pragma unroll
-      for (int m = 0; m < kQMfma; ++m) {
-        const int row = 8 * t + (col & 7);
-        const int term = 2 * m + (col >> 3);
-        const uint32_t* src = s_qp + (((size_t)term * ROWS + row) * 4 + quad) * 6;
-        uint32_t* w = dst + (size_t)(t * kS + m) * 64 * kW;
-        *reinterpret_cast<u32x4_t*>(w) = u32x4_t{src[0], src[1], src[2], src[3]};
-        *reinterpret_cast<u32x4_t*>(w + 4) = u32x4_t{src[4], src[5], (uint32_t)s_qsc[term][row][quad], 0u};
-      }
+    for (int tm = 0; tm < kQTerms; ++tm) {
+      float am = fmaxf(fabsf(x0), fabsf(x1));
+      am = fmaxf(am, __shfl_xor(am, 1, 64));
+      am = fmaxf(am, __shfl_xor(am, 2, 64));
+      am = fmaxf(am, __shfl_xor(am, 4, 64));
+      am = fmaxf(am, __shfl_xor(am, 8, 64));
+      const int byte = max((int)((as_u32(am) >> 23) & 0xFFu) - 2, 0);
+      const int e = byte - 127;
+      float v0, v1;
+      const uint32_t c0 = e2m3_split(x0, e, v0);
+      const uint32_t c1 = e2m3_split(x1, e, v1);
+      x0 -= v0;
+      x1 -= v1;
+      const uint32_t v12 = c0 | (c1 << 6);
+      const uint32_t u24 = v12 | ((uint32_t)__shfl_xor((int)v12, 1, 64) << 12);  // valid on even li
+      const uint32_t ua = (uint32_t)__shfl((int)u24, src_a, 64);
+      const uint32_t ub = (uint32_t)__shfl((int)u24, src_a + 2, 64);
+      const uint32_t d = (ua >> sh) | (ub << (24 - sh));
+      const int m = tm >> 1;
+      const int col = c7 + 8 * (tm & 1);
+      uint32_t* dst = base + ((size_t)(t * kS + m) * 64 + 16 * blk + col) * kW;
+      if (li < 8) dst[li] = (li < 6) ? d : (li == 6 ? (uint32_t)byte : 0u);
     }
   } else {
-    // ---- bf16 hi + lo parts of the pre-scaled query; lane group j covers
-    // channels 32j + 8s .. 32j + 8s + 7 in k-step s (the K operand order)
-    const bool hi_col = col < 8;
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const float* src = s_rows + (8 * t + (col & 7)) * kD + 32 * quad + 8 * s;
-        u32x4_t w;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float x0 = src[2 * e] * p.qscale;
-          const float x1 = src[2 * e + 1] * p.qscale;
-          uint32_t h0 = f32_to_bf16_rne(x0), h1 = f32_to_bf16_rne(x1);
-          if (!hi_col) {
-            h0 = f32_to_bf16_rne(x0 - bf16_to_f32((uint16_t)h0));
-            h1 = f32_to_bf16_rne(x1 - bf16_to_f32((uint16_t)h1));
-          }
-          w[e] = h0 | (h1 << 16);
-        }
-        *reinterpret_cast<u32x4_t*>(dst + (size_t)(t * kS + s) * 64 * kW) = w;
-      }
-    }
+    // bf16 hi + lo parts; the operand lane (col, quad) of k-step s holds
+    // channels 32 quad + 8 s .. + 7 of row 8t + (col & 7), hi for col < 8.
+    const uint32_t h0 = f32_to_bf16_rne(x0), h1 = f32_to_bf16_rne(x1);
+    const uint32_t l0 = f32_to_bf16_rne(x0 - bf16_to_f32((uint16_t)h0));
+    const uint32_t l1 = f32_to_bf16_rne(x1 - bf16_to_f32((uint16_t)h1));
+    const int quad = lane >> 4;
+    const int s4 = (lane & 15) >> 2;
+    const int e = lane & 3;
+    uint32_t* dst = base + ((size_t)(t * kS + s4) * 64 + 16 * quad + c7) * kW + e;
+    dst[0] = h0 | (h1 << 16);
+    dst[8 * kW] = l0 | (l1 << 16);
   }
 }
 
@@ -675,60 +672,70 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
   }
 }
 
-// Combine the split partials of one (sequence, KV head): weights 2^(m_s - M),
-// normalise by the combined sum, rotate back, store.  256 threads: 32 per
-// row, 4 channels each; all split loads are issued before any arithmetic.
+// Combine the split partials of each query row: weights 2^(m_s - M),
+// normalise by the combined sum, rotate back, store.  One wave per row
+// (four per block); lane s < S holds split s's (m, l), lane l accumulates
+// channels 2l and 2l + 1 over the splits.
 constexpr int kMaxSplits = 64;
 
 template <int NT>
 __global__ __launch_bounds__(256) void merge_kernel(const DecodeParams p) {
   constexpr int ROWS = 8 * NT;
-  __shared__ __attribute__((aligned(16))) float s_rows[ROWS * kD];
-  const int tid = threadIdx.x;
-  const int kvh = blockIdx.x;
-  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int gr = blockIdx.x * 4 + (threadIdx.x >> 6);  // grid covers exactly B * hkv * ROWS
+  const int r = gr % ROWS;
+  const int bh = gr / ROWS;
+  if (r >= p.rows) return;  // padding row: the whole wave leaves (no barrier follows)
+  const int kvh = bh % p.hkv;
+  const int b = bh / p.hkv;
   const int S = p.splits;
-  const size_t base = ((size_t)b * p.hkv + kvh) * S * ROWS;
-  const int c4 = (tid & 31) * 4;
-  for (int r = tid >> 5; r < ROWS; r += 8) {
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, p.ws_ml[(base + (size_t)s * ROWS + r) * 2]);
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    float lsum = 0.0f;
-    if (M != -INFINITY) {
+  const size_t row0 = (size_t)bh * S * ROWS + r;  // split s: row0 + s * ROWS
+
+  float ms = -INFINITY, ls = 0.0f;
+  if (lane < S) {
+    ms = p.ws_ml[(row0 + (size_t)lane * ROWS) * 2 + 0];
+    ls = p.ws_ml[(row0 + (size_t)lane * ROWS) * 2 + 1];
+  }
+  float M = ms;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  const float ws = (M != -INFINITY) ? __builtin_amdgcn_exp2f(ms - M) : 0.0f;
+  float lsum = ws * ls;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) lsum += __shfl_xor(lsum, o, 64);
+
+  float a0 = 0.0f, a1 = 0.0f;
+  const float* po = p.ws_o + row0 * kD + 2 * lane;
 #pragma unroll 8
-      for (int s = 0; s < S; ++s) {
-        const size_t row = base + (size_t)s * ROWS + r;
-        const float w = __builtin_amdgcn_exp2f(p.ws_ml[row * 2] - M);
-        lsum += w * p.ws_ml[row * 2 + 1];
-        const f32x4_t o = *reinterpret_cast<const f32x4_t*>(p.ws_o + row * kD + c4);
-        acc += w * o;
-      }
-    }
-    const float inv = (lsum > 0.0f) ? 1.0f / lsum : 0.0f;
-    *reinterpret_cast<f32x4_t*>(s_rows + r * kD + c4) = acc * inv;
+  for (int sp = 0; sp < S; ++sp) {
+    const float w = as_f32((uint32_t)__builtin_amdgcn_readlane((int)as_u32(ws), sp));
+    const f32x2_t o = *reinterpret_cast<const f32x2_t*>(po + (size_t)sp * ROWS * kD);
+    a0 += w * o[0];
+    a1 += w * o[1];
   }
-  __syncthreads();
-  if (p.rotate_out) fwht_rows_lds(s_rows, p.rows, kD, p.norm, tid, 256);
-  for (int i = tid; i < p.rows * kD; i += 256) {
-    const int r = i / kD;
-    const int ch = i % kD;
-    const int j = r / p.group;
-    const int hh = r - j * p.group;
-    p.out[(((size_t)b * p.n_q + j) * p.hq + (size_t)kvh * p.group + hh) * kD + ch] = s_rows[i];
-  }
+  const float inv = (lsum > 0.0f) ? 1.0f / lsum : 0.0f;
+  a0 *= inv;
+  a1 *= inv;
+  if (p.rotate_out) wave_fwht128(a0, a1, lane, p.norm);
+  const int j = r / p.group;
+  const int hh = r - j * p.group;
+  float* dst = p.out + (((size_t)b * p.n_q + j) * p.hq + (size_t)kvh * p.group + hh) * kD + 2 * lane;
+  dst[0] = a0;
+  dst[1] = a1;
 }
 
 template <int FMT, int NT>
 hipError_t launch_nt(const DecodeParams& p, int batch, hipStream_t stream) {
-  hipLaunchKernelGGL((qprep_kernel<FMT, NT>), dim3((unsigned)p.hkv, (unsigned)batch), dim3(64), 0, stream, p);
+  // 8 * NT rows per (sequence, KV head), four row-waves per block
+  const unsigned qblocks = (unsigned)((size_t)batch * p.hkv * 8 * NT / 4);
+  hipLaunchKernelGGL((qprep_kernel<FMT, NT>), dim3(qblocks), dim3(256), 0, stream, p);
   hipError_t e0 = hipGetLastError();
   if (e0 != hipSuccess) return e0;
   dim3 grid((unsigned)p.splits, (unsigned)p.hkv, (unsigned)batch);
   hipLaunchKernelGGL((decode_kernel<FMT, NT>), grid, dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  hipLaunchKernelGGL((merge_kernel<NT>), dim3((unsigned)p.hkv, (unsigned)batch), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((merge_kernel<NT>), dim3(qblocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

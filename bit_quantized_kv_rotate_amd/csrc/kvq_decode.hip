@@ -33,6 +33,8 @@
 //    memory wait counts stay exact.
 //  * Context split into `splits` ranges; partial (m, l, O) go to the
 //    workspace and a merge kernel combines them, normalises, rotates back.
+#include <atomic>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -677,6 +679,9 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
 // (four per block); lane s < S holds split s's (m, l), lane l accumulates
 // channels 2l and 2l + 1 over the splits.
 constexpr int kMaxSplits = 64;
+constexpr int kMinTilesPerSplit = 8;     // 128 tokens
+constexpr int kDefaultWaveSlots = 2048;  // MI355X: 256 CUs x 8 resident waves
+constexpr int kMaxDevices = 64;
 
 template <int NT>
 __global__ __launch_bounds__(256) void merge_kernel(const DecodeParams p) {
@@ -749,6 +754,42 @@ hipError_t launch_fmt(const DecodeParams& p, int row_tiles, int batch, hipStream
   }
 }
 
+// Page-scan waves the current device holds at once: compute units times
+// resident 64-thread blocks per unit for this kernel; 0 without a device.
+// Cached per (device, format, row tiles).
+template <int FMT, int NT>
+int resident_waves_nt(int dev) {
+  static std::atomic<int> cache[kMaxDevices];
+  if (dev < kMaxDevices) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int cus = 0, blocks = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode_kernel<FMT, NT>, 64, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  const int v = cus * blocks;
+  if (dev < kMaxDevices) cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+int resident_waves(int fmt, int row_tiles) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  const bool fp4 = fmt == KVQ_FMT_FP4_E2M1;
+  switch (row_tiles) {
+    case 1: return fp4 ? resident_waves_nt<KVQ_FMT_FP4_E2M1, 1>(dev) : resident_waves_nt<KVQ_FMT_FP8_E4M3, 1>(dev);
+    case 2: return fp4 ? resident_waves_nt<KVQ_FMT_FP4_E2M1, 2>(dev) : resident_waves_nt<KVQ_FMT_FP8_E4M3, 2>(dev);
+    case 3: return fp4 ? resident_waves_nt<KVQ_FMT_FP4_E2M1, 3>(dev) : resident_waves_nt<KVQ_FMT_FP8_E4M3, 3>(dev);
+    default: return 0;
+  }
+}
+
 }  // namespace
 
 int plan_decode(const CacheGeom& c, int batch, int hq, int n_q, int max_context_len, uint32_t flags,
@@ -761,11 +802,16 @@ int plan_decode(const CacheGeom& c, int batch, int hq, int n_q, int max_context_
   const int n_tiles = (max_context_len + 15) / 16;
   int splits = (int)((flags & KVQ_SPLITS_MASK) >> KVQ_SPLITS_SHIFT);
   if (splits <= 0) {
-    // Aim at ~4096 waves in total, each scanning at least 8 tiles (128 tokens).
+    // One round of waves: as many splits as fill the device's resident wave
+    // slots once (a second, partial round costs more than the larger
+    // partials save), but at least kMinTilesPerSplit tiles per split.
+    int slots = resident_waves(c.fmt, row_tiles);
+    if (slots <= 0) slots = kDefaultWaveSlots;
     const long long units = (long long)batch * c.hkv;
-    const long long want_tiles = ((long long)units * n_tiles + 4095) / 4096;
-    long long per = want_tiles < 8 ? 8 : want_tiles;
-    splits = (int)((n_tiles + per - 1) / per);
+    long long want = units >= slots ? 1 : slots / units;
+    const long long by_len = n_tiles / kMinTilesPerSplit;
+    if (want > by_len) want = by_len;
+    splits = (int)(want < 1 ? 1 : want);
   }
   if (splits < 1) splits = 1;
   if (splits > kMaxSplits) splits = kMaxSplits;

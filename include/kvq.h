@@ -19,7 +19,8 @@
  * Conventions shared by every call
  *   - Every pointer argument that names tensor data is a DEVICE pointer owned
  *     by the caller.  The library allocates nothing, keeps no state between
- *     calls, never synchronises, and enqueues its kernels on `stream`.
+ *     calls beyond a cache of device properties (compute units, kernel
+ *     occupancy), never synchronises, and enqueues its kernels on `stream`.
  *   - Arguments are checked on the host before any HIP call; on a failed
  *     check nothing is enqueued and the call returns a negative KVQ_ERR_*.
  *   - Contract violations that can only be seen on the device (a block-table
@@ -133,7 +134,10 @@ int kvq_rotate_quantize_append(const kvq_cache_desc *desc, const void *k_new,
  * (sequence, KV head), and the partial results of the context splits.  The
  * caller passes at least this much device memory, 16-byte aligned, to the
  * decode call; its contents need no initialisation.  Calls that overlap in
- * time must not share a workspace.  Host-only. */
+ * time must not share a workspace.  Unless KVQ_SPLITS(n) fixes the split
+ * count, the count (and so the size) is planned for the current HIP device:
+ * query with the device current that the decode call will run on.  No
+ * device work is enqueued. */
 size_t kvq_decode_workspace_bytes(const kvq_cache_desc *desc, int32_t batch,
                                   int32_t num_q_heads, int32_t n_q,
                                   int32_t max_context_len, uint32_t flags);

@@ -10,19 +10,26 @@
 // positions per sequence; here they share one pass over the cache (the page
 // names this fusion as future work).
 //
-// Design (gfx950, wave64, one wave per (sequence, KV head, context split)):
-//  * The page scan streams 16-token tiles.  Lane l loads the code bytes of
-//    token l%16, channel group l/16, plus that group's scale byte.
-//  * QK^T runs on v_mfma_scale_f32_16x16x128_f8f6f4: the K codes (FP4, or
-//    E4M3 for the comparator) and their UE8M0 scale bytes are the A operand
-//    and A scale as loaded -- the FP4 operand layout of that instruction is
-//    exactly one (token, 32-channel group) per lane.  The query (rotated and
-//    pre-scaled by sm_scale * log2 e) is split into kQTerms E4M3 terms with
-//    their own per-32 scales (each term carries the previous residual, ~4
-//    more bits per term), two terms per MFMA in columns c and c + 8; one DPP
-//    row rotate adds the halves.  Scores come out transposed (S^T: tokens x
-//    query rows), which is directly the A operand layout of the PV product.
-//  * V codes are converted with their scale (gfx950 scaled converts, 2
+// Design (gfx950, wave64).  Three kernels per call:
+//  * qprep_kernel, one wave per query row: load, rotate (lane-shuffle
+//    butterfly), pre-scale by sm_scale * log2 e, and store each page-scan
+//    lane's score operands in the workspace.  FP4 cache: the query is split
+//    into kQTerms FP6 (E2M3) terms with their own per-32 UE8M0 scales, each
+//    term carrying the previous residual; FP4 x FP6 products are exact in
+//    the scaled MFMA, and six terms leave a residual near 2^-25 of the
+//    block maximum.  FP8 cache: bf16 hi + lo parts.
+//  * decode_kernel, one wave per (sequence, KV head, context split): the
+//    page scan streams 16-token tiles.  Lane l loads the code bytes of token
+//    l%16, channel group l/16, plus that group's scale byte.  For the FP4
+//    cache, QK^T runs on v_mfma_scale_f32_16x16x128_f8f6f4 with the K codes
+//    and their UE8M0 bytes as the A operand and A scale exactly as loaded:
+//    the FP4 operand layout of that instruction is one (token, 32-channel
+//    group) per lane.  Two query terms per MFMA sit in columns c and c + 8;
+//    one DPP row rotate adds the halves.  The FP8 comparator converts K to
+//    bf16 (exact) for bf16 MFMAs against the hi/lo query.  Scores come out
+//    transposed (S^T: tokens x query rows), which is directly the A operand
+//    layout of the PV product.
+//  * V codes are converted with their scale (gfx950 scaled converts, two
 //    values per instruction) into a wave-private bf16 LDS tile and read back
 //    transposed with ds_read_b64_tr_b16 as the B operand of PV; P is split
 //    into bf16 hi + lo (8 rows each in the 16 MFMA rows).  fp32 accumulation.
@@ -31,8 +38,9 @@
 //  * Codes are prefetched through a ring of kRing tile pairs held in
 //    registers; refills are unconditional (clamped to the last tile) so the
 //    memory wait counts stay exact.
-//  * Context split into `splits` ranges; partial (m, l, O) go to the
-//    workspace and a merge kernel combines them, normalises, rotates back.
+//  * merge_kernel, one wave per query row: partial (m, l, O) of the context
+//    splits are combined, normalised and rotated back.  The planner picks
+//    the split count that fills the device's resident wave slots once.
 #include <atomic>
 
 #include "kvq_device.h"

@@ -138,3 +138,25 @@ def assert_close(got: np.ndarray, want: np.ndarray, what: str = ""):
     assert max_abs <= MAX_ABS and rel <= REL_L2, \
         "%s: max_abs %.3g (<= %.1g), rel_l2 %.3g (<= %.1g)" % (what, max_abs, MAX_ABS, rel, REL_L2)
     return max_abs, rel
+
+
+def oracle_decode_pairs(filled: Filled, q_host: np.ndarray, pairs, threads: int = 16,
+                        sm_scale=None) -> Dict[tuple, np.ndarray]:
+    """Oracle outputs {(b, kv_head): [n_q, group, d] float64} for sampled
+    (sequence, KV head) pairs, computed on host threads (the oracle's C code
+    runs without the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+    wl = filled.wl
+    g = wl.group
+    rotate = filled.cache.rotate
+    sm = 1.0 / math.sqrt(wl.head_dim) if sm_scale is None else sm_scale
+
+    def one(bh):
+        b, h = bh
+        k = np.ascontiguousarray(filled.host["k"][b][:, h:h + 1])
+        v = None if wl.kv_shared else np.ascontiguousarray(filled.host["v"][b][:, h:h + 1])
+        return bh, oracle.reference_decode_seq(q_host[b][:, h * g:(h + 1) * g], k, v, filled.fmt,
+                                               rotate, sm)
+
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        return dict(ex.map(one, list(pairs)))

@@ -271,6 +271,32 @@ def main():
             "byte_ratio": round(kv_fp8 / kv_fp4, 4),
         }
 
+    # ---------------- bulk append: one sequence's whole context, re-appended
+    # (rewrites identical codes), FP4
+    b0 = 0
+    n_sh0 = plan.n_shared_pages[b0] * P
+    L0 = int(plan.context_lens[b0]) - n_sh0
+    kv0 = {t: syn.private_tokens(wl, t, b0, L0, dev) for t in syn.tensor_names(wl)}
+    sl0 = torch_from(syn.slots_for(plan.private_pages[b0], L0, P), dev)
+    torch.cuda.synchronize()
+    app_ms = []
+    for r in range(12):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        kvq.rotate_quantize_append(c4s[r % R], kv0["k"], kv0.get("v"), sl0, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        app_ms.append(a.elapsed_time(b))
+    app_t = statistics.median(app_ms[2:])
+    app_bytes = L0 * H * n_t * (2 * D + D // 2 + D // 32) + L0 * 4
+    append_bulk = {
+        "tokens": L0, "ms": round(app_t, 4),
+        "bytes": app_bytes, "gbs": round(app_bytes / (app_t * 1e-3) / 1e9, 1),
+        "hbm_frac": round(app_bytes / (app_t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "note": "bf16 K and V read, FP4 codes + scales written, slot ids read",
+    }
+    del kv0
+
     if args.copy_calibration:
         # torch's elementwise kernel: reads 512 MiB, writes 512 MiB
         src = torch.ones(1 << 27, dtype=torch.float32, device=dev)
@@ -317,6 +343,7 @@ def main():
             "bytes_per_launch": dec_alg,
         },
         "fp8_comparator": fp8,
+        "append_bulk": append_bulk,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)

@@ -51,6 +51,9 @@ int check_desc(const kvq_cache_desc* d, CacheGeom* g) {
 int check_cache_ptrs(const kvq_cache_desc* d) {
   if (!d->k_codes || !d->k_scales) return KVQ_ERR_NULL;
   if (!d->kv_shared && (!d->v_codes || !d->v_scales)) return KVQ_ERR_NULL;
+  // code arrays are read and written in 16-byte (token, group) units
+  if ((uintptr_t)d->k_codes & 15u) return KVQ_ERR_SHAPE;
+  if (!d->kv_shared && ((uintptr_t)d->v_codes & 15u)) return KVQ_ERR_SHAPE;
   return KVQ_OK;
 }
 

@@ -14,8 +14,6 @@
 namespace kvq {
 namespace {
 
-constexpr int kMaxD = 1024;
-
 // E2M1 code (bit 3 = sign) of y in a group with scale exponent e_s: round
 // |y| * 2^-e_s to the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6, a tie going to
 // the even code, saturating at 6.  The thresholds are the midpoints; ">="
@@ -54,57 +52,123 @@ struct AppendParams {
   const uint16_t* k_new;
   const uint16_t* v_new;
   const int32_t* slots;
+  int n_tokens;
   float norm;
 };
 
-// One wave per (token, KV head, tensor).
-__global__ __launch_bounds__(64) void append_kernel(const AppendParams p) {
-  __shared__ float x[kMaxD];
-  __shared__ int gexp[kMaxD / 32];
-  const int tid = threadIdx.x;
-  const int tok = blockIdx.x;
+// One wave covers 64 / G tokens of one (KV head, tensor) for vectors of
+// G = D / 32 channel groups: lane l holds the 32 channels of group l % G of
+// token l / G.  Stages h = 1 .. 16 of the transform run inside the lane;
+// stage h >= 32 pairs lane l with lane l ^ (h / 32).  Every stage is the fp32
+// a + b / a - b of the radix-2 definition, in stage order, followed by one
+// multiply by fp32(1/sqrt(D)): the operations and their order are those of
+// the definition, so the codes are reproducible bit for bit.  The group's
+// amax, scale byte and codes are then all lane-local: 16 code bytes (FP4)
+// or 32 (FP8) leave in 16-byte stores, and the tokens of a wave that share a
+// page fill whole 16-token runs of each group.
+template <int G>
+__global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
+  constexpr int TW = 64 / G;  // tokens per wave
+  constexpr int D = 32 * G;
+  const CacheGeom& c = p.c;
+  const int lane = threadIdx.x & 63;
+  const int g = lane & (G - 1);
+  const int tok = (blockIdx.x * 4 + (threadIdx.x >> 6)) * TW + lane / G;
   const int h = blockIdx.y;
   const int tensor = blockIdx.z;
-  const int slot = p.slots[tok];
-  if (slot < 0) return;
-  const CacheGeom& c = p.c;
-  const int d = c.d;
-  const uint16_t* src = (tensor == 0 ? p.k_new : p.v_new) + ((size_t)tok * c.hkv + h) * d;
-  for (int i = tid; i < d; i += 64) x[i] = bf16_to_f32(src[i]);
-  __syncthreads();
-  if (c.rotate) fwht_rows_lds(x, 1, d, p.norm, tid, 64);
+  const bool valid = tok < p.n_tokens;
+  const int slot = valid ? p.slots[tok] : -1;
+
+  float x[32];
+  const uint16_t* base = tensor == 0 ? p.k_new : p.v_new;
+  if (valid) {
+    const uint16_t* src = base + ((size_t)tok * c.hkv + h) * D + 32 * g;
+    if (((uintptr_t)base & 15) == 0) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(src + 8 * k);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[8 * k + 2 * e] = as_f32(w[e] << 16);
+          x[8 * k + 2 * e + 1] = as_f32(w[e] & 0xFFFF0000u);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) x[i] = bf16_to_f32(src[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = 0.0f;
+  }
+
+  if (c.rotate) {
+#pragma unroll
+    for (int hh = 1; hh < 32; hh <<= 1) {
+#pragma unroll
+      for (int j = 0; j < 32; ++j) {
+        if (!(j & hh)) {
+          const float a = x[j];
+          const float b = x[j + hh];
+          x[j] = a + b;
+          x[j + hh] = a - b;
+        }
+      }
+    }
+#pragma unroll
+    for (int s = 1; s < G; s <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const float y = __shfl_xor(x[i], s, 64);
+        x[i] = (g & s) ? (y - x[i]) : (x[i] + y);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = x[i] * p.norm;
+  }
+  if (slot < 0) return;  // no shuffles below
+
+  // Scale exponent: floor(log2 amax) is the exponent field of amax (a
+  // subnormal or zero amax has field 0); byte = max(field - emax, 0).
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(x[i]));
+  const bool fp4 = c.fmt == KVQ_FMT_FP4_E2M1;
+  const int field = (int)((as_u32(am) >> 23) & 0xFFu);
+  const int byte = max(field - (fp4 ? 2 : 8), 0);
+  const int e_s = byte - 127;
 
   const int page = slot / c.p;
   const int off = slot - page * c.p;
-  uint8_t* codes = (tensor == 0 ? p.kc : p.vc) + (int64_t)page * c.c_page + (int64_t)h * c.c_head;
+  const int64_t unit = (int64_t)g * c.p + off;  // (group, offset) inside the (page, head) block
+  uint8_t* codes = (tensor == 0 ? p.kc : p.vc) + (int64_t)page * c.c_page + (int64_t)h * c.c_head + unit * c.cb;
   uint8_t* scales = (tensor == 0 ? p.ks : p.vs) + (int64_t)page * c.s_page + (int64_t)h * c.s_head;
-  const int emax = (c.fmt == KVQ_FMT_FP4_E2M1) ? 2 : 8;
-
-  // Scale exponent per group: floor(log2 amax) is the exponent field of amax
-  // (a subnormal or zero amax has field 0); byte = max(field - emax, 0).
-  for (int g = tid; g < c.g; g += 64) {
-    float amax = 0.0f;
-    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[32 * g + i]));
-    const int field = (int)((as_u32(amax) >> 23) & 0xFFu);
-    const int byte = max(field - emax, 0);
-    gexp[g] = byte - 127;
-    scales[(int64_t)g * c.p + off] = (uint8_t)byte;
-  }
-  __syncthreads();
-
-  if (c.fmt == KVQ_FMT_FP4_E2M1) {
-    for (int b = tid; b < d / 2; b += 64) {
-      const int g = b >> 4;
-      const int i = b & 15;
-      const int e_s = gexp[g];
-      const uint32_t lo = e2m1_code(x[32 * g + 2 * i], e_s);
-      const uint32_t hi = e2m1_code(x[32 * g + 2 * i + 1], e_s);
-      codes[((int64_t)g * c.p + off) * 16 + i] = (uint8_t)(lo | (hi << 4));
+  scales[unit] = (uint8_t)byte;
+  if (fp4) {
+    u32x4_t w;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      uint32_t d = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 8 * k + 2 * e;
+        d |= (e2m1_code(x[i], e_s) | (e2m1_code(x[i + 1], e_s) << 4)) << (8 * e);
+      }
+      w[k] = d;
     }
+    *reinterpret_cast<u32x4_t*>(codes) = w;
   } else {
-    for (int ch = tid; ch < d; ch += 64) {
-      const int g = ch >> 5;
-      codes[((int64_t)g * c.p + off) * 32 + (ch & 31)] = (uint8_t)e4m3_code(x[ch], gexp[g]);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      u32x4_t w;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        uint32_t d = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) d |= e4m3_code(x[16 * half + 4 * k + e], e_s) << (8 * e);
+        w[k] = d;
+      }
+      *reinterpret_cast<u32x4_t*>(codes + 16 * half) = w;
     }
   }
 }
@@ -177,9 +241,20 @@ hipError_t launch_append(const CacheGeom& c, uint8_t* kc, uint8_t* ks, uint8_t* 
   p.k_new = k_new;
   p.v_new = v_new;
   p.slots = slots;
+  p.n_tokens = n_tokens;
   p.norm = fwht_norm(c.d);
-  dim3 grid((unsigned)n_tokens, (unsigned)c.hkv, c.kv_shared ? 1u : 2u);
-  hipLaunchKernelGGL(append_kernel, grid, dim3(64), 0, stream, p);
+  const int G = c.d / 32;
+  const long long chunks = ((long long)n_tokens * G + 63) / 64;  // waves per (head, tensor)
+  const dim3 grid((unsigned)((chunks + 3) / 4), (unsigned)c.hkv, c.kv_shared ? 1u : 2u);
+  switch (G) {
+    case 1: hipLaunchKernelGGL((append_kernel<1>), grid, dim3(256), 0, stream, p); break;
+    case 2: hipLaunchKernelGGL((append_kernel<2>), grid, dim3(256), 0, stream, p); break;
+    case 4: hipLaunchKernelGGL((append_kernel<4>), grid, dim3(256), 0, stream, p); break;
+    case 8: hipLaunchKernelGGL((append_kernel<8>), grid, dim3(256), 0, stream, p); break;
+    case 16: hipLaunchKernelGGL((append_kernel<16>), grid, dim3(256), 0, stream, p); break;
+    case 32: hipLaunchKernelGGL((append_kernel<32>), grid, dim3(256), 0, stream, p); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

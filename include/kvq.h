@@ -90,7 +90,8 @@ extern "C" {
 typedef void *kvq_stream_t;
 
 /* Description of one paged cache.  The code and scale arrays are caller-owned
- * device memory of kvq_cache_code_bytes / kvq_cache_scale_bytes bytes each.
+ * device memory of kvq_cache_code_bytes / kvq_cache_scale_bytes bytes each;
+ * code arrays must be 16-byte aligned (KVQ_ERR_SHAPE otherwise).
  *   format       KVQ_FMT_FP4_E2M1 or KVQ_FMT_FP8_E4M3
  *   rotate       1: vectors are Walsh-Hadamard rotated before quantisation
  *   kv_shared    1: values are the keys (latent cache); v_* are ignored

@@ -105,6 +105,17 @@ def test_decode_argument_errors():
     assert _decode(B=0) == 0                     # empty batch: nothing enqueued
 
 
+def test_misaligned_code_array_is_rejected():
+    L = kvq.library()
+    d = _desc()
+    d.v_codes = ctypes.c_void_p(0x1008)
+    assert L.kvq_rotate_quantize_append(ctypes.byref(d), 0x10, 0x20, 0x30, 4, None) == -2
+    assert _decode(desc=d) == -2
+    d = _desc()
+    d.k_codes = ctypes.c_void_p(0x1004)
+    assert L.kvq_rotate_quantize_append(ctypes.byref(d), 0x10, 0x20, 0x30, 4, None) == -2
+
+
 def test_decode_workspace_checks():
     L = kvq.library()
     d = _desc()

@@ -31,6 +31,8 @@ SOURCES = {
     # keep MFMA accumulators in VGPRs: the softmax rescale touches them with
     # VALU ops, and AGPR placement costs a copy per access
     "kvq_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    # head_dim 512: the accumulators need the AGPR half of the register file
+    "kvq_decode512.hip": [],
 }
 
 

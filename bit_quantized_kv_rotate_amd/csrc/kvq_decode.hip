@@ -43,8 +43,7 @@
 //    the split count that fills the device's resident wave slots once.
 #include <atomic>
 
-#include "kvq_device.h"
-#include "kvq_internal.h"
+#include "kvq_decode_common.h"
 
 namespace kvq {
 namespace {
@@ -54,38 +53,6 @@ constexpr int kQTerms = 6;           // FP6 (E2M3) terms of the pre-scaled query
 constexpr int kQMfma = kQTerms / 2;  // scaled MFMAs per tile and row tile
 constexpr int kVRow = 2 * kD + 32;   // LDS bytes per token row of V (bf16, padded)
 constexpr int kRing = 2;             // tile pairs held in registers per wave
-
-typedef int i32x8_t __attribute__((ext_vector_type(8)));
-
-struct DecodeParams {
-  const uint8_t* kc;
-  const uint8_t* ks;
-  const uint8_t* vc;
-  const uint8_t* vs;
-  int64_t c_head, c_page, s_head, s_page;
-  int P;
-  int p_shift;  // log2(P)
-  int hkv;
-  const uint16_t* q;
-  int hq, n_q, group, rows;
-  const int32_t* block_tables;
-  int max_pages;
-  const int32_t* context_lens;
-  float qscale;
-  float norm;
-  int rotate_q, rotate_out;
-  int splits, tiles_per_split;
-  float* out;
-  float* ws_o;       // [B][hkv][splits][8*NT][kD]
-  float* ws_ml;      // [B][hkv][splits][8*NT][2]
-  uint32_t* qops;    // [B][hkv][NT][QOpsLayout::kSlots][64 lanes][kDwords]
-};
-
-template <int FMT>
-struct Fmt {
-  static constexpr bool kFP4 = FMT == KVQ_FMT_FP4_E2M1;
-  static constexpr int kWords = kFP4 ? 4 : 8;      // uint32 of codes per (token, group)
-};
 
 // Query operands of the score product.
 //  FP4 cache: kQTerms FP6 terms for the scaled MFMA (6 packed dwords + scale).
@@ -111,84 +78,6 @@ struct QOpsLayout {
   static constexpr int kDwords = (FMT == KVQ_FMT_FP4_E2M1) ? 8 : 4;
 };
 
-// Dequantise one (token, 32-channel group) into 16 packed bf16x2 words
-// (channel order 0..31), applying the group's power-of-two scale.
-template <int FMT>
-__device__ __forceinline__ void dequant_group(const uint32_t (&w)[Fmt<FMT>::kWords], float scale,
-                                              uint32_t (&o)[16]) {
-  if constexpr (Fmt<FMT>::kFP4) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      o[4 * i + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 0));
-      o[4 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 1));
-      o[4 * i + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 2));
-      o[4 * i + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 3));
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      o[2 * i + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], scale, false));
-      o[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], scale, true));
-    }
-  }
-}
-
-__device__ __forceinline__ float dpp_ror8(float x) {
-  return as_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u32(x), 0x128, 0xF, 0xF, false));
-}
-
-// max over lanes l, l^16, l^32, l^48 (VALU lane swaps, no LDS traffic)
-__device__ __forceinline__ float quad_max(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(as_u32(x), as_u32(x), false, false);
-  x = fmaxf(as_f32(a[0]), as_f32(a[1]));
-  auto b = __builtin_amdgcn_permlane32_swap(as_u32(x), as_u32(x), false, false);
-  return fmaxf(as_f32(b[0]), as_f32(b[1]));
-}
-
-__device__ __forceinline__ float quad_sum(float x) {
-  auto a = __builtin_amdgcn_permlane16_swap(as_u32(x), as_u32(x), false, false);
-  x = as_f32(a[0]) + as_f32(a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap(as_u32(x), as_u32(x), false, false);
-  return as_f32(b[0]) + as_f32(b[1]);
-}
-
-// x + (the value in lane l ^ 32)
-__device__ __forceinline__ float add_half_swap(float x) {
-  auto b = __builtin_amdgcn_permlane32_swap(as_u32(x), as_u32(x), false, false);
-  return as_f32(b[0]) + as_f32(b[1]);
-}
-
-// Round y * 2^-e onto FP6 E2M3 (1 sign, 2 exponent bits with bias 1, 3
-// mantissa bits; largest 7.5), nearest even, saturating.  Returns the 6-bit
-// code (bit 5 = sign) and, in `val`, the value it stands for (code * 2^e), so
-// y - val is the exact residual.
-__device__ __forceinline__ uint32_t e2m3_split(float y, int e, float& val) {
-  const float a = fabsf(ldexpf(y, -e));
-  float r;
-  uint32_t code;
-  if (a < 1.0f) {
-    const float m = rintf(a * 8.0f);  // 0..8; 8 is the smallest normal
-    code = (uint32_t)m;
-    r = m * 0.125f;
-  } else {
-    uint32_t u = as_u32(a);
-    u += 0x7FFFFu + ((u >> 20) & 1u);
-    u &= 0xFFF00000u;
-    const int ex = (int)(u >> 23) - 127;
-    const uint32_t mm = (u >> 20) & 7u;
-    if (ex > 2) {
-      code = 31u;
-      r = 7.5f;
-    } else {
-      code = ((uint32_t)(ex + 1) << 3) | mm;
-      r = as_f32(u);
-    }
-  }
-  const uint32_t sign = as_u32(y) & 0x80000000u;
-  val = as_f32(as_u32(ldexpf(r, e)) | sign);
-  return code | (sign >> 26);
-}
-
 template <int FMT>
 struct RawTile {
   uint32_t k[Fmt<FMT>::kWords];
@@ -208,14 +97,6 @@ __device__ __forceinline__ LaneOffsets lane_offsets(const DecodeParams& p, int l
   constexpr int kBytes = Fmt<FMT>::kWords * 4;
   const uint32_t idx = (uint32_t)((lane >> 4) * p.P + (lane & 15));
   return LaneOffsets{idx * kBytes, idx};
-}
-
-// Buffer resource over one (page, KV head) block: loads through it take a
-// scalar base, a scalar in-page offset and the lane's constant offset, and
-// reads past the block return zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t* base, int64_t off,
-                                                             int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc((void*)(base + off), 0, (int)bytes, 0x00020000);
 }
 
 // Loads of one 16-token tile (all addressing scalar except the lane offset).
@@ -425,30 +306,6 @@ __device__ __forceinline__ void compute_pair(const DecodeParams& p, const int32_
   }
 }
 
-// Walsh-Hadamard transform of one 128-channel row held by a wave, lane l
-// holding channels 2l and 2l + 1: stage h = 1 in the lane, stage h >= 2
-// between lanes l and l ^ (h / 2); fp32 a + b and a - b in the order of the
-// radix-2 definition, then one multiply by c.
-__device__ __forceinline__ void wave_fwht128(float& x0, float& x1, int lane, float c) {
-  const float a = x0;
-  x0 = a + x1;
-  x1 = a - x1;
-#pragma unroll
-  for (int hs = 1; hs < 64; hs <<= 1) {
-    const float y0 = __shfl_xor(x0, hs, 64);
-    const float y1 = __shfl_xor(x1, hs, 64);
-    if (lane & hs) {
-      x0 = y0 - x0;
-      x1 = y1 - x1;
-    } else {
-      x0 = x0 + y0;
-      x1 = x1 + y1;
-    }
-  }
-  x0 = x0 * c;
-  x1 = x1 * c;
-}
-
 // Query prologue, once per query row: load the row, rotate it with the fp32
 // transform, pre-scale by sm_scale * log2 e, and store the score-MFMA
 // operands the page-scan lanes will hold (FP6 terms for the FP4 cache, bf16
@@ -477,7 +334,12 @@ __global__ __launch_bounds__(256) void qprep_kernel(const DecodeParams p) {
     x0 = bf16_to_f32(src[0]);
     x1 = bf16_to_f32(src[1]);
   }
-  if (p.rotate_q) wave_fwht128(x0, x1, lane, p.norm);
+  if (p.rotate_q) {
+    float xr[2] = {x0, x1};
+    wave_fwht<2>(xr, lane, p.norm);
+    x0 = xr[0];
+    x1 = xr[1];
+  }
   x0 = x0 * p.qscale;
   x1 = x1 * p.qscale;
 
@@ -682,60 +544,9 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
   }
 }
 
-// Combine the split partials of each query row: weights 2^(m_s - M),
-// normalise by the combined sum, rotate back, store.  One wave per row
-// (four per block); lane s < S holds split s's (m, l), lane l accumulates
-// channels 2l and 2l + 1 over the splits.
-constexpr int kMaxSplits = 64;
 constexpr int kMinTilesPerSplit = 8;     // 128 tokens
 constexpr int kDefaultWaveSlots = 2048;  // MI355X: 256 CUs x 8 resident waves
 constexpr int kMaxDevices = 64;
-
-template <int NT>
-__global__ __launch_bounds__(256) void merge_kernel(const DecodeParams p) {
-  constexpr int ROWS = 8 * NT;
-  const int lane = threadIdx.x & 63;
-  const int gr = blockIdx.x * 4 + (threadIdx.x >> 6);  // grid covers exactly B * hkv * ROWS
-  const int r = gr % ROWS;
-  const int bh = gr / ROWS;
-  if (r >= p.rows) return;  // padding row: the whole wave leaves (no barrier follows)
-  const int kvh = bh % p.hkv;
-  const int b = bh / p.hkv;
-  const int S = p.splits;
-  const size_t row0 = (size_t)bh * S * ROWS + r;  // split s: row0 + s * ROWS
-
-  float ms = -INFINITY, ls = 0.0f;
-  if (lane < S) {
-    ms = p.ws_ml[(row0 + (size_t)lane * ROWS) * 2 + 0];
-    ls = p.ws_ml[(row0 + (size_t)lane * ROWS) * 2 + 1];
-  }
-  float M = ms;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-  const float ws = (M != -INFINITY) ? __builtin_amdgcn_exp2f(ms - M) : 0.0f;
-  float lsum = ws * ls;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) lsum += __shfl_xor(lsum, o, 64);
-
-  float a0 = 0.0f, a1 = 0.0f;
-  const float* po = p.ws_o + row0 * kD + 2 * lane;
-#pragma unroll 8
-  for (int sp = 0; sp < S; ++sp) {
-    const float w = as_f32((uint32_t)__builtin_amdgcn_readlane((int)as_u32(ws), sp));
-    const f32x2_t o = *reinterpret_cast<const f32x2_t*>(po + (size_t)sp * ROWS * kD);
-    a0 += w * o[0];
-    a1 += w * o[1];
-  }
-  const float inv = (lsum > 0.0f) ? 1.0f / lsum : 0.0f;
-  a0 *= inv;
-  a1 *= inv;
-  if (p.rotate_out) wave_fwht128(a0, a1, lane, p.norm);
-  const int j = r / p.group;
-  const int hh = r - j * p.group;
-  float* dst = p.out + (((size_t)b * p.n_q + j) * p.hq + (size_t)kvh * p.group + hh) * kD + 2 * lane;
-  dst[0] = a0;
-  dst[1] = a1;
-}
 
 template <int FMT, int NT>
 hipError_t launch_nt(const DecodeParams& p, int batch, hipStream_t stream) {
@@ -748,7 +559,7 @@ hipError_t launch_nt(const DecodeParams& p, int batch, hipStream_t stream) {
   hipLaunchKernelGGL((decode_kernel<FMT, NT>), grid, dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
-  hipLaunchKernelGGL((merge_kernel<NT>), dim3(qblocks), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((merge_kernel<8 * NT, 2>), dim3(qblocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -802,6 +613,7 @@ int resident_waves(int fmt, int row_tiles) {
 
 int plan_decode(const CacheGeom& c, int batch, int hq, int n_q, int max_context_len, uint32_t flags,
                 DecodePlan* plan) {
+  if (c.d == 512) return plan_decode512(c, batch, hq, n_q, max_context_len, flags, plan);
   if (c.d != kD) return KVQ_ERR_UNSUPPORTED;
   const int group = hq / c.hkv;
   const int rows = group * n_q;
@@ -844,6 +656,7 @@ int plan_decode(const CacheGeom& c, int batch, int hq, int n_q, int max_context_
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  if (a.c.d == 512) return launch_decode512(a, stream);
   DecodeParams p;
   p.kc = a.c.kc;
   p.ks = a.c.ks;

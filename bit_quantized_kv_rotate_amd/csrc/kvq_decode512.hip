@@ -1,0 +1,544 @@
+// Decode attention over a latent-width FP4 cache: head_dim 512, keys and
+// values from the same rotated latent vectors (or separate ones), up to 64
+// query rows per KV head (absorbed query heads x MTP positions).
+//
+// Method: ROCm blog "UltraQuant on AMD Instinct", section "What is
+// UltraQuant?" (FP4 codes and their power-of-two scales straight into the
+// scaled MFMA); the latent width and the absorbed query heads are the shape
+// of the MLA-style models the blog's serving stack runs.
+//
+// At 64 rows x 512 channels the step is MFMA-bound, not HBM-bound: the query
+// operands (four FP6 terms) and the output accumulators of 64 rows do not fit
+// one wave, and the bf16 V operands must be shared.  One block of 8 waves
+// per (sequence, KV head, context split):
+//  * wave w is the score owner of rows 8w .. 8w + 7 (QK^T on the scaled
+//    MFMA, online softmax, P split into bf16 hi + lo);
+//  * wave w converts one 128-channel quarter of one tile of each tile pair
+//    to bf16 into the shared LDS tile;
+//  * wave w accumulates O for all rows over channels 64w .. 64w + 63.  The
+//    PV product puts hi and lo of P in the contraction (k = 16 tokens x
+//    {hi, lo}), so one accumulator holds 16 full rows.
+// P (as ready MFMA A operands), the rescale factors and V pass through LDS,
+// double-buffered by tile-pair parity: one barrier per pair.
+#include <atomic>
+
+#include "kvq_decode_common.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kD5 = 512;
+constexpr int kT5 = 4;               // FP6 query terms
+constexpr int kM5 = kT5 / 2;         // scaled MFMAs per 128-channel block (two terms each)
+constexpr int kW5 = 8;               // waves per block
+constexpr int kVRow5 = 2 * kD5 + 32;  // LDS bytes per bf16 token row (padded)
+constexpr int kMaxRG5 = 4;           // 16-row groups (64 rows)
+
+// Raw codes of one 16-token tile as this wave needs them: all four K chunks
+// (chunk c = channel groups 4c .. 4c + 3; lane l holds token l%16, group
+// 4c + l/16) and, for a separate V cache, the one V chunk it converts.
+struct Tile5 {
+  uint32_t k[4][4];
+  uint32_t ksc[4];
+  uint32_t v[4];
+  uint32_t vsc;
+};
+
+template <bool SHARED>
+__device__ __forceinline__ void load_tile5(const DecodeParams& p, const int32_t* bt_row, int kvh,
+                                           int tile, int lane, int vchunk, Tile5& t) {
+  const int tok = tile * 16;
+  const int page = __builtin_amdgcn_readfirstlane(bt_row[tok >> p.p_shift]);
+  const int in_page = tok & (p.P - 1);
+  const int64_t cb = (int64_t)page * p.c_page + (int64_t)kvh * p.c_head;
+  const int64_t sb = (int64_t)page * p.s_page + (int64_t)kvh * p.s_head;
+  const __amdgpu_buffer_rsrc_t rk = block_rsrc(p.kc, cb, p.c_head);
+  const __amdgpu_buffer_rsrc_t rks = block_rsrc(p.ks, sb, p.s_head);
+  const int coff = in_page * 16;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int idx = (4 * c + (lane >> 4)) * p.P + (lane & 15);
+    const u32x4_t a = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, idx * 16, coff, 2));
+#pragma unroll
+    for (int w = 0; w < 4; ++w) t.k[c][w] = a[w];
+    t.ksc[c] = __builtin_amdgcn_raw_buffer_load_b8(rks, idx, in_page, 0);
+  }
+  if constexpr (!SHARED) {
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc(p.vc, cb, p.c_head);
+    const __amdgpu_buffer_rsrc_t rvs = block_rsrc(p.vs, sb, p.s_head);
+    const int idx = (4 * vchunk + (lane >> 4)) * p.P + (lane & 15);
+    const u32x4_t a = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, idx * 16, coff, 2));
+#pragma unroll
+    for (int w = 0; w < 4; ++w) t.v[w] = a[w];
+    t.vsc = __builtin_amdgcn_raw_buffer_load_b8(rvs, idx, in_page, 0);
+  }
+}
+
+// Query prologue for the 512-wide kernel, one wave per query row (rows of a
+// KV head padded to 16 RG): load, rotate, pre-scale, split into kT5 FP6
+// terms per 32-channel block and store the score owner's B operands
+// [B][hkv][2 RG owners][4 blocks][kM5][64 lanes][8 dwords].  Lane l holds
+// channels 8l .. 8l + 7; a 32-channel block is 4 lanes whose 8 six-bit codes
+// (48 bits each) make the block's 192-bit stream.
+template <int RG>
+__global__ __launch_bounds__(256) void qprep512_kernel(const DecodeParams p) {
+  constexpr int ROWS = 16 * RG;
+  constexpr int NO = 2 * RG;  // score owners
+  const int lane = threadIdx.x & 63;
+  const int gr = blockIdx.x * 4 + (threadIdx.x >> 6);  // grid covers exactly B * hkv * ROWS
+  const int r = gr % ROWS;
+  const int bh = gr / ROWS;
+  const int kvh = bh % p.hkv;
+  const int b = bh / p.hkv;
+
+  float x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = 0.0f;
+  if (r < p.rows) {
+    const int j = r / p.group;
+    const int hh = r - j * p.group;
+    const uint16_t* src = p.q + (((size_t)b * p.n_q + j) * p.hq + (size_t)kvh * p.group + hh) * kD5 + 8 * lane;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = bf16_to_f32(src[i]);
+  }
+  if (p.rotate_q) wave_fwht<8>(x, lane, p.norm);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = x[i] * p.qscale;
+
+  const int owner = r >> 3;
+  const int gi = lane >> 2;  // 32-channel group of the lane
+  const int blk = gi >> 2;
+  const int q = gi & 3;
+  const int j4 = lane & 3;
+  const int base = lane & ~3;
+  const int sa = base + min(j4, 2);
+#pragma unroll
+  for (int t = 0; t < kT5; ++t) {
+    float am = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(x[i]));
+    am = fmaxf(am, __shfl_xor(am, 1, 64));
+    am = fmaxf(am, __shfl_xor(am, 2, 64));
+    const int byte = max((int)((as_u32(am) >> 23) & 0xFFu) - 2, 0);
+    const int e = byte - 127;
+    uint64_t bits = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float v;
+      const uint32_t c = e2m3_split(x[i], e, v);
+      x[i] -= v;
+      bits |= (uint64_t)c << (6 * i);
+    }
+    const uint32_t lo = (uint32_t)bits;
+    const uint32_t hi = (uint32_t)(bits >> 32);  // 16 bits
+    const uint32_t alo = (uint32_t)__shfl((int)lo, sa, 64);
+    const uint32_t ahi = (uint32_t)__shfl((int)hi, sa, 64);
+    const uint32_t blo = (uint32_t)__shfl((int)lo, sa + 1, 64);
+    const uint32_t bhi = (uint32_t)__shfl((int)hi, sa + 1, 64);
+    uint32_t d0, d1;
+    if (j4 == 0) {
+      d0 = alo;
+      d1 = ahi | (blo << 16);
+    } else if (j4 == 1) {
+      d0 = (alo >> 16) | (ahi << 16);
+      d1 = blo;
+    } else if (j4 == 2) {
+      d0 = ahi | (blo << 16);
+      d1 = (blo >> 16) | (bhi << 16);
+    } else {
+      d0 = (uint32_t)byte;
+      d1 = 0u;
+    }
+    const int m = t >> 1;
+    const int col = (r & 7) + 8 * (t & 1);
+    uint32_t* dst = p.qops + (((((size_t)bh * NO + owner) * 4 + blk) * kM5 + m) * 64 + 16 * q + col) * 8 + 2 * j4;
+    *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{d0, d1};
+  }
+}
+
+template <int RG, bool SHARED>
+__global__ __launch_bounds__(512) void decode512_kernel(const DecodeParams p) {
+  constexpr int ROWS = 16 * RG;
+  constexpr int NO = 2 * RG;
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[2][2][16][kVRow5];
+  __shared__ __attribute__((aligned(16))) u32x4_t s_p[2][RG][2][64];
+  __shared__ float s_alpha[2][ROWS];
+  __shared__ int s_flag[2][NO];
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int split = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  const int bh = b * p.hkv + kvh;
+  const int L = p.context_lens[b];
+  const int n_tiles = (L + 15) >> 4;
+  const int t_begin = split * p.tiles_per_split;
+  const int t_end = min(n_tiles, t_begin + p.tiles_per_split);
+  const int tok_limit = min(L, t_end * 16);
+  const int col = lane & 15;
+  const int quad = lane >> 4;
+  const int32_t* bt_row = p.block_tables + (size_t)b * p.max_pages;
+  const int n_pairs = (t_end > t_begin) ? ((t_end - t_begin + 1) >> 1) : 0;
+  const bool owner = w < NO;
+  const int vtile = w & 1;   // tile of each pair this wave converts
+  const int vchunk = w >> 1;  // ... and its 128-channel quarter
+
+  Tile5 cur[2];
+  if (n_pairs > 0) {
+    load_tile5<SHARED>(p, bt_row, kvh, t_begin, lane, vchunk, cur[0]);
+    load_tile5<SHARED>(p, bt_row, kvh, min(t_begin + 1, t_end - 1), lane, vchunk, cur[1]);
+  }
+
+  // score owner: query operands of rows 8w .. 8w + 7
+  i32x8_t qb[4][kM5];
+  int qs[4][kM5];
+  if (owner) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int m = 0; m < kM5; ++m) {
+        const uint32_t* src = p.qops + (((((size_t)bh * NO + w) * 4 + c) * kM5 + m) * 64 + lane) * 8;
+        const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(src);
+        const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(src + 4);
+        qb[c][m] = i32x8_t{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], 0, 0};
+        qs[c][m] = (int)a1[2];
+      }
+    }
+  }
+  const int row = 8 * w + (col & 7);  // owner's row in this lane
+  const int row_last = (owner && row < p.rows) ? (L - p.n_q + row / p.group) : -1;
+  const int interior_limit = min(tok_limit, L - p.n_q + 1);
+  const bool hi_col = col < 8;
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  f32x4_t O[RG][4];
+#pragma unroll
+  for (int g = 0; g < RG; ++g)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) O[g][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll 1
+  for (int pi = 0; pi < n_pairs; ++pi) {
+    const int par = pi & 1;
+    const int tile = t_begin + 2 * pi;
+    const bool boundary = tile * 16 + 32 > interior_limit;
+
+    // ---- V quarter of one tile -> bf16 LDS rows (zero past the context)
+    {
+      // (wave-uniform selects: no dynamic register indexing)
+      uint32_t vw[4];
+      uint32_t vsc;
+      if constexpr (SHARED) {
+        // mask-and-or selects over all eight candidates (a conditional
+        // expression over array elements can turn into a scratch access)
+        const uint32_t mt[2] = {vtile ? 0u : ~0u, vtile ? ~0u : 0u};
+        const uint32_t mc[4] = {vchunk == 0 ? ~0u : 0u, vchunk == 1 ? ~0u : 0u, vchunk == 2 ? ~0u : 0u,
+                                vchunk == 3 ? ~0u : 0u};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          uint32_t acc = 0u;
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc |= cur[s].k[c][i] & mt[s] & mc[c];
+          vw[i] = acc;
+        }
+        uint32_t acc = 0u;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc |= cur[s].ksc[c] & mt[s] & mc[c];
+        vsc = acc;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vw[i] = vtile ? cur[1].v[i] : cur[0].v[i];
+        vsc = vtile ? cur[1].vsc : cur[0].vsc;
+      }
+      if (boundary) {
+        const bool dead = (tile + vtile) * 16 + col >= tok_limit;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) vw[i] = dead ? 0u : vw[i];
+        vsc = dead ? 0u : vsc;
+      }
+      uint32_t vb[16];
+      dequant_group<KVQ_FMT_FP4_E2M1>(vw, scale_operand(vsc), vb);
+      u32x4_t* dst = reinterpret_cast<u32x4_t*>(&s_v[par][vtile][col][2 * (128 * vchunk + 32 * quad)]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = u32x4_t{vb[4 * i], vb[4 * i + 1], vb[4 * i + 2], vb[4 * i + 3]};
+    }
+
+    // ---- scores S^T (tokens x (8 rows x 2 terms)) for the owner's rows
+    f32x4_t S[2];
+    if (owner) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const i32x8_t A = {(int)cur[s].k[c][0], (int)cur[s].k[c][1], (int)cur[s].k[c][2], (int)cur[s].k[c][3], 0, 0, 0, 0};
+#pragma unroll
+          for (int m = 0; m < kM5; ++m)
+            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, qb[c][m], acc, 4, 2, 0, (int)cur[s].ksc[c], 0,
+                                                                   qs[c][m]);
+        }
+        S[s] = acc;
+      }
+    }
+
+    // ---- the codes are consumed: fetch the next pair
+    if (pi + 1 < n_pairs) {
+      load_tile5<SHARED>(p, bt_row, kvh, tile + 2, lane, vchunk, cur[0]);
+      load_tile5<SHARED>(p, bt_row, kvh, min(tile + 3, t_end - 1), lane, vchunk, cur[1]);
+    }
+
+    // ---- owner: online softmax, P hi / lo as PV A operands
+    if (owner) {
+      float sc[8];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = S[s][i];
+          sc[4 * s + i] = x + dpp_ror8(x);
+        }
+      }
+      if (boundary) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int tok = (tile + s) * 16 + 4 * quad + i;
+            const bool ok = (tok < tok_limit) && (tok <= row_last);
+            sc[4 * s + i] = ok ? sc[4 * s + i] : -INFINITY;
+          }
+        }
+      }
+      float mloc = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                         fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+      mloc = quad_max(mloc);
+      const float m_old = m_run;
+      const float m_new = fmaxf(m_old, mloc);
+      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+      m_run = m_new;
+      float psum = 0.0f;
+      uint32_t pw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(sc[2 * e] - m_use);
+        const float p1 = __builtin_amdgcn_exp2f(sc[2 * e + 1] - m_use);
+        psum += p0 + p1;
+        const uint32_t u0 = as_u32(p0), u1 = as_u32(p1);
+        const uint32_t h = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+        const uint32_t l = pack_bf16x2(p0 - as_f32(u0 & 0xFFFF0000u), p1 - as_f32(u1 & 0xFFFF0000u));
+        pw[e] = hi_col ? h : l;
+      }
+      // A operand slot: MFMA quad / 2 (token quads {0,1} or {2,3}); lanes
+      // k-group (quad & 1) + 2 * lo, row 8 (w & 1) + (col & 7)
+      const int kg = (quad & 1) + (hi_col ? 0 : 2);
+      s_p[par][w >> 1][quad >> 1][16 * kg + 8 * (w & 1) + (col & 7)] = u32x4_t{pw[0], pw[1], pw[2], pw[3]};
+      const bool moved = __builtin_amdgcn_ballot_w64(m_new != m_old) != 0;
+      if (moved) {
+        const float alpha = __builtin_amdgcn_exp2f(m_old - m_use);
+        l_run *= alpha;
+        if (lane < 8) s_alpha[par][8 * w + lane] = alpha;
+      }
+      if (lane == 0) s_flag[par][w] = moved ? 1 : 0;
+      l_run += psum;
+    }
+    __syncthreads();
+
+    // ---- PV over channels 64w .. 64w + 63 for every row group
+    const int rr = col >> 2;
+    const int c4 = (col & 3) * 4;
+    typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+    auto read_b = [&](int Q, int n) {
+      const int cb = 2 * (64 * w + 16 * n + c4);
+      lds_bf16x4* a0 = (lds_bf16x4*)((__attribute__((address_space(3))) uint8_t*)&s_v[par][0][4 * Q + rr][cb]);
+      lds_bf16x4* a1 = (lds_bf16x4*)((__attribute__((address_space(3))) uint8_t*)&s_v[par][1][4 * Q + rr][cb]);
+      const u32x2_t w0 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(a0));
+      const u32x2_t w1 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(a1));
+      return __builtin_bit_cast(bf16x8_t, u32x4_t{w0[0], w0[1], w1[0], w1[1]});
+    };
+    bf16x8_t A[RG][2];
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+      A[g][0] = __builtin_bit_cast(bf16x8_t, s_p[par][g][0][lane]);
+      A[g][1] = __builtin_bit_cast(bf16x8_t, s_p[par][g][1][lane]);
+      // rows 16g + 4 quad + i belong to owner 2g + (quad >> 1)
+      if (s_flag[par][2 * g] | s_flag[par][2 * g + 1]) {
+        const bool mine = s_flag[par][2 * g + (quad >> 1)] != 0;
+        float ar[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ar[i] = mine ? s_alpha[par][16 * g + 4 * quad + i] : 1.0f;
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) O[g][n][i] *= ar[i];
+      }
+    }
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      const bf16x8_t B0 = read_b(quad & 1, n);
+      const bf16x8_t B1 = read_b(2 + (quad & 1), n);
+#pragma unroll
+      for (int g = 0; g < RG; ++g) {
+        O[g][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][0], B0, O[g][n], 0, 0, 0);
+        O[g][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][1], B1, O[g][n], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- partials: O rows 16g + 4 quad + i, channel 64w + 16n + col; (m, l)
+  const size_t base = ((size_t)bh * p.splits + split) * ROWS;
+#pragma unroll
+  for (int g = 0; g < RG; ++g)
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        p.ws_o[(base + 16 * g + 4 * quad + i) * kD5 + 64 * w + 16 * n + col] = O[g][n][i];
+  const float lrow = quad_sum(l_run);
+  if (owner && lane < 8) {
+    p.ws_ml[(base + 8 * w + lane) * 2 + 0] = m_run;
+    p.ws_ml[(base + 8 * w + lane) * 2 + 1] = lrow;
+  }
+}
+
+constexpr int kMinTilesPerSplit5 = 8;
+constexpr int kDefaultSlots5 = 256;  // MI355X: 256 CUs x 1 block
+constexpr int kMaxDevices5 = 64;
+
+template <int RG, bool SHARED>
+int resident_blocks5(int dev) {
+  static std::atomic<int> cache[kMaxDevices5];
+  if (dev < kMaxDevices5) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int cus = 0, blocks = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode512_kernel<RG, SHARED>, 512, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  const int v = cus * blocks;
+  if (dev < kMaxDevices5) cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+int resident_slots5(int rg, bool shared) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  switch (rg) {
+    case 1: return shared ? resident_blocks5<1, true>(dev) : resident_blocks5<1, false>(dev);
+    case 2: return shared ? resident_blocks5<2, true>(dev) : resident_blocks5<2, false>(dev);
+    case 3: return shared ? resident_blocks5<3, true>(dev) : resident_blocks5<3, false>(dev);
+    case 4: return shared ? resident_blocks5<4, true>(dev) : resident_blocks5<4, false>(dev);
+    default: return 0;
+  }
+}
+
+template <int RG, bool SHARED>
+hipError_t launch5(const DecodeParams& p, int batch, hipStream_t stream) {
+  const unsigned qblocks = (unsigned)((size_t)batch * p.hkv * 16 * RG / 4);
+  hipLaunchKernelGGL((qprep512_kernel<RG>), dim3(qblocks), dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 grid((unsigned)p.splits, (unsigned)p.hkv, (unsigned)batch);
+  hipLaunchKernelGGL((decode512_kernel<RG, SHARED>), grid, dim3(64 * kW5), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((merge_kernel<16 * RG, 8>), dim3(qblocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <bool SHARED>
+hipError_t launch5_rg(const DecodeParams& p, int rg, int batch, hipStream_t stream) {
+  switch (rg) {
+    case 1: return launch5<1, SHARED>(p, batch, stream);
+    case 2: return launch5<2, SHARED>(p, batch, stream);
+    case 3: return launch5<3, SHARED>(p, batch, stream);
+    case 4: return launch5<4, SHARED>(p, batch, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+int plan_decode512(const CacheGeom& c, int batch, int hq, int n_q, int max_context_len, uint32_t flags,
+                   DecodePlan* plan) {
+  if (c.d != kD5) return KVQ_ERR_UNSUPPORTED;
+  if (c.fmt != KVQ_FMT_FP4_E2M1) return KVQ_ERR_UNSUPPORTED;
+  const int group = hq / c.hkv;
+  const int rows = group * n_q;
+  const int rg = (rows + 15) / 16;
+  if (rg > kMaxRG5) return KVQ_ERR_UNSUPPORTED;
+  const int n_tiles = (max_context_len + 15) / 16;
+  int splits = (int)((flags & KVQ_SPLITS_MASK) >> KVQ_SPLITS_SHIFT);
+  if (splits <= 0) {
+    // one round of blocks over the device (one block per compute unit)
+    int slots = resident_slots5(rg, c.kv_shared != 0);
+    if (slots <= 0) slots = kDefaultSlots5;
+    const long long units = (long long)batch * c.hkv;
+    long long want = units >= slots ? 1 : slots / units;
+    const long long by_len = n_tiles / kMinTilesPerSplit5;
+    if (want > by_len) want = by_len;
+    splits = (int)(want < 1 ? 1 : want);
+  }
+  if (splits > kMaxSplits) splits = kMaxSplits;
+  int per = (n_tiles + splits - 1) / splits;
+  per = (per + 1) & ~1;
+  if (per < 2) per = 2;
+  splits = (n_tiles + per - 1) / per;
+  if (splits < 1) splits = 1;
+  plan->rows = rows;
+  plan->row_tiles = rg;
+  plan->splits = splits;
+  plan->tiles_per_split = per;
+  plan->qops_bytes = (size_t)batch * c.hkv * (2 * rg) * 4 * kM5 * 64 * 8 * sizeof(uint32_t);
+  plan->workspace = plan->qops_bytes + (size_t)batch * c.hkv * splits * (16 * rg) * (kD5 + 2) * sizeof(float);
+  return KVQ_OK;
+}
+
+hipError_t launch_decode512(const DecodeArgs& a, hipStream_t stream) {
+  DecodeParams p;
+  p.kc = a.c.kc;
+  p.ks = a.c.ks;
+  p.vc = a.c.kv_shared ? a.c.kc : a.c.vc;
+  p.vs = a.c.kv_shared ? a.c.ks : a.c.vs;
+  p.c_head = a.c.c_head;
+  p.c_page = a.c.c_page;
+  p.s_head = a.c.s_head;
+  p.s_page = a.c.s_page;
+  p.P = a.c.p;
+  p.p_shift = __builtin_ctz((unsigned)a.c.p);
+  p.hkv = a.c.hkv;
+  p.q = a.q;
+  p.hq = a.hq;
+  p.n_q = a.n_q;
+  p.group = a.group;
+  p.rows = a.plan.rows;
+  p.block_tables = a.block_tables;
+  p.max_pages = a.max_pages;
+  p.context_lens = a.context_lens;
+  p.qscale = a.qscale;
+  p.norm = fwht_norm(kD5);
+  p.rotate_q = a.rotate_q;
+  p.rotate_out = a.rotate_out;
+  p.splits = a.plan.splits;
+  p.tiles_per_split = a.plan.tiles_per_split;
+  p.out = a.out;
+  const size_t n_o = (size_t)a.batch * a.c.hkv * a.plan.splits * (16 * a.plan.row_tiles) * kD5;
+  uint8_t* ws = reinterpret_cast<uint8_t*>(a.workspace);
+  p.qops = reinterpret_cast<uint32_t*>(ws);
+  p.ws_o = reinterpret_cast<float*>(ws + a.plan.qops_bytes);
+  p.ws_ml = p.ws_o + n_o;
+  if (a.c.kv_shared) return launch5_rg<true>(p, a.plan.row_tiles, a.batch, stream);
+  return launch5_rg<false>(p, a.plan.row_tiles, a.batch, stream);
+}
+
+}  // namespace kvq

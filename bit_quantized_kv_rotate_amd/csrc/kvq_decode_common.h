@@ -1,0 +1,222 @@
+// Pieces shared by the decode kernels (head_dim 128 in kvq_decode.hip, 512
+// in kvq_decode512.hip): kernel parameters, code conversions, lane
+// reductions, the FP6 query split, buffer resources, the wave-level
+// Walsh-Hadamard transform and the split merge.  Everything sits in an
+// anonymous namespace: each translation unit gets its own copy.
+#pragma once
+
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+struct DecodeParams {
+  const uint8_t* kc;
+  const uint8_t* ks;
+  const uint8_t* vc;
+  const uint8_t* vs;
+  int64_t c_head, c_page, s_head, s_page;
+  int P;
+  int p_shift;  // log2(P)
+  int hkv;
+  const uint16_t* q;
+  int hq, n_q, group, rows;
+  const int32_t* block_tables;
+  int max_pages;
+  const int32_t* context_lens;
+  float qscale;
+  float norm;
+  int rotate_q, rotate_out;
+  int splits, tiles_per_split;
+  float* out;
+  float* ws_o;       // [B][hkv][splits][8*NT][kD]
+  float* ws_ml;      // [B][hkv][splits][8*NT][2]
+  uint32_t* qops;    // [B][hkv][NT][QOpsLayout::kSlots][64 lanes][kDwords]
+};
+
+template <int FMT>
+struct Fmt {
+  static constexpr bool kFP4 = FMT == KVQ_FMT_FP4_E2M1;
+  static constexpr int kWords = kFP4 ? 4 : 8;      // uint32 of codes per (token, group)
+};
+
+// Dequantise one (token, 32-channel group) into 16 packed bf16x2 words
+// (channel order 0..31), applying the group's power-of-two scale.
+template <int FMT>
+__device__ __forceinline__ void dequant_group(const uint32_t (&w)[Fmt<FMT>::kWords], float scale,
+                                              uint32_t (&o)[16]) {
+  if constexpr (Fmt<FMT>::kFP4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[4 * i + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 0));
+      o[4 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 1));
+      o[4 * i + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 2));
+      o[4 * i + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[i], scale, 3));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      o[2 * i + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], scale, false));
+      o[2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[i], scale, true));
+    }
+  }
+}
+
+__device__ __forceinline__ float dpp_ror8(float x) {
+  return as_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u32(x), 0x128, 0xF, 0xF, false));
+}
+
+// max over lanes l, l^16, l^32, l^48 (VALU lane swaps, no LDS traffic)
+__device__ __forceinline__ float quad_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(as_u32(x), as_u32(x), false, false);
+  x = fmaxf(as_f32(a[0]), as_f32(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(as_u32(x), as_u32(x), false, false);
+  return fmaxf(as_f32(b[0]), as_f32(b[1]));
+}
+
+__device__ __forceinline__ float quad_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(as_u32(x), as_u32(x), false, false);
+  x = as_f32(a[0]) + as_f32(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(as_u32(x), as_u32(x), false, false);
+  return as_f32(b[0]) + as_f32(b[1]);
+}
+
+// x + (the value in lane l ^ 32)
+__device__ __forceinline__ float add_half_swap(float x) {
+  auto b = __builtin_amdgcn_permlane32_swap(as_u32(x), as_u32(x), false, false);
+  return as_f32(b[0]) + as_f32(b[1]);
+}
+
+// Round y * 2^-e onto FP6 E2M3 (1 sign, 2 exponent bits with bias 1, 3
+// mantissa bits; largest 7.5), nearest even, saturating.  Returns the 6-bit
+// code (bit 5 = sign) and, in `val`, the value it stands for (code * 2^e), so
+// y - val is the exact residual.
+__device__ __forceinline__ uint32_t e2m3_split(float y, int e, float& val) {
+  const float a = fabsf(ldexpf(y, -e));
+  float r;
+  uint32_t code;
+  if (a < 1.0f) {
+    const float m = rintf(a * 8.0f);  // 0..8; 8 is the smallest normal
+    code = (uint32_t)m;
+    r = m * 0.125f;
+  } else {
+    uint32_t u = as_u32(a);
+    u += 0x7FFFFu + ((u >> 20) & 1u);
+    u &= 0xFFF00000u;
+    const int ex = (int)(u >> 23) - 127;
+    const uint32_t mm = (u >> 20) & 7u;
+    if (ex > 2) {
+      code = 31u;
+      r = 7.5f;
+    } else {
+      code = ((uint32_t)(ex + 1) << 3) | mm;
+      r = as_f32(u);
+    }
+  }
+  const uint32_t sign = as_u32(y) & 0x80000000u;
+  val = as_f32(as_u32(ldexpf(r, e)) | sign);
+  return code | (sign >> 26);
+}
+
+// Buffer resource over one (page, KV head) block: loads through it take a
+// scalar base, a scalar in-page offset and the lane's constant offset, and
+// reads past the block return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t* base, int64_t off,
+                                                             int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(base + off), 0, (int)bytes, 0x00020000);
+}
+
+// Walsh-Hadamard transform of one row of D = 64 C channels held by a wave,
+// lane l holding channels C l .. C l + C - 1: stages h < C inside the lane,
+// stage h >= C between lanes l and l ^ (h / C); fp32 a + b and a - b in the
+// order of the radix-2 definition, then one multiply by c.
+template <int C>
+__device__ __forceinline__ void wave_fwht(float (&x)[C], int lane, float c) {
+#pragma unroll
+  for (int hh = 1; hh < C; hh <<= 1) {
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      if (!(j & hh)) {
+        const float a = x[j];
+        const float b = x[j + hh];
+        x[j] = a + b;
+        x[j + hh] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int hs = 1; hs < 64; hs <<= 1) {
+#pragma unroll
+    for (int i = 0; i < C; ++i) {
+      const float y = __shfl_xor(x[i], hs, 64);
+      x[i] = (lane & hs) ? (y - x[i]) : (x[i] + y);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < C; ++i) x[i] = x[i] * c;
+}
+
+constexpr int kMaxSplits = 64;
+
+// Combine the split partials of each query row: weights 2^(m_s - M),
+// normalise by the combined sum, rotate back, store.  One wave per row
+// (four per block, ROWS padded rows per (sequence, KV head)); lane s < S
+// holds split s's (m, l), lane l accumulates channels C l .. C l + C - 1 of
+// the D = 64 C channels over the splits.
+template <int ROWS, int C>
+__global__ __launch_bounds__(256) void merge_kernel(const DecodeParams p) {
+  constexpr int D = 64 * C;
+  const int lane = threadIdx.x & 63;
+  const int gr = blockIdx.x * 4 + (threadIdx.x >> 6);  // grid covers exactly B * hkv * ROWS
+  const int r = gr % ROWS;
+  const int bh = gr / ROWS;
+  if (r >= p.rows) return;  // padding row: the whole wave leaves (no barrier follows)
+  const int kvh = bh % p.hkv;
+  const int b = bh / p.hkv;
+  const int S = p.splits;
+  const size_t row0 = (size_t)bh * S * ROWS + r;  // split s: row0 + s * ROWS
+
+  float ms = -INFINITY, ls = 0.0f;
+  if (lane < S) {
+    ms = p.ws_ml[(row0 + (size_t)lane * ROWS) * 2 + 0];
+    ls = p.ws_ml[(row0 + (size_t)lane * ROWS) * 2 + 1];
+  }
+  float M = ms;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  const float ws = (M != -INFINITY) ? __builtin_amdgcn_exp2f(ms - M) : 0.0f;
+  float lsum = ws * ls;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) lsum += __shfl_xor(lsum, o, 64);
+
+  float acc[C];
+#pragma unroll
+  for (int i = 0; i < C; ++i) acc[i] = 0.0f;
+  const float* po = p.ws_o + row0 * D + C * lane;
+#pragma unroll 4
+  for (int sp = 0; sp < S; ++sp) {
+    const float w = as_f32((uint32_t)__builtin_amdgcn_readlane((int)as_u32(ws), sp));
+    const float* src = po + (size_t)sp * ROWS * D;
+#pragma unroll
+    for (int i = 0; i < C; i += 2) {
+      const f32x2_t o = *reinterpret_cast<const f32x2_t*>(src + i);
+      acc[i] += w * o[0];
+      acc[i + 1] += w * o[1];
+    }
+  }
+  const float inv = (lsum > 0.0f) ? 1.0f / lsum : 0.0f;
+#pragma unroll
+  for (int i = 0; i < C; ++i) acc[i] *= inv;
+  if (p.rotate_out) wave_fwht<C>(acc, lane, p.norm);
+  const int j = r / p.group;
+  const int hh = r - j * p.group;
+  float* dst = p.out + (((size_t)b * p.n_q + j) * p.hq + (size_t)kvh * p.group + hh) * D + C * lane;
+#pragma unroll
+  for (int i = 0; i < C; ++i) dst[i] = acc[i];
+}
+
+}  // namespace
+}  // namespace kvq

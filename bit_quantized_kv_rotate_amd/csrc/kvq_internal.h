@@ -73,4 +73,9 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
+// head_dim 512 (latent width): planned and launched by kvq_decode512.hip
+int plan_decode512(const CacheGeom& c, int batch, int hq, int n_q, int max_context_len, uint32_t flags,
+                   DecodePlan* plan);
+hipError_t launch_decode512(const DecodeArgs& a, hipStream_t stream);
+
 }  // namespace kvq

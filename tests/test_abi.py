@@ -102,6 +102,15 @@ def test_decode_argument_errors():
     assert _decode(fn="kvq_decode_attn_fp8", desc=_desc(fmt=1)) == -3
     assert _decode(desc=_desc(d=64)) == -4       # no kernel for head_dim 64 yet
     assert _decode(hq=8 * 32) == -4              # 32 rows per KV head: not built
+    # latent width 512: FP4 up to 64 rows per KV head; no FP8 kernel at 512
+    d512 = _desc(d=512, hkv=1, p=64, shared=1)
+    L = kvq.library()
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(d512), 16, 64, 1, 131072, 0) > 0
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(d512), 16, 65, 1, 131072, 0) == 0  # 65 rows
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(_desc(fmt=2, d=512, hkv=1, p=64, shared=1)),
+                                        16, 64, 1, 131072, 0) == 0
+    assert _decode(fn="kvq_decode_attn_fp8", desc=_desc(fmt=2, d=512, hkv=1, p=64, shared=1), hq=64) == -4
+    assert _decode(desc=d512, hq=65) == -4
     assert _decode(B=0) == 0                     # empty batch: nothing enqueued
 
 

@@ -155,3 +155,36 @@ def test_decode_repeatable(gpu):
     a = f.decode(q)
     b = f.decode(q)
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("group,n_q,shared,ctx", [
+    (64, 1, True, (300, 1500)),    # absorbed MLA shape: 64 rows, K = V latent
+    (16, 1, True, (1, 130)),       # one row group; contexts inside a tile, pair, page
+    (16, 3, True, (100, 900)),     # MTP: 48 rows with the causal rule
+    (20, 3, True, (64, 700)),      # 60 rows: padded last row group
+    (8, 1, False, (50, 800)),      # separate V cache, 2 KV heads
+])
+def test_decode_latent_512(gpu, group, n_q, shared, ctx):
+    """head_dim 512 (latent width), page 64: the 8-wave kernel."""
+    hkv = 1 if shared else 2
+    wl = syn.Workload("lat_g%d_nq%d_%d" % (group, n_q, int(shared)), batch=3, num_kv_heads=hkv,
+                      num_q_heads=group * hkv, head_dim=512, page_size=64, context=0, n_q=n_q,
+                      kv_shared=shared, std=math.sqrt(0.5), n_outliers=4, outlier_mult=16.0,
+                      ctx_range=ctx)
+    f, qh, out = _run(wl, "fp4")
+    want = oracle_decode_batch(f, qh)
+    for b in range(wl.batch):
+        assert_close(out[b], want[b], "latent g%d n_q%d seq %d (L=%d)" % (group, n_q, b, int(f.plan.context_lens[b])))
+
+
+def test_decode_latent_512_split_invariance(gpu):
+    wl = syn.Workload("lat_split", batch=1, num_kv_heads=1, num_q_heads=64, head_dim=512, page_size=64,
+                      context=2048, kv_shared=True, std=math.sqrt(0.5), n_outliers=4, outlier_mult=16.0)
+    f = Filled(wl, "fp4")
+    q = syn.queries(wl).cuda()
+    ref = f.decode(q, flags=kvq.splits_flag(1)).cpu().numpy()
+    for s in (2, 3, 7, 16):
+        got = f.decode(q, flags=kvq.splits_flag(s)).cpu().numpy()
+        np.testing.assert_allclose(got, ref, rtol=1e-5, atol=5e-5)
+    want = oracle_decode_batch(f, syn.bf16_bits(q))
+    assert_close(ref[0], want[0], "latent one split")

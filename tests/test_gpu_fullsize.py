@@ -7,6 +7,8 @@ compared element by element (max |err| <= 2e-3, relative L2 <= 1e-3).
                  (FP4 cache and the FP8 comparator)
   mtp_mixed_b32  batch 32, contexts 4K-128K log-uniform, 92% of pages shared
                  from 4 prefixes, 3 MTP verify positions (24 rows per KV head)
+  mla_b16_l128k  batch 16, one latent head of width 512 (K = V), 64 absorbed
+                 query heads, context 131072, page 64
 """
 import numpy as np
 import pytest
@@ -23,7 +25,7 @@ def _pairs(wl, n, seed):
     sequence and every KV head at least once when n allows."""
     rng = np.random.default_rng(seed)
     pairs = {(0, 0), (wl.batch - 1, wl.num_kv_heads - 1)}
-    for h in range(wl.num_kv_heads):
+    for h in range(min(wl.num_kv_heads, n - 2)):
         pairs.add((int(rng.integers(wl.batch)), h))
     while len(pairs) < n:
         pairs.add((int(rng.integers(wl.batch)), int(rng.integers(wl.num_kv_heads))))
@@ -57,3 +59,8 @@ def test_fullsize_b32_l32k_sampled(gpu, fmt):
 
 def test_fullsize_mtp_mixed_b32_sampled(gpu):
     _check("mtp_mixed_b32", "fp4", 16, 2)
+
+
+def test_fullsize_mla_b16_l128k_sampled(gpu):
+    """Four whole sequences (all 64 rows) of the latent workload."""
+    _check("mla_b16_l128k", "fp4", 4, 3)

@@ -34,7 +34,7 @@ WORKLOAD = "b32_l32k"
 # scaled by a plain copy kernel; valid only for the kernel source it names.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_fp4_b32_l32k_hbm_traffic.md")
 KERNEL_SOURCES = [os.path.join(ROOT, "bit_quantized_kv_rotate_amd", "csrc", f)
-                  for f in ("kvq_decode.hip", "kvq_device.h")]
+                  for f in ("kvq_decode.hip", "kvq_decode_common.h", "kvq_device.h")]
 
 
 def parse():
@@ -51,6 +51,7 @@ def parse():
                     help="threads of the parallel oracle sample (0: host cores, at most 16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
+    ap.add_argument("--no-mla", action="store_true", help="skip the head_dim 512 latent decode")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain fp32 elementwise kernel over 2 x 512 MiB "
                          "(reference for the HBM byte counters)")
@@ -306,6 +307,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # ---------------- latent-width decode (head_dim 512, MFMA-bound)
+    mla = None
+    if not args.no_mla:
+        mla = bench_latent(kvq, syn, dev, stream, max(args.steps // 2, 20), R)
+
     # ---------------- CPU oracle baseline on a bounded sample
     cpu = None
     if not args.no_cpu_baseline:
@@ -344,9 +350,71 @@ def main():
         },
         "fp8_comparator": fp8,
         "append_bulk": append_bulk,
+        "latent_512": mla,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+# dense MFMA peaks of MI355X (TFLOP/s)
+PEAK_FP4_FP6 = 10100.0
+PEAK_BF16 = 2500.0
+
+
+def bench_latent(kvq, syn, dev, stream, steps, R, name="mla_b16_l128k"):
+    """Decode over the latent cache (batch 16, one K = V head of width 512,
+    64 absorbed query heads, context 131072, page 64): mean HIP-event time
+    of one decode call over cache replicas, against the MFMA time the
+    kernel's instructions need at the dense peaks (QK^T: four FP4 x FP6
+    terms; PV: bf16 hi + lo)."""
+    import numpy as np
+    import torch
+    wl = syn.WORKLOADS[name]
+    plan = syn.page_plan(wl)
+    c, _ = build_cache(kvq, syn, wl, plan, kvq.FMT_FP4_E2M1, dev)
+    cs = replicate(kvq, c, R)
+    q = syn.queries(wl, dev)
+    bt = torch_from(plan.block_tables, dev)
+    cl = torch_from(plan.context_lens, dev)
+    maxL = int(plan.context_lens.max())
+    B, HQ, NQ, D = wl.batch, wl.num_q_heads, wl.n_q, wl.head_dim
+    out = torch.empty((B, NQ, HQ, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(kvq.decode_workspace_bytes(c, B, HQ, NQ, maxL), dtype=torch.uint8, device=dev)
+    for i in range(10):
+        kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (a, b) in enumerate(es):
+        a.record(stream)
+        kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = statistics.fmean([a.elapsed_time(b) for a, b in es])
+    tokens = int(plan.context_lens.astype(np.int64).sum()) * wl.num_kv_heads
+    rows = wl.group * NQ
+    alg_flops = 4.0 * D * rows * tokens                 # QK^T + PV, single term
+    qk_flops = 2.0 * D * rows * tokens * 4              # four FP6 query terms
+    pv_flops = 2.0 * D * rows * tokens * 2              # P hi + lo
+    t_peak = qk_flops / (PEAK_FP4_FP6 * 1e12) + pv_flops / (PEAK_BF16 * 1e12)
+    issued = qk_flops + pv_flops
+    kv_bytes = tokens * (D // 2 + D // 32)
+    del cs, c
+    return {
+        "workload": "%s: %s" % (wl.name, wl.description),
+        "decode_ms_events_mean": round(t, 4),
+        "kv_gbs": round(kv_bytes / (t * 1e-3) / 1e9, 1),
+        "hbm_frac": round(kv_bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "algorithmic_tflops": round(alg_flops / (t * 1e-3) / 1e12, 1),
+        "roofline": {
+            "bound": "mfma", "unit": "TFLOP/s",
+            "achieved": round(issued / (t * 1e-3) / 1e12, 1),
+            "peak": round(issued / t_peak / 1e12, 1),
+            "frac": round(t_peak / (t * 1e-3), 4),
+            "traffic": None,
+            "note": "issued MFMA flops (QK^T 4 FP4xFP6 terms at 10.1 PF/s, PV bf16 hi+lo at 2.5 PF/s); "
+                    "peak = their time-weighted dense peak",
+        },
+    }
 
 
 def cpu_baseline(wl, plan, target_s, threads):

@@ -33,43 +33,45 @@ constexpr int kM5 = kT5 / 2;         // scaled MFMAs per 128-channel block (two 
 constexpr int kW5 = 8;               // waves per block
 constexpr int kVRow5 = 2 * kD5 + 32;  // LDS bytes per bf16 token row (padded)
 constexpr int kMaxRG5 = 4;           // 16-row groups (64 rows)
+// tile pairs in flight per wave (one chunk each): three, fewer where the
+// accumulators of 64 rows (and a separate V chunk) leave no room
+template <int RG, bool SHARED>
+struct Ring5 {
+  static constexpr int kN = RG >= 4 ? (SHARED ? 2 : 1) : (SHARED || RG <= 2 ? 3 : 2);
+};
 
-// Raw codes of one 16-token tile as this wave needs them: all four K chunks
-// (chunk c = channel groups 4c .. 4c + 3; lane l holds token l%16, group
-// 4c + l/16) and, for a separate V cache, the one V chunk it converts.
-struct Tile5 {
-  uint32_t k[4][4];
-  uint32_t ksc[4];
+// Raw codes of the one (tile, 128-channel chunk) of a tile pair this wave
+// stages: lane l holds token l%16, channel group 4 chunk + l/16 (16 code
+// bytes) and that group's scale byte; V likewise for a separate V cache.
+struct Chunk5 {
+  uint32_t k[4];
+  uint32_t ksc;
   uint32_t v[4];
   uint32_t vsc;
 };
 
 template <bool SHARED>
-__device__ __forceinline__ void load_tile5(const DecodeParams& p, const int32_t* bt_row, int kvh,
-                                           int tile, int lane, int vchunk, Tile5& t) {
+__device__ __forceinline__ void load_chunk5(const DecodeParams& p, const int32_t* bt_row, int kvh,
+                                            int tile, int chunk, int lane, Chunk5& t) {
   const int tok = tile * 16;
   const int page = __builtin_amdgcn_readfirstlane(bt_row[tok >> p.p_shift]);
   const int in_page = tok & (p.P - 1);
   const int64_t cb = (int64_t)page * p.c_page + (int64_t)kvh * p.c_head;
   const int64_t sb = (int64_t)page * p.s_page + (int64_t)kvh * p.s_head;
+  const int idx = (4 * chunk + (lane >> 4)) * p.P + (lane & 15);
+  const int coff = in_page * 16;
   const __amdgpu_buffer_rsrc_t rk = block_rsrc(p.kc, cb, p.c_head);
   const __amdgpu_buffer_rsrc_t rks = block_rsrc(p.ks, sb, p.s_head);
-  const int coff = in_page * 16;
+  const u32x4_t a = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, idx * 16, coff, 2));
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int idx = (4 * c + (lane >> 4)) * p.P + (lane & 15);
-    const u32x4_t a = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, idx * 16, coff, 2));
-#pragma unroll
-    for (int w = 0; w < 4; ++w) t.k[c][w] = a[w];
-    t.ksc[c] = __builtin_amdgcn_raw_buffer_load_b8(rks, idx, in_page, 0);
-  }
+  for (int w = 0; w < 4; ++w) t.k[w] = a[w];
+  t.ksc = __builtin_amdgcn_raw_buffer_load_b8(rks, idx, in_page, 0);
   if constexpr (!SHARED) {
     const __amdgpu_buffer_rsrc_t rv = block_rsrc(p.vc, cb, p.c_head);
     const __amdgpu_buffer_rsrc_t rvs = block_rsrc(p.vs, sb, p.s_head);
-    const int idx = (4 * vchunk + (lane >> 4)) * p.P + (lane & 15);
-    const u32x4_t a = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, idx * 16, coff, 2));
+    const u32x4_t c = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, idx * 16, coff, 2));
 #pragma unroll
-    for (int w = 0; w < 4; ++w) t.v[w] = a[w];
+    for (int w = 0; w < 4; ++w) t.v[w] = c[w];
     t.vsc = __builtin_amdgcn_raw_buffer_load_b8(rvs, idx, in_page, 0);
   }
 }
@@ -156,17 +158,37 @@ __global__ __launch_bounds__(256) void qprep512_kernel(const DecodeParams p) {
   }
 }
 
+// Score contribution of one 128-channel chunk: K codes (FP4) and scale
+// byte as the A operand, the two FP6 query-term MFMAs of that chunk as B;
+// the query scale byte sits in byte 2 (C & 1) + m of register C / 2.
+template <int C>
+__device__ __forceinline__ f32x4_t qk_chunk5(f32x4_t acc, const u32x4_t kc, int ksc,
+                                             const i32x8_t (&qb)[4][kM5], const int (&qs)[2]) {
+  const i32x8_t A = {(int)kc[0], (int)kc[1], (int)kc[2], (int)kc[3], 0, 0, 0, 0};
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, qb[C][0], acc, 4, 2, 0, ksc, 2 * (C & 1), qs[C >> 1]);
+  acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, qb[C][1], acc, 4, 2, 0, ksc, 2 * (C & 1) + 1,
+                                                         qs[C >> 1]);
+  return acc;
+}
+
 template <int RG, bool SHARED>
 __global__ __launch_bounds__(512) void decode512_kernel(const DecodeParams p) {
   constexpr int ROWS = 16 * RG;
   constexpr int NO = 2 * RG;
-  __shared__ __attribute__((aligned(16))) uint8_t s_v[2][2][16][kVRow5];
+  // staged K codes / scales for the scores (by pair parity), bf16 V rows
+  // (three buffers: a pair is staged while the previous one is still read),
+  // P as PV A operands and the rescale factors (by pair parity)
+  __shared__ __attribute__((aligned(16))) u32x4_t s_k[2][2][4][64];
+  __shared__ uint32_t s_ks[2][2][4][64];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[3][2][16][kVRow5];
   __shared__ __attribute__((aligned(16))) u32x4_t s_p[2][RG][2][64];
   __shared__ float s_alpha[2][ROWS];
   __shared__ int s_flag[2][NO];
 
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  // wave index as a scalar: everything derived from it (staged tile and
+  // chunk, buffer offsets) stays in SGPRs, with no per-lane loops
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int split = blockIdx.x;
   const int kvh = blockIdx.y;
   const int b = blockIdx.z;
@@ -180,19 +202,45 @@ __global__ __launch_bounds__(512) void decode512_kernel(const DecodeParams p) {
   const int quad = lane >> 4;
   const int32_t* bt_row = p.block_tables + (size_t)b * p.max_pages;
   const int n_pairs = (t_end > t_begin) ? ((t_end - t_begin + 1) >> 1) : 0;
-  const bool owner = w < NO;
-  const int vtile = w & 1;   // tile of each pair this wave converts
-  const int vchunk = w >> 1;  // ... and its 128-channel quarter
+  constexpr int kRing5 = Ring5<RG, SHARED>::kN;
+  const int n_iter = (n_pairs + kRing5 - 1) / kRing5;  // pairs padded to a multiple of kRing5
+  const bool owner = (NO == kW5) || w < NO;  // every wave owns rows at 64 rows
+  const int mtile = w & 1;   // tile of each pair this wave stages
+  const int mchunk = w >> 1;  // ... and its 128-channel chunk
+  const int interior_limit = min(tok_limit, L - p.n_q + 1);
 
-  Tile5 cur[2];
+  // stage pair pi (codes in `c`): K codes and scales for the scores, V as
+  // bf16 rows (zero past the context; branch-free)
+  auto stage = [&](int pi, const Chunk5& c) {
+    const int tile = t_begin + 2 * pi + mtile;
+    s_k[pi & 1][mtile][mchunk][lane] = u32x4_t{c.k[0], c.k[1], c.k[2], c.k[3]};
+    s_ks[pi & 1][mtile][mchunk][lane] = c.ksc;
+    const bool dead = tile * 16 + col >= tok_limit;
+    uint32_t vw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vw[i] = dead ? 0u : (SHARED ? c.k[i] : c.v[i]);
+    const uint32_t vsc = dead ? 0u : (SHARED ? c.ksc : c.vsc);
+    uint32_t vb[16];
+    dequant_group<KVQ_FMT_FP4_E2M1>(vw, scale_operand(vsc), vb);
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(&s_v[pi % 3][mtile][col][2 * (128 * mchunk + 32 * quad)]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = u32x4_t{vb[4 * i], vb[4 * i + 1], vb[4 * i + 2], vb[4 * i + 3]};
+  };
+  // refill a ring slot with pair pi (clamped to the split's last tile)
+  auto fetch = [&](int pi, Chunk5& c) {
+    load_chunk5<SHARED>(p, bt_row, kvh, min(t_begin + 2 * pi + mtile, t_end - 1), mchunk, lane, c);
+  };
+
+  Chunk5 ring[kRing5];
   if (n_pairs > 0) {
-    load_tile5<SHARED>(p, bt_row, kvh, t_begin, lane, vchunk, cur[0]);
-    load_tile5<SHARED>(p, bt_row, kvh, min(t_begin + 1, t_end - 1), lane, vchunk, cur[1]);
+#pragma unroll
+    for (int u = 0; u < kRing5; ++u) fetch(u, ring[u]);
   }
 
-  // score owner: query operands of rows 8w .. 8w + 7
+  // score owner: query operands of rows 8w .. 8w + 7; their eight scale
+  // bytes packed four to a register (the MFMA's scale op_sel picks the byte)
   i32x8_t qb[4][kM5];
-  int qs[4][kM5];
+  int qs[2] = {0, 0};
   if (owner) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -202,15 +250,70 @@ __global__ __launch_bounds__(512) void decode512_kernel(const DecodeParams p) {
         const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(src);
         const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(src + 4);
         qb[c][m] = i32x8_t{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], 0, 0};
-        qs[c][m] = (int)a1[2];
+        qs[c >> 1] |= (int)((a1[2] & 0xFFu) << (8 * (2 * (c & 1) + m)));
       }
     }
   }
   const int row = 8 * w + (col & 7);  // owner's row in this lane
-  const int row_last = (owner && row < p.rows) ? (L - p.n_q + row / p.group) : -1;
-  const int interior_limit = min(tok_limit, L - p.n_q + 1);
+  // last token this lane's row may see (context end, MTP causal rule)
+  const int row_lim = (owner && row < p.rows) ? min(tok_limit - 1, L - p.n_q + row / p.group) : -1;
   const bool hi_col = col < 8;
   float m_run = -INFINITY, l_run = 0.0f;
+
+  // owner: scores of pair pi, online softmax, P hi / lo as PV A operands,
+  // rescale factors (branch-free: one basic block with the PV product)
+  auto scores = [&](int pi) {
+    const int par = pi & 1;
+    const int tile = t_begin + 2 * pi;
+    f32x4_t S[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+      acc = qk_chunk5<0>(acc, s_k[par][s][0][lane], (int)s_ks[par][s][0][lane], qb, qs);
+      acc = qk_chunk5<1>(acc, s_k[par][s][1][lane], (int)s_ks[par][s][1][lane], qb, qs);
+      acc = qk_chunk5<2>(acc, s_k[par][s][2][lane], (int)s_ks[par][s][2][lane], qb, qs);
+      acc = qk_chunk5<3>(acc, s_k[par][s][3][lane], (int)s_ks[par][s][3][lane], qb, qs);
+      S[s] = acc;
+    }
+    float sc[8];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x = S[s][i];
+        const int tok = (tile + s) * 16 + 4 * quad + i;
+        sc[4 * s + i] = (tok <= row_lim) ? x + dpp_ror8(x) : -INFINITY;
+      }
+    }
+    float mloc = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                       fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+    mloc = quad_max(mloc);
+    const float m_old = m_run;
+    const float m_new = fmaxf(m_old, mloc);
+    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+    m_run = m_new;
+    float psum = 0.0f;
+    uint32_t pw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float p0 = __builtin_amdgcn_exp2f(sc[2 * e] - m_use);
+      const float p1 = __builtin_amdgcn_exp2f(sc[2 * e + 1] - m_use);
+      psum += p0 + p1;
+      const uint32_t u0 = as_u32(p0), u1 = as_u32(p1);
+      const uint32_t h = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+      const uint32_t l = pack_bf16x2(p0 - as_f32(u0 & 0xFFFF0000u), p1 - as_f32(u1 & 0xFFFF0000u));
+      pw[e] = hi_col ? h : l;
+    }
+    // A operand slot: MFMA quad / 2 (token quads {0,1} or {2,3}); lane
+    // k-group (quad & 1) + 2 * lo, row 8 (w & 1) + (col & 7)
+    const int kg = (quad & 1) + (hi_col ? 0 : 2);
+    s_p[par][w >> 1][quad >> 1][16 * kg + 8 * (w & 1) + (col & 7)] = u32x4_t{pw[0], pw[1], pw[2], pw[3]};
+    const float alpha = __builtin_amdgcn_exp2f(m_old - m_use);
+    l_run = l_run * alpha + psum;
+    if (lane < 8) s_alpha[par][8 * w + lane] = alpha;
+    const bool moved = __builtin_amdgcn_ballot_w64(m_new != m_old) != 0;
+    if (lane == 0) s_flag[par][w] = moved ? 1 : 0;
+  };
 
   f32x4_t O[RG][4];
 #pragma unroll
@@ -218,174 +321,78 @@ __global__ __launch_bounds__(512) void decode512_kernel(const DecodeParams p) {
 #pragma unroll
     for (int n = 0; n < 4; ++n) O[g][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // ---- prologue: stage pairs 0 and 1, scores of pair 0
+  if (n_pairs > 0) {
+    stage(0, ring[0]);
+    fetch(kRing5, ring[0]);
+  }
+  __syncthreads();
+  if (n_pairs > 0) {
+    stage(1, ring[1 % kRing5]);
+    fetch(1 + kRing5, ring[1 % kRing5]);
+    if (owner) scores(0);
+  }
+  __syncthreads();
+
+  // ---- segment pi: PV of pair pi, scores of pair pi + 1, staging of pair
+  // pi + 2; one barrier per segment
 #pragma unroll 1
-  for (int pi = 0; pi < n_pairs; ++pi) {
-    const int par = pi & 1;
-    const int tile = t_begin + 2 * pi;
-    const bool boundary = tile * 16 + 32 > interior_limit;
-
-    // ---- V quarter of one tile -> bf16 LDS rows (zero past the context)
-    {
-      // (wave-uniform selects: no dynamic register indexing)
-      uint32_t vw[4];
-      uint32_t vsc;
-      if constexpr (SHARED) {
-        // mask-and-or selects over all eight candidates (a conditional
-        // expression over array elements can turn into a scratch access)
-        const uint32_t mt[2] = {vtile ? 0u : ~0u, vtile ? ~0u : 0u};
-        const uint32_t mc[4] = {vchunk == 0 ? ~0u : 0u, vchunk == 1 ? ~0u : 0u, vchunk == 2 ? ~0u : 0u,
-                                vchunk == 3 ? ~0u : 0u};
+  for (int it = 0; it < n_iter; ++it) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          uint32_t acc = 0u;
-#pragma unroll
-          for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc |= cur[s].k[c][i] & mt[s] & mc[c];
-          vw[i] = acc;
-        }
-        uint32_t acc = 0u;
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) acc |= cur[s].ksc[c] & mt[s] & mc[c];
-        vsc = acc;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vw[i] = vtile ? cur[1].v[i] : cur[0].v[i];
-        vsc = vtile ? cur[1].vsc : cur[0].vsc;
-      }
-      if (boundary) {
-        const bool dead = (tile + vtile) * 16 + col >= tok_limit;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) vw[i] = dead ? 0u : vw[i];
-        vsc = dead ? 0u : vsc;
-      }
-      uint32_t vb[16];
-      dequant_group<KVQ_FMT_FP4_E2M1>(vw, scale_operand(vsc), vb);
-      u32x4_t* dst = reinterpret_cast<u32x4_t*>(&s_v[par][vtile][col][2 * (128 * vchunk + 32 * quad)]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = u32x4_t{vb[4 * i], vb[4 * i + 1], vb[4 * i + 2], vb[4 * i + 3]};
-    }
-
-    // ---- scores S^T (tokens x (8 rows x 2 terms)) for the owner's rows
-    f32x4_t S[2];
-    if (owner) {
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const i32x8_t A = {(int)cur[s].k[c][0], (int)cur[s].k[c][1], (int)cur[s].k[c][2], (int)cur[s].k[c][3], 0, 0, 0, 0};
-#pragma unroll
-          for (int m = 0; m < kM5; ++m)
-            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, qb[c][m], acc, 4, 2, 0, (int)cur[s].ksc[c], 0,
-                                                                   qs[c][m]);
-        }
-        S[s] = acc;
-      }
-    }
-
-    // ---- the codes are consumed: fetch the next pair
-    if (pi + 1 < n_pairs) {
-      load_tile5<SHARED>(p, bt_row, kvh, tile + 2, lane, vchunk, cur[0]);
-      load_tile5<SHARED>(p, bt_row, kvh, min(tile + 3, t_end - 1), lane, vchunk, cur[1]);
-    }
-
-    // ---- owner: online softmax, P hi / lo as PV A operands
-    if (owner) {
-      float sc[8];
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x = S[s][i];
-          sc[4 * s + i] = x + dpp_ror8(x);
-        }
-      }
-      if (boundary) {
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int tok = (tile + s) * 16 + 4 * quad + i;
-            const bool ok = (tok < tok_limit) && (tok <= row_last);
-            sc[4 * s + i] = ok ? sc[4 * s + i] : -INFINITY;
-          }
-        }
-      }
-      float mloc = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                         fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-      mloc = quad_max(mloc);
-      const float m_old = m_run;
-      const float m_new = fmaxf(m_old, mloc);
-      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      m_run = m_new;
-      float psum = 0.0f;
-      uint32_t pw[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = __builtin_amdgcn_exp2f(sc[2 * e] - m_use);
-        const float p1 = __builtin_amdgcn_exp2f(sc[2 * e + 1] - m_use);
-        psum += p0 + p1;
-        const uint32_t u0 = as_u32(p0), u1 = as_u32(p1);
-        const uint32_t h = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
-        const uint32_t l = pack_bf16x2(p0 - as_f32(u0 & 0xFFFF0000u), p1 - as_f32(u1 & 0xFFFF0000u));
-        pw[e] = hi_col ? h : l;
-      }
-      // A operand slot: MFMA quad / 2 (token quads {0,1} or {2,3}); lanes
-      // k-group (quad & 1) + 2 * lo, row 8 (w & 1) + (col & 7)
-      const int kg = (quad & 1) + (hi_col ? 0 : 2);
-      s_p[par][w >> 1][quad >> 1][16 * kg + 8 * (w & 1) + (col & 7)] = u32x4_t{pw[0], pw[1], pw[2], pw[3]};
-      const bool moved = __builtin_amdgcn_ballot_w64(m_new != m_old) != 0;
-      if (moved) {
-        const float alpha = __builtin_amdgcn_exp2f(m_old - m_use);
-        l_run *= alpha;
-        if (lane < 8) s_alpha[par][8 * w + lane] = alpha;
-      }
-      if (lane == 0) s_flag[par][w] = moved ? 1 : 0;
-      l_run += psum;
-    }
-    __syncthreads();
-
-    // ---- PV over channels 64w .. 64w + 63 for every row group
-    const int rr = col >> 2;
-    const int c4 = (col & 3) * 4;
-    typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
-    auto read_b = [&](int Q, int n) {
-      const int cb = 2 * (64 * w + 16 * n + c4);
-      lds_bf16x4* a0 = (lds_bf16x4*)((__attribute__((address_space(3))) uint8_t*)&s_v[par][0][4 * Q + rr][cb]);
-      lds_bf16x4* a1 = (lds_bf16x4*)((__attribute__((address_space(3))) uint8_t*)&s_v[par][1][4 * Q + rr][cb]);
-      const u32x2_t w0 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(a0));
-      const u32x2_t w1 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(a1));
-      return __builtin_bit_cast(bf16x8_t, u32x4_t{w0[0], w0[1], w1[0], w1[1]});
-    };
-    bf16x8_t A[RG][2];
-#pragma unroll
-    for (int g = 0; g < RG; ++g) {
-      A[g][0] = __builtin_bit_cast(bf16x8_t, s_p[par][g][0][lane]);
-      A[g][1] = __builtin_bit_cast(bf16x8_t, s_p[par][g][1][lane]);
-      // rows 16g + 4 quad + i belong to owner 2g + (quad >> 1)
-      if (s_flag[par][2 * g] | s_flag[par][2 * g + 1]) {
-        const bool mine = s_flag[par][2 * g + (quad >> 1)] != 0;
-        float ar[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ar[i] = mine ? s_alpha[par][16 * g + 4 * quad + i] : 1.0f;
-#pragma unroll
-        for (int n = 0; n < 4; ++n)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) O[g][n][i] *= ar[i];
-      }
-    }
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      const bf16x8_t B0 = read_b(quad & 1, n);
-      const bf16x8_t B1 = read_b(2 + (quad & 1), n);
+    for (int u = 0; u < kRing5; ++u) {
+      const int pi = it * kRing5 + u;
+      const int par = pi & 1;
+      // rescale O by the factors of pair pi (rows 16g + 4 quad + i belong to
+      // owner 2g + (quad >> 1)), then load its P operands
+      bf16x8_t A[RG][2];
 #pragma unroll
       for (int g = 0; g < RG; ++g) {
-        O[g][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][0], B0, O[g][n], 0, 0, 0);
-        O[g][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][1], B1, O[g][n], 0, 0, 0);
+        if (s_flag[par][2 * g] | s_flag[par][2 * g + 1]) {
+          float ar[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ar[i] = s_alpha[par][16 * g + 4 * quad + i];
+#pragma unroll
+          for (int n = 0; n < 4; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) O[g][n][i] *= ar[i];
+        }
+        A[g][0] = __builtin_bit_cast(bf16x8_t, s_p[par][g][0][lane]);
+        A[g][1] = __builtin_bit_cast(bf16x8_t, s_p[par][g][1][lane]);
       }
+      // scores of the next pair (its codes were staged a segment ago); past
+      // the last pair the staged tiles lie beyond the context and every
+      // score is masked, so the call leaves the softmax state unchanged
+      if (owner) scores(pi + 1);
+      // PV over channels 64w .. 64w + 63 for every row group
+      const int vb = pi % 3;
+      const int rr = col >> 2;
+      const int c4 = (col & 3) * 4;
+      typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+      auto read_b = [&](int Q, int n) {
+        const int cb = 2 * (64 * w + 16 * n + c4);
+        lds_bf16x4* a0 = (lds_bf16x4*)((__attribute__((address_space(3))) uint8_t*)&s_v[vb][0][4 * Q + rr][cb]);
+        lds_bf16x4* a1 = (lds_bf16x4*)((__attribute__((address_space(3))) uint8_t*)&s_v[vb][1][4 * Q + rr][cb]);
+        const u32x2_t w0 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(a0));
+        const u32x2_t w1 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(a1));
+        return __builtin_bit_cast(bf16x8_t, u32x4_t{w0[0], w0[1], w1[0], w1[1]});
+      };
+#pragma unroll
+      for (int n = 0; n < 4; ++n) {
+        const bf16x8_t B0 = read_b(quad & 1, n);
+        const bf16x8_t B1 = read_b(2 + (quad & 1), n);
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+          O[g][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][0], B0, O[g][n], 0, 0, 0);
+          O[g][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][1], B1, O[g][n], 0, 0, 0);
+        }
+      }
+      // stage pair pi + 2 from the ring, refill the slot
+      {
+        const int su = (u + 2) % kRing5;
+        stage(pi + 2, ring[su]);
+        fetch(pi + 2 + kRing5, ring[su]);
+      }
+      __syncthreads();
     }
   }
 

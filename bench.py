@@ -52,6 +52,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-mla", action="store_true", help="skip the head_dim 512 latent decode")
+    ap.add_argument("--no-mix", action="store_true", help="skip the shared-prefix MTP mix")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain fp32 elementwise kernel over 2 x 512 MiB "
                          "(reference for the HBM byte counters)")
@@ -307,6 +308,11 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # ---------------- agentic mix: shared prefixes, MTP verify positions
+    mix = None
+    if not args.no_mix:
+        mix = bench_mix(kvq, syn, dev, stream, max(args.steps // 2, 20), R)
+
     # ---------------- latent-width decode (head_dim 512, MFMA-bound)
     mla = None
     if not args.no_mla:
@@ -350,6 +356,7 @@ def main():
         },
         "fp8_comparator": fp8,
         "append_bulk": append_bulk,
+        "agentic_mix": mix,
         "latent_512": mla,
         "cpu_baseline": cpu,
     }
@@ -359,6 +366,54 @@ def main():
 # dense MFMA peaks of MI355X (TFLOP/s)
 PEAK_FP4_FP6 = 10100.0
 PEAK_BF16 = 2500.0
+
+
+def bench_mix(kvq, syn, dev, stream, steps, R, name="mtp_mixed_b32"):
+    """Decode over the agentic mix (batch 32, contexts 4K-128K, 92% of each
+    sequence's pages shared from 4 prefixes, 3 MTP verify positions):
+    mean HIP-event time of one FP4 decode call over cache replicas.
+    Reports logical KV bytes (every sequence's pages, shared ones counted
+    per sequence) and unique bytes (each physical page once)."""
+    import numpy as np
+    import torch
+    wl = syn.WORKLOADS[name]
+    plan = syn.page_plan(wl)
+    c, _ = build_cache(kvq, syn, wl, plan, kvq.FMT_FP4_E2M1, dev)
+    cs = replicate(kvq, c, R)
+    q = syn.queries(wl, dev)
+    bt = torch_from(plan.block_tables, dev)
+    cl = torch_from(plan.context_lens, dev)
+    maxL = int(plan.context_lens.max())
+    B, HQ, NQ, D = wl.batch, wl.num_q_heads, wl.n_q, wl.head_dim
+    out = torch.empty((B, NQ, HQ, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(kvq.decode_workspace_bytes(c, B, HQ, NQ, maxL), dtype=torch.uint8, device=dev)
+    for i in range(5):
+        kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (a, b) in enumerate(es):
+        a.record(stream)
+        kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = statistics.fmean([a.elapsed_time(b) for a, b in es])
+    per_tok = (D // 2 + D // 32) * 2 * wl.num_kv_heads
+    logical = int(plan.context_lens.astype(np.int64).sum()) * per_tok
+    P = wl.page_size
+    used = set()
+    for b in range(B):
+        n = (int(plan.context_lens[b]) + P - 1) // P
+        used.update(int(x) for x in plan.block_tables[b][:n])
+    unique = len(used) * P * per_tok
+    del cs, c
+    return {
+        "workload": "%s: %s" % (wl.name, wl.description),
+        "decode_ms_events_mean": round(t, 4),
+        "logical_kv_bytes": logical,
+        "unique_kv_bytes": unique,
+        "logical_gbs": round(logical / (t * 1e-3) / 1e9, 1),
+        "unique_gbs": round(unique / (t * 1e-3) / 1e9, 1),
+    }
 
 
 def bench_latent(kvq, syn, dev, stream, steps, R, name="mla_b16_l128k"):

@@ -404,9 +404,15 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t s_v[2][16][kVRow];
 
   const int lane = threadIdx.x;
-  const int split = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int b = blockIdx.z;
+  // 1-D grid, the splits of one (sequence, KV head) unit consecutive, the
+  // split index rotated by the sequence: blocks go to the XCDs round-robin,
+  // and with ragged contexts only the low splits of short sequences have
+  // work, so without the rotation a split count divisible by 8 would pile
+  // that work onto a few XCDs
+  const int u = blockIdx.x / p.splits;
+  const int kvh = u % p.hkv;
+  const int b = u / p.hkv;
+  const int split = (blockIdx.x - u * p.splits + b) % p.splits;
   const int L = p.context_lens[b];
   const int n_tiles = (L + 15) >> 4;
   const int t_begin = split * p.tiles_per_split;
@@ -545,6 +551,7 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
 }
 
 constexpr int kMinTilesPerSplit = 8;     // 128 tokens
+constexpr int kMaxTilesPerSplit = 256;   // 4096 tokens
 constexpr int kDefaultWaveSlots = 2048;  // MI355X: 256 CUs x 8 resident waves
 constexpr int kMaxDevices = 64;
 
@@ -555,7 +562,7 @@ hipError_t launch_nt(const DecodeParams& p, int batch, hipStream_t stream) {
   hipLaunchKernelGGL((qprep_kernel<FMT, NT>), dim3(qblocks), dim3(256), 0, stream, p);
   hipError_t e0 = hipGetLastError();
   if (e0 != hipSuccess) return e0;
-  dim3 grid((unsigned)p.splits, (unsigned)p.hkv, (unsigned)batch);
+  const dim3 grid((unsigned)((size_t)p.splits * p.hkv * batch));
   hipLaunchKernelGGL((decode_kernel<FMT, NT>), grid, dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1) return e;
@@ -624,16 +631,20 @@ int plan_decode(const CacheGeom& c, int batch, int hq, int n_q, int max_context_
   if (splits <= 0) {
     // One round of waves: as many splits as fill the device's resident wave
     // slots once (a second, partial round costs more than the larger
-    // partials save), but at least kMinTilesPerSplit tiles per split.
+    // partials save), but at least kMinTilesPerSplit tiles per split and at
+    // most kMaxTilesPerSplit: with ragged context lengths only the maximum
+    // is known here, and long splits of the longest sequences would then
+    // set the time of the whole call.
     int slots = resident_waves(c.fmt, row_tiles);
     if (slots <= 0) slots = kDefaultWaveSlots;
     const long long units = (long long)batch * c.hkv;
     long long want = units >= slots ? 1 : slots / units;
     const long long by_len = n_tiles / kMinTilesPerSplit;
     if (want > by_len) want = by_len;
+    const long long by_cap = (n_tiles + kMaxTilesPerSplit - 1) / kMaxTilesPerSplit;
+    if (want < by_cap) want = by_cap;
     splits = (int)(want < 1 ? 1 : want);
   }
-  if (splits < 1) splits = 1;
   if (splits > kMaxSplits) splits = kMaxSplits;
   int per = (n_tiles + splits - 1) / splits;
   per = (per + 1) & ~1;  // tiles are processed in pairs

@@ -16,7 +16,7 @@
 //    lane's score operands in the workspace.  FP4 cache: the query is split
 //    into kQTerms FP6 (E2M3) terms with their own per-32 UE8M0 scales, each
 //    term carrying the previous residual; FP4 x FP6 products are exact in
-//    the scaled MFMA, and six terms leave a residual near 2^-25 of the
+//    the scaled MFMA, and four terms leave a residual of about 2^-16 of the
 //    block maximum.  FP8 cache: bf16 hi + lo parts.
 //  * decode_kernel, one wave per (sequence, KV head, context split): the
 //    page scan streams 16-token tiles.  Lane l loads the code bytes of token
@@ -49,10 +49,16 @@ namespace kvq {
 namespace {
 
 constexpr int kD = 128;              // head_dim handled by this kernel
-constexpr int kQTerms = 6;           // FP6 (E2M3) terms of the pre-scaled query (FP4 cache)
+constexpr int kQTerms = 4;           // FP6 (E2M3) terms of the pre-scaled query (FP4 cache)
 constexpr int kQMfma = kQTerms / 2;  // scaled MFMAs per tile and row tile
 constexpr int kVRow = 2 * kD + 32;   // LDS bytes per token row of V (bf16, padded)
-constexpr int kRing = 2;             // tile pairs held in registers per wave
+// tile pairs held in registers per wave: two, except one at 16 rows, where
+// that keeps two waves per SIMD (at 24 rows one wave fits either way, and the
+// deeper ring wins)
+template <int NT>
+struct Ring {
+  static constexpr int kN = NT == 2 ? 1 : 2;
+};
 
 // Query operands of the score product.
 //  FP4 cache: kQTerms FP6 terms for the scaled MFMA (6 packed dwords + scale).
@@ -159,39 +165,37 @@ __device__ __forceinline__ void compute_pair(const DecodeParams& p, const int32_
   const int quad = lane >> 4;
   const bool hi_col = col < 8;
 
-  // ---- scores S^T = K q^T
-  f32x4_t S[2][NT];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
+  // ---- scores S^T = K q^T for row tile t.  With 8 rows they are all
+  // computed up front; with 16 or 24 rows one row tile at a time, inside the
+  // softmax loop, to keep register pressure down.
+  constexpr bool kLate = NT >= 2;
+  auto scores_t = [&](int s, int t) -> f32x4_t {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     if constexpr (Fmt<FMT>::kFP4) {
       // FP4 codes and UE8M0 scales straight into the scaled MFMA (A operand)
       const i32x8_t A = {(int)r[s].k[0], (int)r[s].k[1], (int)r[s].k[2], (int)r[s].k[3], 0, 0, 0, 0};
-      const int ksc = (int)r[s].ksc;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int m = 0; m < kQMfma; ++m)
-          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, q.b[t][m], acc, 4, 2, 0, ksc, 0,
-                                                                 q.sc[t][m]);
-        S[s][t] = acc;
-      }
+      for (int m = 0; m < kQMfma; ++m)
+        acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, q.b[t][m], acc, 4, 2, 0, (int)r[s].ksc, 0,
+                                                               q.sc[t][m]);
     } else {
       // E4M3 codes dequantised to bf16 (exact) as the A operand of bf16 MFMAs
       uint32_t kb[16];
       dequant_group<FMT>(r[s].k, scale_operand(r[s].ksc), kb);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const u32x4_t a = {kb[4 * ks], kb[4 * ks + 1], kb[4 * ks + 2], kb[4 * ks + 3]};
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), q.b[t][ks], acc,
-                                                        0, 0, 0);
-        }
-        S[s][t] = acc;
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4_t a = {kb[4 * ks], kb[4 * ks + 1], kb[4 * ks + 2], kb[4 * ks + 3]};
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), q.b[t][ks], acc, 0, 0, 0);
       }
     }
+    return acc;
+  };
+  f32x4_t S[2][kLate ? 1 : NT];
+  if constexpr (!kLate) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) S[s][t] = scores_t(s, t);
   }
 
   // ---- V tiles -> LDS as bf16 token rows.  Past the end of the context the
@@ -217,18 +221,22 @@ __device__ __forceinline__ void compute_pair(const DecodeParams& p, const int32_
   }
 
   // the raw codes are consumed: start the next loads into the same registers
-  issue_pair<FMT>(p, bt_row, kvh, refill, t_end, lo, r);
+  if constexpr (!kLate) issue_pair<FMT>(p, bt_row, kvh, refill, t_end, lo, r);
 
   // ---- softmax update and P (bf16 hi/lo) per row tile
   bf16x8_t A[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
+    f32x4_t St[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) St[s] = kLate ? scores_t(s, t) : S[s][kLate ? 0 : t];
+    if (kLate && t == NT - 1) issue_pair<FMT>(p, bt_row, kvh, refill, t_end, lo, r);
     float sc[8];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float x = S[s][t][i];
+        const float x = St[s][i];
         sc[4 * s + i] = x + dpp_ror8(x);
       }
     }
@@ -423,6 +431,7 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
   const int32_t* bt_row = p.block_tables + (size_t)b * p.max_pages;
   const bool has_work = t_end > t_begin;
   const int n_pairs = has_work ? ((t_end - t_begin + 1) >> 1) : 0;
+  constexpr int kRing = Ring<NT>::kN;
   const int n_iter = (n_pairs + kRing - 1) / kRing;
 
   // ---- start streaming the first tile pairs

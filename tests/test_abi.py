@@ -133,10 +133,10 @@ def test_decode_workspace_checks():
     assert _decode(B=32, hq=64, maxp=2048, maxl=32768, ws=None, wsb=0) == -5
     assert _decode(B=32, hq=64, maxp=2048, maxl=32768, ws=0x50, wsb=need - 1) == -5
     assert _decode(B=32, hq=64, maxp=2048, maxl=32768, ws=0x58, wsb=need) == -5  # not 16-byte aligned
-    # one forced split: only the prepared query operands (FP4: 3 MFMA operands
+    # one forced split: only the prepared query operands (FP4: 2 MFMA operands
     # of 8 dwords per lane for each 8-row tile of each (sequence, KV head))
     one = L.kvq_decode_workspace_bytes(ctypes.byref(d), 32, 64, 1, 32768, kvq.splits_flag(1))
-    assert one == 32 * d.num_kv_heads * 1 * 64 * 4 * 3 * 8
+    assert one == 32 * d.num_kv_heads * 1 * 64 * 4 * 2 * 8
     assert need > one
     # an empty context is planned like a one-token context; a negative one is invalid
     z = L.kvq_decode_workspace_bytes(ctypes.byref(d), 32, 64, 1, 0, 0)

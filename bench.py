@@ -53,6 +53,7 @@ def parse():
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-mla", action="store_true", help="skip the head_dim 512 latent decode")
     ap.add_argument("--no-mix", action="store_true", help="skip the shared-prefix MTP mix")
+    ap.add_argument("--no-extend", action="store_true", help="skip the extend-chunk attention")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain fp32 elementwise kernel over 2 x 512 MiB "
                          "(reference for the HBM byte counters)")
@@ -313,6 +314,11 @@ def main():
     if not args.no_mix:
         mix = bench_mix(kvq, syn, dev, stream, max(args.steps // 2, 20), R)
 
+    # ---------------- extend chunk (many query rows per KV head, MFMA-bound)
+    ext = None
+    if not args.no_extend:
+        ext = bench_extend(kvq, syn, dev, stream, max(args.steps // 10, 10), R)
+
     # ---------------- latent-width decode (head_dim 512, MFMA-bound)
     mla = None
     if not args.no_mla:
@@ -357,6 +363,7 @@ def main():
         "fp8_comparator": fp8,
         "append_bulk": append_bulk,
         "agentic_mix": mix,
+        "extend_chunk": ext,
         "latent_512": mla,
         "cpu_baseline": cpu,
     }
@@ -413,6 +420,66 @@ def bench_mix(kvq, syn, dev, stream, steps, R, name="mtp_mixed_b32"):
         "unique_kv_bytes": unique,
         "logical_gbs": round(logical / (t * 1e-3) / 1e9, 1),
         "unique_gbs": round(unique / (t * 1e-3) / 1e9, 1),
+    }
+
+
+def bench_extend(kvq, syn, dev, stream, steps, R, chunk=1024):
+    """Attention of an extend (prefill) chunk over the FP4 cache: batch 4,
+    8 KV / 64 query heads, head_dim 128, context 32768 whose last `chunk`
+    tokens are the new chunk (position j sees tokens 0 .. L - chunk + j).
+    Mean HIP-event time of one call over cache replicas, against the MFMA
+    time of the instructions the kernel issues (four FP4 x FP6 query terms
+    for QK^T, bf16 hi + lo for PV)."""
+    import torch
+    wl = syn.Workload("extend_b4_l32k", batch=4, num_kv_heads=8, num_q_heads=64, head_dim=128,
+                      page_size=16, context=32768, n_q=chunk,
+                      description="batch 4, 8 KV / 64 Q heads, d128, context 32768 of which the "
+                                  "last %d tokens are the chunk" % chunk)
+    plan = syn.page_plan(wl)
+    c, _ = build_cache(kvq, syn, wl, plan, kvq.FMT_FP4_E2M1, dev)
+    cs = replicate(kvq, c, R)
+    q = syn.queries(wl, dev)
+    bt = torch_from(plan.block_tables, dev)
+    cl = torch_from(plan.context_lens, dev)
+    maxL = int(plan.context_lens.max())
+    B, HQ, NQ, D = wl.batch, wl.num_q_heads, wl.n_q, wl.head_dim
+    out = torch.empty((B, NQ, HQ, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(kvq.decode_workspace_bytes(c, B, HQ, NQ, maxL), dtype=torch.uint8, device=dev)
+    for i in range(3):
+        kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream)
+    torch.cuda.synchronize()
+    es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i, (a, b) in enumerate(es):
+        a.record(stream)
+        kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t = statistics.fmean([a.elapsed_time(b) for a, b in es])
+    L = wl.context
+    visible = NQ * (L - NQ) + NQ * (NQ + 1) // 2          # (position, token) pairs per query head
+    row_tokens = float(visible) * HQ * B
+    alg_flops = 4.0 * D * row_tokens
+    qk_flops = 2.0 * D * row_tokens * 4
+    pv_flops = 2.0 * D * row_tokens * 2
+    t_peak = qk_flops / (PEAK_FP4_FP6 * 1e12) + pv_flops / (PEAK_BF16 * 1e12)
+    issued = qk_flops + pv_flops
+    del cs, c
+    return {
+        "workload": "extend_b4_l32k: %s" % wl.description,
+        "chunk_tokens": NQ,
+        "rows_per_kv_head": wl.group * NQ,
+        "decode_ms_events_mean": round(t, 4),
+        "algorithmic_tflops": round(alg_flops / (t * 1e-3) / 1e12, 1),
+        "tokens_per_s": round(B * NQ / (t * 1e-3), 1),
+        "roofline": {
+            "bound": "mfma", "unit": "TFLOP/s",
+            "achieved": round(issued / (t * 1e-3) / 1e12, 1),
+            "peak": round(issued / t_peak / 1e12, 1),
+            "frac": round(t_peak / (t * 1e-3), 4),
+            "traffic": None,
+            "note": "issued MFMA flops (QK^T 4 FP4xFP6 terms at 10.1 PF/s, PV bf16 hi+lo at 2.5 PF/s); "
+                    "peak = their time-weighted dense peak",
+        },
     }
 
 

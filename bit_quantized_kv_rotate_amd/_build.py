@@ -33,6 +33,7 @@ SOURCES = {
     "kvq_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     # head_dim 512: the accumulators need the AGPR half of the register file
     "kvq_decode512.hip": [],
+    "kvq_extend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -629,12 +629,20 @@ int resident_waves(int fmt, int row_tiles) {
 
 int plan_decode(const CacheGeom& c, int batch, int hq, int n_q, int max_context_len, uint32_t flags,
                 DecodePlan* plan) {
-  if (c.d == 512) return plan_decode512(c, batch, hq, n_q, max_context_len, flags, plan);
+  if (c.d == 512) {
+    plan->kind = kDecodeLatent;
+    return plan_decode512(c, batch, hq, n_q, max_context_len, flags, plan);
+  }
   if (c.d != kD) return KVQ_ERR_UNSUPPORTED;
   const int group = hq / c.hkv;
-  const int rows = group * n_q;
+  const long long rows_ll = (long long)group * n_q;
+  if (rows_ll > 24) {
+    plan->kind = kDecodeMany;
+    return plan_extend(c, batch, hq, n_q, max_context_len, flags, plan);
+  }
+  plan->kind = kDecodeFew;
+  const int rows = (int)rows_ll;
   const int row_tiles = (rows + 7) / 8;
-  if (row_tiles > 3) return KVQ_ERR_UNSUPPORTED;
   const int n_tiles = (max_context_len + 15) / 16;
   int splits = (int)((flags & KVQ_SPLITS_MASK) >> KVQ_SPLITS_SHIFT);
   if (splits <= 0) {
@@ -676,7 +684,8 @@ int plan_decode(const CacheGeom& c, int batch, int hq, int n_q, int max_context_
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
-  if (a.c.d == 512) return launch_decode512(a, stream);
+  if (a.plan.kind == kDecodeLatent) return launch_decode512(a, stream);
+  if (a.plan.kind == kDecodeMany) return launch_extend(a, stream);
   DecodeParams p;
   p.kc = a.c.kc;
   p.ks = a.c.ks;

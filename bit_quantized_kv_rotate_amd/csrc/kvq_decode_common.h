@@ -22,6 +22,8 @@ struct DecodeParams {
   int P;
   int p_shift;  // log2(P)
   int hkv;
+  int batch;     // sequences (set by the kernels that derive units from it)
+  int rows_pad;  // padded rows per (sequence, KV head) of the many-row kernel
   const uint16_t* q;
   int hq, n_q, group, rows;
   const int32_t* block_tables;
@@ -163,16 +165,18 @@ constexpr int kMaxSplits = 64;
 
 // Combine the split partials of each query row: weights 2^(m_s - M),
 // normalise by the combined sum, rotate back, store.  One wave per row
-// (four per block, ROWS padded rows per (sequence, KV head)); lane s < S
+// (four per block, ROWS padded rows per (sequence, KV head), or p.rows_pad
+// when ROWS is 0); lane s < S
 // holds split s's (m, l), lane l accumulates channels C l .. C l + C - 1 of
 // the D = 64 C channels over the splits.
-template <int ROWS, int C>
+template <int ROWS_T, int C>
 __global__ __launch_bounds__(256) void merge_kernel(const DecodeParams p) {
   constexpr int D = 64 * C;
+  const int ROWS = ROWS_T > 0 ? ROWS_T : p.rows_pad;  // 0: padded row count at run time
   const int lane = threadIdx.x & 63;
-  const int gr = blockIdx.x * 4 + (threadIdx.x >> 6);  // grid covers exactly B * hkv * ROWS
-  const int r = gr % ROWS;
-  const int bh = gr / ROWS;
+  const long long gr = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);  // grid covers exactly B * hkv * ROWS
+  const int r = (int)(gr % ROWS);
+  const int bh = (int)(gr / ROWS);
   if (r >= p.rows) return;  // padding row: the whole wave leaves (no barrier follows)
   const int kvh = bh % p.hkv;
   const int b = bh / p.hkv;

@@ -1,0 +1,461 @@
+// Attention of many query rows per KV head over the FP4 cache, head_dim 128:
+// prefill / extend chunks (n_q new tokens already appended, position j of the
+// chunk sees tokens 0 .. L - n_q + j) and decode shapes with more than 24 rows
+// per KV head (wide query groups x MTP positions).
+//
+// Method: ROCm blog "UltraQuant on AMD Instinct", section "What is
+// UltraQuant?" (FP4 codes and power-of-two scales straight into the scaled
+// MFMA); the blog's key results include the time to first token, which is
+// this step.  With hundreds of rows per KV head the work is MFMA-bound: one
+// block of 8 waves per (row block of 128 rows, sequence, KV head, context
+// split) stages each 16-token tile once in LDS -- the K codes as the scaled
+// MFMA's A operand, V as bf16 rows -- and every wave runs its own 16 rows
+// against it:
+//  * scores S^T = K q^T with the FP4 K codes and scale bytes as A and four
+//    FP6 query terms accumulated in the same 16 x 16 tile (16 full rows);
+//  * online softmax per row, P split into bf16 hi + lo;
+//  * PV with hi and lo in the MFMA rows (rows 0-7 and 8-15 of the wave in two
+//    accumulator sets), so each V operand read serves 32 rows x 32 tokens.
+// One barrier per tile pair; LDS is double-buffered by pair parity.
+#include <atomic>
+
+#include "kvq_decode_common.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kDX = 128;
+constexpr int kTX = 4;                // FP6 query terms
+constexpr int kWX = 8;                // waves per block
+constexpr int kRowsX = 16 * kWX;      // rows per block
+constexpr int kVRowX = 2 * kDX + 32;  // LDS bytes per bf16 token row (padded)
+constexpr int kRingX = 2;             // tile pairs in flight per staging wave
+
+// Query prologue, one wave per query row (rows of a KV head padded to a
+// multiple of 128): load, rotate, pre-scale, split into kTX FP6 terms per
+// 32-channel block and store the B operands [B][hkv][rows_pad / 16]
+// [kTX][64 lanes][8 dwords]: lane (k-group j, column n) holds term t of row
+// 16 g + n, channels 32 j .. 32 j + 31 (6 packed dwords), its scale, a pad.
+__global__ __launch_bounds__(256) void qprep_ext_kernel(const DecodeParams p) {
+  const int lane = threadIdx.x & 63;
+  const long long gr = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);  // grid covers B * hkv * rows_pad
+  const int r = (int)(gr % p.rows_pad);
+  const long long bh = gr / p.rows_pad;
+  const int kvh = (int)(bh % p.hkv);
+  const int b = (int)(bh / p.hkv);
+
+  float x[2] = {0.0f, 0.0f};
+  if (r < p.rows) {
+    const int j = r / p.group;
+    const int hh = r - j * p.group;
+    const uint16_t* src = p.q + (((size_t)b * p.n_q + j) * p.hq + (size_t)kvh * p.group + hh) * kDX + 2 * lane;
+    x[0] = bf16_to_f32(src[0]);
+    x[1] = bf16_to_f32(src[1]);
+  }
+  if (p.rotate_q) wave_fwht<2>(x, lane, p.norm);
+  x[0] = x[0] * p.qscale;
+  x[1] = x[1] * p.qscale;
+
+  // 16 lanes per 32-channel block; lane i of the block holds bits 12i ..
+  // 12i + 11 of the block's 192-bit stream; lanes 0..5 assemble its dwords,
+  // lane 6 the scale byte, lane 7 a zero pad
+  const int blk = lane >> 4;
+  const int li = lane & 15;
+  const int w = min(li, 5);
+  const int src_a = 16 * blk + 8 * (w / 3) + 2 * (w % 3);
+  const int sh = 8 * (w % 3);
+  const int g = r >> 4;
+  const int n = r & 15;
+  uint32_t* base = p.qops + (size_t)bh * (p.rows_pad / 16) * kTX * 64 * 8;
+#pragma unroll
+  for (int t = 0; t < kTX; ++t) {
+    float am = fmaxf(fabsf(x[0]), fabsf(x[1]));
+    am = fmaxf(am, __shfl_xor(am, 1, 64));
+    am = fmaxf(am, __shfl_xor(am, 2, 64));
+    am = fmaxf(am, __shfl_xor(am, 4, 64));
+    am = fmaxf(am, __shfl_xor(am, 8, 64));
+    const int byte = max((int)((as_u32(am) >> 23) & 0xFFu) - 2, 0);
+    const int e = byte - 127;
+    float v0, v1;
+    const uint32_t c0 = e2m3_split(x[0], e, v0);
+    const uint32_t c1 = e2m3_split(x[1], e, v1);
+    x[0] -= v0;
+    x[1] -= v1;
+    const uint32_t v12 = c0 | (c1 << 6);
+    const uint32_t u24 = v12 | ((uint32_t)__shfl_xor((int)v12, 1, 64) << 12);  // valid on even li
+    const uint32_t ua = (uint32_t)__shfl((int)u24, src_a, 64);
+    const uint32_t ub = (uint32_t)__shfl((int)u24, src_a + 2, 64);
+    const uint32_t d = (ua >> sh) | (ub << (24 - sh));
+    uint32_t* dst = base + (((size_t)g * kTX + t) * 64 + 16 * blk + n) * 8;
+    if (li < 8) dst[li] = (li < 6) ? d : (li == 6 ? (uint32_t)byte : 0u);
+  }
+}
+
+// Raw codes a staging wave holds for one tile pair: its one 16-token tile of
+// K (codes + scale byte) or of V, lane l = token l%16, group l/16.
+struct Stage {
+  uint32_t c[4];
+  uint32_t sc;
+};
+
+__device__ __forceinline__ void load_stage(const DecodeParams& p, const int32_t* bt_row, int kvh, int tile,
+                                           bool v, int lane, Stage& t) {
+  const int tok = tile * 16;
+  const int page = __builtin_amdgcn_readfirstlane(bt_row[tok >> p.p_shift]);
+  const int in_page = tok & (p.P - 1);
+  const int64_t cb = (int64_t)page * p.c_page + (int64_t)kvh * p.c_head;
+  const int64_t sb = (int64_t)page * p.s_page + (int64_t)kvh * p.s_head;
+  const int idx = (lane >> 4) * p.P + (lane & 15);
+  const __amdgpu_buffer_rsrc_t rc = block_rsrc(v ? p.vc : p.kc, cb, p.c_head);
+  const __amdgpu_buffer_rsrc_t rs = block_rsrc(v ? p.vs : p.ks, sb, p.s_head);
+  const u32x4_t a = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, idx * 16, in_page * 16, 2));
+#pragma unroll
+  for (int w = 0; w < 4; ++w) t.c[w] = a[w];
+  t.sc = __builtin_amdgcn_raw_buffer_load_b8(rs, idx, in_page, 0);
+}
+
+__global__ __launch_bounds__(512) void extend_kernel(const DecodeParams p) {
+  __shared__ __attribute__((aligned(16))) u32x4_t s_k[2][2][64];
+  __shared__ uint32_t s_ks[2][2][64];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[2][2][16][kVRowX];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int col = lane & 15;
+  const int quad = lane >> 4;
+  const bool hi_col = col < 8;
+  // 1-D grid: split fastest, then (sequence, KV head), then row block; the
+  // row blocks of one (unit, split) share its K/V tiles, and with a unit
+  // count divisible by 8 they land on one XCD (one L2)
+  const int units = p.hkv * p.batch;
+  const int split = blockIdx.x % p.splits;
+  const int u = (blockIdx.x / p.splits) % units;
+  const int rb = blockIdx.x / (p.splits * units);
+  const int kvh = u % p.hkv;
+  const int b = u / p.hkv;
+  const int L = p.context_lens[b];
+  const int n_tiles = (L + 15) >> 4;
+  const int t_begin = split * p.tiles_per_split;
+  // the last token any row of this block may see
+  const int r_last_blk = min(p.rows, (rb + 1) * kRowsX) - 1;
+  const int blk_lim = L - p.n_q + r_last_blk / p.group;
+  const int t_end = min(min(n_tiles, t_begin + p.tiles_per_split), (blk_lim >> 4) + 1);
+  const int tok_limit = min(L, t_end * 16);
+  const int32_t* bt_row = p.block_tables + (size_t)b * p.max_pages;
+  const int n_pairs = (t_end > t_begin) ? ((t_end - t_begin + 1) >> 1) : 0;
+  const int n_iter = (n_pairs + kRingX - 1) / kRingX;  // pairs padded to a multiple of kRingX
+
+  // staging role: waves 0..3 stage K tile 0, K tile 1, V tile 0, V tile 1
+  const bool stager = w < 4;
+  const int st_tile = w & 1;
+  const bool st_v = (w >> 1) & 1;
+  auto fetch = [&](int pi, Stage& c) {
+    load_stage(p, bt_row, kvh, min(t_begin + 2 * pi + st_tile, t_end - 1), st_v, lane, c);
+  };
+  auto stage = [&](int pi, const Stage& c) {
+    const int par = pi & 1;
+    if (!st_v) {
+      s_k[par][st_tile][lane] = u32x4_t{c.c[0], c.c[1], c.c[2], c.c[3]};
+      s_ks[par][st_tile][lane] = c.sc;
+    } else {
+      // zero values past the context (their weights are zero; the cache may
+      // hold anything there)
+      const bool dead = (t_begin + 2 * pi + st_tile) * 16 + col >= tok_limit;
+      uint32_t vw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) vw[i] = dead ? 0u : c.c[i];
+      uint32_t vb[16];
+      dequant_group<KVQ_FMT_FP4_E2M1>(vw, scale_operand(dead ? 0u : c.sc), vb);
+      u32x4_t* dst = reinterpret_cast<u32x4_t*>(&s_v[par][st_tile][col][64 * quad]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = u32x4_t{vb[4 * i], vb[4 * i + 1], vb[4 * i + 2], vb[4 * i + 3]};
+    }
+  };
+
+  Stage ring[kRingX];
+  if (stager && n_pairs > 0) {
+#pragma unroll
+    for (int k = 0; k < kRingX; ++k) fetch(k, ring[k]);
+  }
+
+  // this wave's 16 rows: query operands (four terms, one per MFMA)
+  const int r0 = rb * kRowsX + 16 * w;
+  const int g = r0 >> 4;
+  i32x8_t qb[kTX];
+  int qs[kTX];
+  {
+    const uint32_t* src = p.qops + (((size_t)u * (p.rows_pad / 16) + g) * kTX * 64 + lane) * 8;
+#pragma unroll
+    for (int t = 0; t < kTX; ++t) {
+      const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(src + (size_t)t * 64 * 8);
+      const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(src + (size_t)t * 64 * 8 + 4);
+      qb[t] = i32x8_t{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], 0, 0};
+      qs[t] = (int)a1[2];
+    }
+  }
+  const int row = r0 + col;  // this lane's row (scores and softmax)
+  const int row_lim = (row < p.rows) ? min(tok_limit - 1, L - p.n_q + row / p.group) : -1;
+  float m_run = -INFINITY, l_run = 0.0f;
+  f32x4_t O1[8], O2[8];  // rows 0-7 and 8-15 of the wave: hi in MFMA rows 0-7, lo in 8-15
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    O1[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    O2[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  if (stager && n_pairs > 0) {
+    stage(0, ring[0]);
+    fetch(kRingX, ring[0]);
+  }
+  __syncthreads();
+
+#pragma unroll 1
+  for (int it = 0; it < n_iter; ++it) {
+#pragma unroll
+    for (int k = 0; k < kRingX; ++k) {
+      const int pi = it * kRingX + k;
+      const int par = pi & 1;
+      const int tile = t_begin + 2 * pi;
+      // ---- stage the next pair (its buffer was last read before the
+      // previous barrier), refill the ring slot
+      if (stager) {
+        const int nk = (k + 1) % kRingX;
+        stage(pi + 1, ring[nk]);
+        fetch(pi + 1 + kRingX, ring[nk]);
+      }
+      // ---- scores of the wave's 16 rows (past the last pair every score is
+      // masked: the softmax state does not change)
+      f32x4_t S[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const u32x4_t kc = s_k[par][s][lane];
+        const int ksc = (int)s_ks[par][s][lane];
+        const i32x8_t A = {(int)kc[0], (int)kc[1], (int)kc[2], (int)kc[3], 0, 0, 0, 0};
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < kTX; ++t)
+          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, qb[t], acc, 4, 2, 0, ksc, 0, qs[t]);
+        S[s] = acc;
+      }
+      float sc[8];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tok = (tile + s) * 16 + 4 * quad + i;
+          sc[4 * s + i] = (tok <= row_lim) ? S[s][i] : -INFINITY;
+        }
+      float mloc = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                         fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+      mloc = quad_max(mloc);
+      const float m_old = m_run;
+      const float m_new = fmaxf(m_old, mloc);
+      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+      m_run = m_new;
+      float psum = 0.0f;
+      uint32_t h[4], l[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(sc[2 * e] - m_use);
+        const float p1 = __builtin_amdgcn_exp2f(sc[2 * e + 1] - m_use);
+        psum += p0 + p1;
+        const uint32_t u0 = as_u32(p0), u1 = as_u32(p1);
+        h[e] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+        l[e] = pack_bf16x2(p0 - as_f32(u0 & 0xFFFF0000u), p1 - as_f32(u1 & 0xFFFF0000u));
+      }
+      // A operands with hi / lo in the MFMA rows: rows 0-7 of the wave
+      // (lanes c < 8 own hi, lanes c >= 8 take lo of row c - 8 from lane
+      // c - 8) and rows 8-15 (lanes c < 8 take hi of row c + 8)
+      uint32_t a1[4], a2[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lr = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)l[e], 0x128, 0xF, 0xF, false);
+        const uint32_t hr = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)h[e], 0x128, 0xF, 0xF, false);
+        a1[e] = hi_col ? h[e] : lr;
+        a2[e] = hi_col ? hr : l[e];
+      }
+      if (__builtin_amdgcn_ballot_w64(m_new != m_old)) {
+        // a row max moved: rescale; O1 lane (q, c) holds rows (4q + i) & 7,
+        // O2 rows 8 + ((4q + i) & 7)
+        const float alpha = __builtin_amdgcn_exp2f(m_old - m_use);
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float al1 = __shfl(alpha, (4 * quad + i) & 7, 64);
+          const float al2 = __shfl(alpha, 8 + ((4 * quad + i) & 7), 64);
+#pragma unroll
+          for (int n = 0; n < 8; ++n) {
+            O1[n][i] *= al1;
+            O2[n][i] *= al2;
+          }
+        }
+      }
+      l_run += psum;
+      const bf16x8_t A1 = __builtin_bit_cast(bf16x8_t, u32x4_t{a1[0], a1[1], a1[2], a1[3]});
+      const bf16x8_t A2 = __builtin_bit_cast(bf16x8_t, u32x4_t{a2[0], a2[1], a2[2], a2[3]});
+
+      // ---- PV: B operands read transposed from the LDS V tiles
+      const int rr = col >> 2;
+      const int c4 = (col & 3) * 4;
+      typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+      auto read_b = [&](int n) {
+        lds_bf16x4* p0 = (lds_bf16x4*)((__attribute__((address_space(3))) uint8_t*)&s_v[par][0][4 * quad + rr][2 * (16 * n + c4)]);
+        lds_bf16x4* p1 = (lds_bf16x4*)((__attribute__((address_space(3))) uint8_t*)&s_v[par][1][4 * quad + rr][2 * (16 * n + c4)]);
+        const u32x2_t w0 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p0));
+        const u32x2_t w1 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p1));
+        return __builtin_bit_cast(bf16x8_t, u32x4_t{w0[0], w0[1], w1[0], w1[1]});
+      };
+      bf16x8_t B0 = read_b(0);
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const bf16x8_t C0 = (n + 1 < 8) ? read_b(n + 1) : B0;
+        O1[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B0, O1[n], 0, 0, 0);
+        O2[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, B0, O2[n], 0, 0, 0);
+        B0 = C0;
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- partials: hi + lo halves of O (lanes 0..31 then hold rows 4q + i of
+  // O1 / O2 for q = 0, 1), row sums; rows past p.rows are padding
+  const float lrow = quad_sum(l_run);
+#pragma unroll
+  for (int n = 0; n < 8; ++n)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      O1[n][i] = add_half_swap(O1[n][i]);
+      O2[n][i] = add_half_swap(O2[n][i]);
+    }
+  const size_t base = ((size_t)u * p.splits + split) * p.rows_pad + r0;
+  if (lane < 32) {
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p.ws_o[(base + 4 * quad + i) * kDX + 16 * n + col] = O1[n][i];
+        p.ws_o[(base + 8 + 4 * quad + i) * kDX + 16 * n + col] = O2[n][i];
+      }
+  }
+  if (lane < 16) {
+    p.ws_ml[(base + lane) * 2 + 0] = m_run;
+    p.ws_ml[(base + lane) * 2 + 1] = lrow;
+  }
+}
+
+constexpr int kMinTilesPerSplitX = 8;
+constexpr int kMaxTilesPerSplitX = 512;
+constexpr int kDefaultSlotsX = 256;  // one block per CU
+constexpr int kMaxDevicesX = 64;
+constexpr int kMaxRowsX = 1 << 16;
+
+int resident_blocks_x() {
+  static std::atomic<int> cache[kMaxDevicesX];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  if (dev < kMaxDevicesX) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int cus = 0, blocks = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, extend_kernel, 64 * kWX, 0) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  const int v = cus * blocks;
+  if (dev < kMaxDevicesX) cache[dev].store(v, std::memory_order_relaxed);
+  return v;
+}
+
+}  // namespace
+
+int plan_extend(const CacheGeom& c, int batch, int hq, int n_q, int max_context_len, uint32_t flags,
+                DecodePlan* plan) {
+  if (c.d != kDX || c.fmt != KVQ_FMT_FP4_E2M1) return KVQ_ERR_UNSUPPORTED;
+  const long long rows = (long long)(hq / c.hkv) * n_q;
+  if (rows > kMaxRowsX) return KVQ_ERR_UNSUPPORTED;
+  const int row_blocks = (int)((rows + kRowsX - 1) / kRowsX);
+  const int n_tiles = (max_context_len + 15) / 16;
+  int splits = (int)((flags & KVQ_SPLITS_MASK) >> KVQ_SPLITS_SHIFT);
+  if (splits <= 0) {
+    // one round of blocks over the device, at least kMinTilesPerSplitX tiles
+    // and at most kMaxTilesPerSplitX per split
+    int slots = resident_blocks_x();
+    if (slots <= 0) slots = kDefaultSlotsX;
+    const long long work = (long long)batch * c.hkv * row_blocks;
+    long long want = work >= slots ? 1 : slots / work;
+    const long long by_len = n_tiles / kMinTilesPerSplitX;
+    if (want > by_len) want = by_len;
+    const long long by_cap = (n_tiles + kMaxTilesPerSplitX - 1) / kMaxTilesPerSplitX;
+    if (want < by_cap) want = by_cap;
+    splits = (int)(want < 1 ? 1 : want);
+  }
+  if (splits > kMaxSplits) splits = kMaxSplits;
+  int per = (n_tiles + splits - 1) / splits;
+  per = (per + 1) & ~1;
+  if (per < 2) per = 2;
+  splits = (n_tiles + per - 1) / per;
+  if (splits < 1) splits = 1;
+  const size_t rows_pad = (size_t)row_blocks * kRowsX;
+  plan->rows = (int)rows;
+  plan->row_tiles = row_blocks;
+  plan->splits = splits;
+  plan->tiles_per_split = per;
+  plan->qops_bytes = (size_t)batch * c.hkv * (rows_pad / 16) * kTX * 64 * 8 * sizeof(uint32_t);
+  plan->workspace = plan->qops_bytes + (size_t)batch * c.hkv * splits * rows_pad * (kDX + 2) * sizeof(float);
+  return KVQ_OK;
+}
+
+hipError_t launch_extend(const DecodeArgs& a, hipStream_t stream) {
+  DecodeParams p;
+  p.kc = a.c.kc;
+  p.ks = a.c.ks;
+  p.vc = a.c.kv_shared ? a.c.kc : a.c.vc;
+  p.vs = a.c.kv_shared ? a.c.ks : a.c.vs;
+  p.c_head = a.c.c_head;
+  p.c_page = a.c.c_page;
+  p.s_head = a.c.s_head;
+  p.s_page = a.c.s_page;
+  p.P = a.c.p;
+  p.p_shift = __builtin_ctz((unsigned)a.c.p);
+  p.hkv = a.c.hkv;
+  p.batch = a.batch;
+  p.q = a.q;
+  p.hq = a.hq;
+  p.n_q = a.n_q;
+  p.group = a.group;
+  p.rows = a.plan.rows;
+  p.rows_pad = a.plan.row_tiles * kRowsX;
+  p.block_tables = a.block_tables;
+  p.max_pages = a.max_pages;
+  p.context_lens = a.context_lens;
+  p.qscale = a.qscale;
+  p.norm = fwht_norm(kDX);
+  p.rotate_q = a.rotate_q;
+  p.rotate_out = a.rotate_out;
+  p.splits = a.plan.splits;
+  p.tiles_per_split = a.plan.tiles_per_split;
+  p.out = a.out;
+  const size_t units = (size_t)a.batch * a.c.hkv;
+  const size_t n_o = units * a.plan.splits * (size_t)p.rows_pad * kDX;
+  uint8_t* ws = reinterpret_cast<uint8_t*>(a.workspace);
+  p.qops = reinterpret_cast<uint32_t*>(ws);
+  p.ws_o = reinterpret_cast<float*>(ws + a.plan.qops_bytes);
+  p.ws_ml = p.ws_o + n_o;
+  const unsigned qblocks = (unsigned)(units * p.rows_pad / 4);
+  hipLaunchKernelGGL(qprep_ext_kernel, dim3(qblocks), dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const dim3 grid((unsigned)((size_t)p.splits * units * a.plan.row_tiles));
+  hipLaunchKernelGGL(extend_kernel, grid, dim3(64 * kWX), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((merge_kernel<0, 2>), dim3(qblocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -44,8 +44,9 @@ hipError_t launch_dequant(const CacheGeom& c, const int32_t* slots, int n,
                           float* k_out, float* v_out, hipStream_t stream);
 
 struct DecodePlan {
+  int kind;              // kDecodeFew, kDecodeMany or kDecodeLatent
   int rows;              // query rows per KV head = n_q * group
-  int row_tiles;         // 8-row tiles (hi/lo split fills a 16-wide MFMA)
+  int row_tiles;         // 8-row tiles (few), 128-row blocks (many), 16-row groups (latent)
   int splits;            // context splits per (sequence, KV head)
   int tiles_per_split;   // 16-token tiles per split (even)
   size_t qops_bytes;     // query operands (first part of the workspace)
@@ -72,6 +73,16 @@ struct DecodeArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// which decode kernel family a plan uses
+constexpr int kDecodeFew = 0;     // head_dim 128, up to 24 rows per KV head (kvq_decode.hip)
+constexpr int kDecodeMany = 1;    // head_dim 128, more rows (kvq_extend.hip)
+constexpr int kDecodeLatent = 2;  // head_dim 512 (kvq_decode512.hip)
+
+// many rows per KV head (extend / prefill chunks): kvq_extend.hip
+int plan_extend(const CacheGeom& c, int batch, int hq, int n_q, int max_context_len, uint32_t flags,
+                DecodePlan* plan);
+hipError_t launch_extend(const DecodeArgs& a, hipStream_t stream);
 
 // head_dim 512 (latent width): planned and launched by kvq_decode512.hip
 int plan_decode512(const CacheGeom& c, int batch, int hq, int n_q, int max_context_len, uint32_t flags,

@@ -147,7 +147,11 @@ size_t kvq_decode_workspace_bytes(const kvq_cache_desc *desc, int32_t batch,
  * decode step that reads codes and scales natively, no lookup table).
  *   q               bf16 [batch][n_q][num_q_heads][head_dim]
  *   num_q_heads     multiple of num_kv_heads; query head h reads KV head
- *                   h / (num_q_heads / num_kv_heads)
+ *                   h / (num_q_heads / num_kv_heads).  Rows per KV head =
+ *                   n_q * num_q_heads / num_kv_heads: up to 65536 at
+ *                   head_dim 128 (more than 24 rows run the many-row kernel
+ *                   meant for prefill / extend chunks), up to 64 at
+ *                   head_dim 512; other head_dims: KVQ_ERR_UNSUPPORTED
  *   n_q             query positions per sequence (MTP verify: > 1); the last
  *                   n_q cached tokens are the verify tokens and position j
  *                   sees tokens 0 .. context_lens[b] - n_q + j
@@ -173,7 +177,8 @@ int kvq_decode_attn_fp4(const kvq_cache_desc *desc, const void *q,
 
 /* The same decode over an FP8 (E4M3, per-32 UE8M0 scale) cache: the 8-bit
  * comparator of "UltraQuant vs 8-bit KV".  Identical arguments; returns
- * KVQ_ERR_FORMAT unless desc->format == KVQ_FMT_FP8_E4M3. */
+ * KVQ_ERR_FORMAT unless desc->format == KVQ_FMT_FP8_E4M3, and
+ * KVQ_ERR_UNSUPPORTED for head_dim != 128 or more than 24 rows per KV head. */
 int kvq_decode_attn_fp8(const kvq_cache_desc *desc, const void *q,
                         int32_t batch, int32_t num_q_heads, int32_t n_q,
                         const int32_t *block_tables, int32_t max_pages_per_seq,

@@ -101,7 +101,10 @@ def test_decode_argument_errors():
     assert _decode(desc=_desc(fmt=2)) == -3      # FP4 entry point, FP8 cache
     assert _decode(fn="kvq_decode_attn_fp8", desc=_desc(fmt=1)) == -3
     assert _decode(desc=_desc(d=64)) == -4       # no kernel for head_dim 64 yet
-    assert _decode(hq=8 * 32) == -4              # 32 rows per KV head: not built
+    # more than 24 rows per KV head: FP4 has the many-row kernel, FP8 does not
+    assert _decode(fn="kvq_decode_attn_fp8", hq=8 * 32) == -4
+    assert kvq.library().kvq_decode_workspace_bytes(ctypes.byref(_desc()), 2, 8 * 32, 1, 128, 0) > 0
+    assert kvq.library().kvq_decode_workspace_bytes(ctypes.byref(_desc()), 2, 8 * 8193, 8, 128, 0) == 0
     # latent width 512: FP4 up to 64 rows per KV head; no FP8 kernel at 512
     d512 = _desc(d=512, hkv=1, p=64, shared=1)
     L = kvq.library()

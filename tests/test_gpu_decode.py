@@ -188,3 +188,36 @@ def test_decode_latent_512_split_invariance(gpu):
         np.testing.assert_allclose(got, ref, rtol=1e-5, atol=5e-5)
     want = oracle_decode_batch(f, syn.bf16_bits(q))
     assert_close(ref[0], want[0], "latent one split")
+
+
+@pytest.mark.parametrize("group,n_q,ctx", [
+    (16, 3, (100, 900)),      # GQA 16 x MTP 3: 48 rows
+    (8, 4, (33, 700)),        # 32 rows, contexts just above the chunk
+    (8, 64, (200, 1500)),     # extend chunk of 64 tokens: 512 rows
+    (4, 130, (300, 2000)),    # 520 rows: a padded last row block
+])
+def test_decode_many_rows(gpu, group, n_q, ctx):
+    """More than 24 rows per KV head: the many-row (extend / prefill) kernel,
+    with the causal rule between chunk positions."""
+    wl = syn.Workload("many_g%d_nq%d" % (group, n_q), batch=3, num_kv_heads=2, num_q_heads=2 * group,
+                      head_dim=128, page_size=16, context=0, n_q=n_q, ctx_range=ctx)
+    f, qh, out = _run(wl, "fp4")
+    want = oracle_decode_batch(f, qh)
+    for b in range(wl.batch):
+        assert_close(out[b], want[b], "many rows g%d n_q%d seq %d (L=%d)" % (group, n_q, b, int(f.plan.context_lens[b])))
+
+
+def test_decode_many_rows_split_invariance(gpu):
+    wl = syn.Workload("many_split", batch=2, num_kv_heads=1, num_q_heads=8, head_dim=128, page_size=32,
+                      context=1500, n_q=40)
+    f = Filled(wl, "fp4")
+    q = syn.queries(wl).cuda()
+    ref = f.decode(q, flags=kvq.splits_flag(1)).cpu().numpy()
+    for s in (2, 5, 11):
+        got = f.decode(q, flags=kvq.splits_flag(s)).cpu().numpy()
+        # each split rounds its weights to bf16 hi + lo against its own running
+        # maximum (2^-17 relative per weight) besides reordering the fp32 sums
+        np.testing.assert_allclose(got, ref, rtol=5e-5, atol=1e-4)
+    want = oracle_decode_batch(f, syn.bf16_bits(q))
+    for b in range(wl.batch):
+        assert_close(ref[b], want[b], "many rows one split seq %d" % b)

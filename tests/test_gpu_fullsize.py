@@ -9,6 +9,8 @@ compared element by element (max |err| <= 2e-3, relative L2 <= 1e-3).
                  from 4 prefixes, 3 MTP verify positions (24 rows per KV head)
   mla_b16_l128k  batch 16, one latent head of width 512 (K = V), 64 absorbed
                  query heads, context 131072, page 64
+  extend         batch 4, 8 KV / 64 Q heads, context 32768 whose last 64
+                 tokens are a new chunk (512 rows per KV head)
 """
 import numpy as np
 import pytest
@@ -64,3 +66,11 @@ def test_fullsize_mtp_mixed_b32_sampled(gpu):
 def test_fullsize_mla_b16_l128k_sampled(gpu):
     """Four whole sequences (all 64 rows) of the latent workload."""
     _check("mla_b16_l128k", "fp4", 4, 3)
+
+
+def test_fullsize_extend_chunk_sampled(gpu):
+    """An extend chunk over a 32K cache: the many-row kernel at full length."""
+    wl = syn.Workload("extend_b4_l32k_c64", batch=4, num_kv_heads=8, num_q_heads=64, head_dim=128,
+                      page_size=16, context=32768, n_q=64)
+    syn.WORKLOADS.setdefault(wl.name, wl)
+    _check(wl.name, "fp4", 4, 4)

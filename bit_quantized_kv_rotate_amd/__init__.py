@@ -18,7 +18,7 @@ from __future__ import annotations
 import ctypes
 import math
 import os
-from typing import Optional, Tuple
+from typing import Optional, Sequence, Tuple
 
 import torch  # loads torch's HIP runtime first; libkvq then shares it
 
@@ -66,11 +66,25 @@ class CacheDesc(ctypes.Structure):
     ]
 
 
+class PrefixGroupsDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_groups", ctypes.c_int32),
+        ("max_group_size", ctypes.c_int32),
+        ("indptr", ctypes.c_void_p),
+        ("members", ctypes.c_void_p),
+        ("prefix_tables", ctypes.c_void_p),
+        ("max_prefix_pages", ctypes.c_int32),
+        ("shared_lens", ctypes.c_void_p),
+        ("max_suffix_len", ctypes.c_int32),
+    ]
+
+
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 _U32 = ctypes.c_uint32
 _SZ = ctypes.c_size_t
 _DESC = ctypes.POINTER(CacheDesc)
+_GROUPS = ctypes.POINTER(PrefixGroupsDesc)
 
 # name -> (restype, argtypes); every symbol include/kvq.h declares
 SIGNATURES = {
@@ -82,6 +96,9 @@ SIGNATURES = {
                                            ctypes.c_float, _U32, _P, _P, _SZ, _P]),
     "kvq_decode_attn_fp8": (ctypes.c_int, [_DESC, _P, _I32, _I32, _I32, _P, _I32, _P, _I32,
                                            ctypes.c_float, _U32, _P, _P, _SZ, _P]),
+    "kvq_decode_shared_workspace_bytes": (_SZ, [_DESC, _I32, _I32, _I32, _GROUPS, _U32]),
+    "kvq_decode_attn_fp4_shared": (ctypes.c_int, [_DESC, _P, _I32, _I32, _I32, _P, _I32, _P, _GROUPS,
+                                                  ctypes.c_float, _U32, _P, _P, _SZ, _P]),
     "kvq_dequant": (ctypes.c_int, [_DESC, _P, _I32, _P, _P, _P]),
     "kvq_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "kvq_version": (ctypes.c_int, []),
@@ -253,6 +270,92 @@ def decode_attn_fp8(cache: KVCache, q: torch.Tensor, block_tables: torch.Tensor,
                     stream=None) -> torch.Tensor:
     return _decode("kvq_decode_attn_fp8", cache, q, block_tables, context_lens, max_context_len,
                    sm_scale, flags, out, workspace, stream)
+
+
+class PrefixGroups:
+    """Prefix groups of a shared-prefix decode: device int32 tensors plus the
+    host-side bounds (the fields of kvq_prefix_groups)."""
+
+    def __init__(self, indptr: torch.Tensor, members: torch.Tensor, prefix_tables: torch.Tensor,
+                 shared_lens: torch.Tensor, max_group_size: int, max_suffix_len: int):
+        if prefix_tables.dim() != 2 or prefix_tables.shape[0] != indptr.numel() - 1:
+            raise ValueError("prefix_tables must be [num_groups, max_prefix_pages]")
+        if members.numel() == 0:  # no member at all: a valid pointer is still passed
+            members = torch.zeros(1, dtype=torch.int32, device=indptr.device)
+        self.indptr, self.members = indptr, members
+        self.prefix_tables, self.shared_lens = prefix_tables, shared_lens
+        self.max_group_size, self.max_suffix_len = int(max_group_size), int(max_suffix_len)
+        self._desc = PrefixGroupsDesc(
+            int(indptr.numel() - 1), self.max_group_size, _dev(indptr, torch.int32, "indptr"),
+            _dev(members, torch.int32, "members"),
+            _dev(prefix_tables, torch.int32, "prefix_tables"), int(prefix_tables.shape[1]),
+            _dev(shared_lens, torch.int32, "shared_lens"), self.max_suffix_len)
+
+    @classmethod
+    def from_lists(cls, groups: Sequence[Sequence[int]], prefix_pages: Sequence[Sequence[int]],
+                   shared_lens: Sequence[int], context_lens: Sequence[int], device="cuda") -> "PrefixGroups":
+        """Build the tensors from host lists: groups[g] lists the member
+        sequences of prefix g, prefix_pages[g] its physical pages.  Members are
+        stored by decreasing shared length (the fastest order)."""
+        if len(groups) != len(prefix_pages) or not groups:
+            raise ValueError("one page list per group, at least one group")
+        indptr, members = [0], []
+        for g in groups:
+            members.extend(sorted(g, key=lambda b: -int(shared_lens[b])))
+            indptr.append(len(members))
+        width = max(1, max(len(pp) for pp in prefix_pages))
+        tables = torch.zeros((len(groups), width), dtype=torch.int32)
+        for i, pp in enumerate(prefix_pages):
+            tables[i, : len(pp)] = torch.as_tensor(list(pp), dtype=torch.int32)
+        suffix = max((int(L) - int(s) for L, s in zip(context_lens, shared_lens)), default=0)
+        as_dev = lambda x: torch.as_tensor(x, dtype=torch.int32).to(device)
+        return cls(as_dev(indptr), as_dev(members), tables.to(device), as_dev(list(shared_lens)),
+                   max(1, max(len(g) for g in groups)), max(suffix, 0))
+
+    def ref(self):
+        return ctypes.byref(self._desc)
+
+
+def decode_shared_workspace_bytes(cache: KVCache, batch: int, num_q_heads: int, n_q: int,
+                                  groups: PrefixGroups, flags: int = 0) -> int:
+    return int(library().kvq_decode_shared_workspace_bytes(cache.ref(), batch, num_q_heads, n_q,
+                                                           groups.ref(), flags))
+
+
+def decode_attn_fp4_shared(cache: KVCache, q: torch.Tensor, block_tables: torch.Tensor,
+                           context_lens: torch.Tensor, groups: PrefixGroups,
+                           sm_scale: Optional[float] = None, flags: int = 0,
+                           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """Shared-prefix decode: the result of decode_attn_fp4 with each group's
+    prefix pages read once for all its members."""
+    B, n_q, hq, d = (int(x) for x in q.shape)
+    if d != cache.head_dim:
+        raise ValueError("q head_dim %d does not match the cache (%d)" % (d, cache.head_dim))
+    qp = _dev(q, torch.bfloat16, "q")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [batch, max_pages]")
+    bp = _dev(block_tables, torch.int32, "block_tables")
+    _shape(context_lens, (B,), "context_lens")
+    cp = _dev(context_lens, torch.int32, "context_lens")
+    _shape(groups.shared_lens, (B,), "shared_lens")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, n_q, hq, d), dtype=torch.float32, device=q.device)
+    _shape(out, (B, n_q, hq, d), "out")
+    op = _dev(out, torch.float32, "out")
+    need = decode_shared_workspace_bytes(cache, B, hq, n_q, groups, flags)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wp, wbytes = None, 0
+    if workspace is not None:
+        wp = _dev(workspace, workspace.dtype, "workspace")
+        wbytes = workspace.numel() * workspace.element_size()
+    _check(library().kvq_decode_attn_fp4_shared(cache.ref(), qp, B, hq, n_q, bp, int(block_tables.shape[1]), cp,
+                                                 groups.ref(), float(sm_scale), int(flags), op, wp, wbytes,
+                                                 _stream(stream)))
+    return out
 
 
 def dequant(cache: KVCache, slots: torch.Tensor, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:

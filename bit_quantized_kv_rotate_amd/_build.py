@@ -34,6 +34,7 @@ SOURCES = {
     # head_dim 512: the accumulators need the AGPR half of the register file
     "kvq_decode512.hip": [],
     "kvq_extend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "kvq_shared.hip": [],
 }
 
 

@@ -109,6 +109,22 @@ int decode_common(int want_fmt, const kvq_cache_desc* desc, const void* q, int32
   return hip_status(launch_decode(a, (hipStream_t)stream));
 }
 
+// Host-side fields of a shared-prefix call's groups, and its plan.
+int plan_shared_call(const CacheGeom& g, int32_t batch, int32_t num_q_heads, int32_t n_q,
+                     const kvq_prefix_groups* groups, uint32_t flags, SharedPlan* plan) {
+  if (!groups) return KVQ_ERR_NULL;
+  if (batch <= 0 || num_q_heads <= 0 || n_q < 1 || num_q_heads % g.hkv != 0) return KVQ_ERR_SHAPE;
+  if (groups->num_groups < 1 || groups->max_group_size < 1 || groups->max_prefix_pages < 1 ||
+      groups->max_suffix_len < 0)
+    return KVQ_ERR_SHAPE;
+  if (flags & ~(KVQ_Q_PREROTATED | KVQ_OUT_ROTATED | KVQ_SPLITS_MASK)) return KVQ_ERR_SHAPE;
+  if ((int64_t)groups->max_prefix_pages * g.p > INT32_MAX) return KVQ_ERR_SHAPE;
+  if (g.d != 128) return KVQ_ERR_UNSUPPORTED;
+  const int64_t rows_seq = (int64_t)(num_q_heads / g.hkv) * n_q;
+  if (rows_seq > 65536 || rows_seq * groups->max_group_size > 65536) return KVQ_ERR_UNSUPPORTED;
+  return plan_shared(g, batch, num_q_heads, n_q, *groups, flags, plan);
+}
+
 }  // namespace
 }  // namespace kvq
 
@@ -156,6 +172,58 @@ size_t kvq_decode_workspace_bytes(const kvq_cache_desc* desc, int32_t batch, int
   if (plan_decode(g, batch, num_q_heads, n_q, max_context_len > 0 ? max_context_len : 1, flags, &plan) != KVQ_OK)
     return 0;
   return plan.workspace;
+}
+
+size_t kvq_decode_shared_workspace_bytes(const kvq_cache_desc* desc, int32_t batch, int32_t num_q_heads,
+                                         int32_t n_q, const kvq_prefix_groups* groups, uint32_t flags) {
+  CacheGeom g;
+  if (check_desc(desc, &g) != KVQ_OK || g.fmt != KVQ_FMT_FP4_E2M1) return 0;
+  SharedPlan plan;
+  if (plan_shared_call(g, batch, num_q_heads, n_q, groups, flags, &plan) != KVQ_OK) return 0;
+  return plan.workspace;
+}
+
+int kvq_decode_attn_fp4_shared(const kvq_cache_desc* desc, const void* q, int32_t batch,
+                               int32_t num_q_heads, int32_t n_q, const int32_t* block_tables,
+                               int32_t max_pages_per_seq, const int32_t* context_lens,
+                               const kvq_prefix_groups* groups, float sm_scale, uint32_t flags, float* out,
+                               void* workspace, size_t workspace_bytes, kvq_stream_t stream) {
+  CacheGeom g;
+  int st = check_desc(desc, &g);
+  if (st != KVQ_OK) return st;
+  if (g.fmt != KVQ_FMT_FP4_E2M1) return KVQ_ERR_FORMAT;
+  st = check_cache_ptrs(desc);
+  if (st != KVQ_OK) return st;
+  if (!q || !block_tables || !context_lens || !out || !groups) return KVQ_ERR_NULL;
+  if (!groups->indptr || !groups->members || !groups->prefix_tables || !groups->shared_lens)
+    return KVQ_ERR_NULL;
+  if (batch < 0 || max_pages_per_seq <= 0) return KVQ_ERR_SHAPE;
+  if (!std::isfinite(sm_scale)) return KVQ_ERR_SHAPE;
+  if (batch == 0) return KVQ_OK;
+  SharedPlan plan;
+  st = plan_shared_call(g, batch, num_q_heads, n_q, groups, flags, &plan);
+  if (st != KVQ_OK) return st;
+  if ((int64_t)max_pages_per_seq * g.p < (int64_t)groups->max_suffix_len) return KVQ_ERR_SHAPE;
+  if (!workspace || workspace_bytes < plan.workspace) return KVQ_ERR_WORKSPACE;
+  if ((uintptr_t)workspace & 15u) return KVQ_ERR_WORKSPACE;
+  SharedArgs a;
+  a.base.c = g;
+  a.base.q = (const uint16_t*)q;
+  a.base.batch = batch;
+  a.base.hq = num_q_heads;
+  a.base.n_q = n_q;
+  a.base.group = num_q_heads / g.hkv;
+  a.base.block_tables = block_tables;
+  a.base.max_pages = max_pages_per_seq;
+  a.base.context_lens = context_lens;
+  a.base.qscale = (float)((double)sm_scale * 1.4426950408889634);  // log2(e)
+  a.base.rotate_q = g.rotate && !(flags & KVQ_Q_PREROTATED);
+  a.base.rotate_out = g.rotate && !(flags & KVQ_OUT_ROTATED);
+  a.base.out = out;
+  a.base.workspace = (float*)workspace;
+  a.plan = plan;
+  a.groups = *groups;
+  return hip_status(launch_shared(a, (hipStream_t)stream));
 }
 
 int kvq_decode_attn_fp4(const kvq_cache_desc* desc, const void* q, int32_t batch,

@@ -423,7 +423,9 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
   const int split = (blockIdx.x - u * p.splits + b) % p.splits;
   const int L = p.context_lens[b];
   const int n_tiles = (L + 15) >> 4;
-  const int t_begin = split * p.tiles_per_split;
+  // a shared-prefix suffix scan starts past the prefix (a multiple of 16)
+  const int t0 = p.tok_start ? (p.tok_start[b] >> 4) : 0;
+  const int t_begin = t0 + split * p.tiles_per_split;
   const int t_end = min(n_tiles, t_begin + p.tiles_per_split);
   const int tok_limit = min(L, t_end * 16);
   const int col = lane & 15;
@@ -510,7 +512,7 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
   }
 
   // lanes 0..31 hold row 8t + 4*quad + i, channel 16n + col
-  if (p.splits == 1) {
+  if (p.splits == 1 && !p.keep_partials) {
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -574,7 +576,7 @@ hipError_t launch_nt(const DecodeParams& p, int batch, hipStream_t stream) {
   const dim3 grid((unsigned)((size_t)p.splits * p.hkv * batch));
   hipLaunchKernelGGL((decode_kernel<FMT, NT>), grid, dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.splits == 1) return e;
+  if (e != hipSuccess || p.splits == 1 || p.keep_partials) return e;
   hipLaunchKernelGGL((merge_kernel<8 * NT, 2>), dim3(qblocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
@@ -686,7 +688,7 @@ int plan_decode(const CacheGeom& c, int batch, int hq, int n_q, int max_context_
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (a.plan.kind == kDecodeLatent) return launch_decode512(a, stream);
   if (a.plan.kind == kDecodeMany) return launch_extend(a, stream);
-  DecodeParams p;
+  DecodeParams p{};
   p.kc = a.c.kc;
   p.ks = a.c.ks;
   p.vc = a.c.kv_shared ? a.c.kc : a.c.vc;
@@ -713,6 +715,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   p.splits = a.plan.splits;
   p.tiles_per_split = a.plan.tiles_per_split;
   p.out = a.out;
+  p.tok_start = a.tok_start;
+  p.keep_partials = a.keep_partials;
   const size_t n_o = (size_t)a.batch * a.c.hkv * a.plan.splits * (8 * a.plan.row_tiles) * kD;
   uint8_t* ws = reinterpret_cast<uint8_t*>(a.workspace);
   p.qops = reinterpret_cast<uint32_t*>(ws);

@@ -512,7 +512,7 @@ int plan_decode512(const CacheGeom& c, int batch, int hq, int n_q, int max_conte
 }
 
 hipError_t launch_decode512(const DecodeArgs& a, hipStream_t stream) {
-  DecodeParams p;
+  DecodeParams p{};
   p.kc = a.c.kc;
   p.ks = a.c.ks;
   p.vc = a.c.kv_shared ? a.c.kc : a.c.vc;

@@ -37,6 +37,18 @@ struct DecodeParams {
   float* ws_o;       // [B][hkv][splits][8*NT][kD]
   float* ws_ml;      // [B][hkv][splits][8*NT][2]
   uint32_t* qops;    // [B][hkv][NT][QOpsLayout::kSlots][64 lanes][kDwords]
+  // Shared-prefix decode (null / zero in a plain call).  Suffix level: each
+  // sequence's scan starts at token tok_start[b] (a multiple of 16).  Prefix
+  // level (head_dim 128 many-row kernel): units are prefix groups, group g's
+  // member sequences are grp_seq[grp_ptr[g] .. grp_ptr[g + 1]), its pages are
+  // block_tables[g], member s sees its tokens 0 .. shared_lens[s] - 1, and
+  // the partials are stored per member sequence, rows_seq rows each.
+  const int32_t* tok_start;
+  const int32_t* grp_ptr;
+  const int32_t* grp_seq;
+  const int32_t* shared_lens;
+  int rows_seq;
+  int keep_partials;  // always leave split partials (a later merge combines them)
 };
 
 template <int FMT>

@@ -28,6 +28,7 @@ constexpr int kDX = 128;
 constexpr int kTX = 4;                // FP6 query terms
 constexpr int kWX = 8;                // waves per block
 constexpr int kRowsX = 16 * kWX;      // rows per block
+static_assert(kRowsX == kExtendRowBlock, "row block of the many-row kernel");
 constexpr int kVRowX = 2 * kDX + 32;  // LDS bytes per bf16 token row (padded)
 constexpr int kRingX = 2;             // tile pairs in flight per staging wave
 
@@ -46,11 +47,24 @@ __global__ __launch_bounds__(256) void qprep_ext_kernel(const DecodeParams p) {
 
   float x[2] = {0.0f, 0.0f};
   if (r < p.rows) {
-    const int j = r / p.group;
-    const int hh = r - j * p.group;
-    const uint16_t* src = p.q + (((size_t)b * p.n_q + j) * p.hq + (size_t)kvh * p.group + hh) * kDX + 2 * lane;
-    x[0] = bf16_to_f32(src[0]);
-    x[1] = bf16_to_f32(src[1]);
+    // row r of a sequence, or of a prefix group: member r / rows_seq, its
+    // row r % rows_seq; rows past the group's members stay zero
+    int seq = b, rr = r;
+    bool live = true;
+    if (p.grp_ptr) {
+      const int k = r / p.rows_seq;
+      const int m0 = p.grp_ptr[b];
+      live = k < p.grp_ptr[b + 1] - m0;
+      seq = live ? p.grp_seq[m0 + k] : 0;
+      rr = r - k * p.rows_seq;
+    }
+    if (live) {
+      const int j = rr / p.group;
+      const int hh = rr - j * p.group;
+      const uint16_t* src = p.q + (((size_t)seq * p.n_q + j) * p.hq + (size_t)kvh * p.group + hh) * kDX + 2 * lane;
+      x[0] = bf16_to_f32(src[0]);
+      x[1] = bf16_to_f32(src[1]);
+    }
   }
   if (p.rotate_q) wave_fwht<2>(x, lane, p.norm);
   x[0] = x[0] * p.qscale;
@@ -114,6 +128,10 @@ __device__ __forceinline__ void load_stage(const DecodeParams& p, const int32_t*
   t.sc = __builtin_amdgcn_raw_buffer_load_b8(rs, idx, in_page, 0);
 }
 
+// GRP: prefix level of a shared-prefix decode (units are prefix groups; see
+// DecodeParams); otherwise units are sequences, optionally scanned from
+// p.tok_start[b] on.
+template <bool GRP>
 __global__ __launch_bounds__(512) void extend_kernel(const DecodeParams p) {
   __shared__ __attribute__((aligned(16))) u32x4_t s_k[2][2][64];
   __shared__ uint32_t s_ks[2][2][64];
@@ -132,15 +150,25 @@ __global__ __launch_bounds__(512) void extend_kernel(const DecodeParams p) {
   const int u = (blockIdx.x / p.splits) % units;
   const int rb = blockIdx.x / (p.splits * units);
   const int kvh = u % p.hkv;
-  const int b = u / p.hkv;
-  const int L = p.context_lens[b];
-  const int n_tiles = (L + 15) >> 4;
-  const int t_begin = split * p.tiles_per_split;
-  // the last token any row of this block may see
+  const int b = u / p.hkv;  // sequence, or prefix group (GRP)
   const int r_last_blk = min(p.rows, (rb + 1) * kRowsX) - 1;
-  const int blk_lim = L - p.n_q + r_last_blk / p.group;
-  const int t_end = min(min(n_tiles, t_begin + p.tiles_per_split), (blk_lim >> 4) + 1);
-  const int tok_limit = min(L, t_end * 16);
+  // blk_tok: tokens 0 .. blk_tok - 1 hold every token a row of this block may
+  // see (and are valid cache entries)
+  int blk_tok, t0 = 0, m0 = 0, n_mem = 0, L = 0;
+  if constexpr (GRP) {
+    m0 = p.grp_ptr[b];
+    n_mem = p.grp_ptr[b + 1] - m0;
+    const int k_hi = min(n_mem, r_last_blk / p.rows_seq + 1);
+    blk_tok = 0;
+    for (int k = (rb * kRowsX) / p.rows_seq; k < k_hi; ++k) blk_tok = max(blk_tok, p.shared_lens[p.grp_seq[m0 + k]]);
+  } else {
+    L = p.context_lens[b];
+    blk_tok = min(L, L - p.n_q + r_last_blk / p.group + 1);
+    if (p.tok_start) t0 = p.tok_start[b] >> 4;
+  }
+  const int t_begin = t0 + split * p.tiles_per_split;
+  const int t_end = min(t_begin + p.tiles_per_split, (blk_tok + 15) >> 4);
+  const int tok_limit = min(blk_tok, t_end * 16);
   const int32_t* bt_row = p.block_tables + (size_t)b * p.max_pages;
   const int n_pairs = (t_end > t_begin) ? ((t_end - t_begin + 1) >> 1) : 0;
   const int n_iter = (n_pairs + kRingX - 1) / kRingX;  // pairs padded to a multiple of kRingX
@@ -194,7 +222,24 @@ __global__ __launch_bounds__(512) void extend_kernel(const DecodeParams p) {
     }
   }
   const int row = r0 + col;  // this lane's row (scores and softmax)
-  const int row_lim = (row < p.rows) ? min(tok_limit - 1, L - p.n_q + row / p.group) : -1;
+  int row_lim = -1;
+  if constexpr (GRP) {
+    const int k = row / p.rows_seq;
+    if (row < p.rows && k < n_mem) {
+      const int sq = p.grp_seq[m0 + k];
+      const int j = (row - k * p.rows_seq) / p.group;
+      row_lim = min(tok_limit - 1, min(p.shared_lens[sq] - 1, p.context_lens[sq] - p.n_q + j));
+    }
+  } else {
+    if (row < p.rows) row_lim = min(tok_limit - 1, L - p.n_q + row / p.group);
+  }
+  // last token any row of this wave sees: pairs past it leave the wave's
+  // state unchanged and are skipped (members of a prefix group may share
+  // prefixes of very different lengths)
+  int wave_lim = row_lim;
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) wave_lim = max(wave_lim, __shfl_xor(wave_lim, o, 64));
+  wave_lim = __builtin_amdgcn_readfirstlane(wave_lim);
   float m_run = -INFINITY, l_run = 0.0f;
   f32x4_t O1[8], O2[8];  // rows 0-7 and 8-15 of the wave: hi in MFMA rows 0-7, lo in 8-15
 #pragma unroll
@@ -223,95 +268,97 @@ __global__ __launch_bounds__(512) void extend_kernel(const DecodeParams p) {
         stage(pi + 1, ring[nk]);
         fetch(pi + 1 + kRingX, ring[nk]);
       }
-      // ---- scores of the wave's 16 rows (past the last pair every score is
-      // masked: the softmax state does not change)
-      f32x4_t S[2];
+      if (tile * 16 <= wave_lim) {
+        // ---- scores of the wave's 16 rows (past the last pair every score is
+        // masked: the softmax state does not change)
+        f32x4_t S[2];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const u32x4_t kc = s_k[par][s][lane];
-        const int ksc = (int)s_ks[par][s][lane];
-        const i32x8_t A = {(int)kc[0], (int)kc[1], (int)kc[2], (int)kc[3], 0, 0, 0, 0};
-        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        for (int s = 0; s < 2; ++s) {
+          const u32x4_t kc = s_k[par][s][lane];
+          const int ksc = (int)s_ks[par][s][lane];
+          const i32x8_t A = {(int)kc[0], (int)kc[1], (int)kc[2], (int)kc[3], 0, 0, 0, 0};
+          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int t = 0; t < kTX; ++t)
-          acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, qb[t], acc, 4, 2, 0, ksc, 0, qs[t]);
-        S[s] = acc;
-      }
-      float sc[8];
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = (tile + s) * 16 + 4 * quad + i;
-          sc[4 * s + i] = (tok <= row_lim) ? S[s][i] : -INFINITY;
+          for (int t = 0; t < kTX; ++t)
+            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, qb[t], acc, 4, 2, 0, ksc, 0, qs[t]);
+          S[s] = acc;
         }
-      float mloc = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                         fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-      mloc = quad_max(mloc);
-      const float m_old = m_run;
-      const float m_new = fmaxf(m_old, mloc);
-      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-      m_run = m_new;
-      float psum = 0.0f;
-      uint32_t h[4], l[4];
+        float sc[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float p0 = __builtin_amdgcn_exp2f(sc[2 * e] - m_use);
-        const float p1 = __builtin_amdgcn_exp2f(sc[2 * e + 1] - m_use);
-        psum += p0 + p1;
-        const uint32_t u0 = as_u32(p0), u1 = as_u32(p1);
-        h[e] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
-        l[e] = pack_bf16x2(p0 - as_f32(u0 & 0xFFFF0000u), p1 - as_f32(u1 & 0xFFFF0000u));
-      }
-      // A operands with hi / lo in the MFMA rows: rows 0-7 of the wave
-      // (lanes c < 8 own hi, lanes c >= 8 take lo of row c - 8 from lane
-      // c - 8) and rows 8-15 (lanes c < 8 take hi of row c + 8)
-      uint32_t a1[4], a2[4];
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lr = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)l[e], 0x128, 0xF, 0xF, false);
-        const uint32_t hr = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)h[e], 0x128, 0xF, 0xF, false);
-        a1[e] = hi_col ? h[e] : lr;
-        a2[e] = hi_col ? hr : l[e];
-      }
-      if (__builtin_amdgcn_ballot_w64(m_new != m_old)) {
-        // a row max moved: rescale; O1 lane (q, c) holds rows (4q + i) & 7,
-        // O2 rows 8 + ((4q + i) & 7)
-        const float alpha = __builtin_amdgcn_exp2f(m_old - m_use);
-        l_run *= alpha;
+          for (int i = 0; i < 4; ++i) {
+            const int tok = (tile + s) * 16 + 4 * quad + i;
+            sc[4 * s + i] = (tok <= row_lim) ? S[s][i] : -INFINITY;
+          }
+        float mloc = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                           fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+        mloc = quad_max(mloc);
+        const float m_old = m_run;
+        const float m_new = fmaxf(m_old, mloc);
+        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+        m_run = m_new;
+        float psum = 0.0f;
+        uint32_t h[4], l[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float al1 = __shfl(alpha, (4 * quad + i) & 7, 64);
-          const float al2 = __shfl(alpha, 8 + ((4 * quad + i) & 7), 64);
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(sc[2 * e] - m_use);
+          const float p1 = __builtin_amdgcn_exp2f(sc[2 * e + 1] - m_use);
+          psum += p0 + p1;
+          const uint32_t u0 = as_u32(p0), u1 = as_u32(p1);
+          h[e] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+          l[e] = pack_bf16x2(p0 - as_f32(u0 & 0xFFFF0000u), p1 - as_f32(u1 & 0xFFFF0000u));
+        }
+        // A operands with hi / lo in the MFMA rows: rows 0-7 of the wave
+        // (lanes c < 8 own hi, lanes c >= 8 take lo of row c - 8 from lane
+        // c - 8) and rows 8-15 (lanes c < 8 take hi of row c + 8)
+        uint32_t a1[4], a2[4];
 #pragma unroll
-          for (int n = 0; n < 8; ++n) {
-            O1[n][i] *= al1;
-            O2[n][i] *= al2;
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t lr = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)l[e], 0x128, 0xF, 0xF, false);
+          const uint32_t hr = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)h[e], 0x128, 0xF, 0xF, false);
+          a1[e] = hi_col ? h[e] : lr;
+          a2[e] = hi_col ? hr : l[e];
+        }
+        if (__builtin_amdgcn_ballot_w64(m_new != m_old)) {
+          // a row max moved: rescale; O1 lane (q, c) holds rows (4q + i) & 7,
+          // O2 rows 8 + ((4q + i) & 7)
+          const float alpha = __builtin_amdgcn_exp2f(m_old - m_use);
+          l_run *= alpha;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float al1 = __shfl(alpha, (4 * quad + i) & 7, 64);
+            const float al2 = __shfl(alpha, 8 + ((4 * quad + i) & 7), 64);
+#pragma unroll
+            for (int n = 0; n < 8; ++n) {
+              O1[n][i] *= al1;
+              O2[n][i] *= al2;
+            }
           }
         }
-      }
-      l_run += psum;
-      const bf16x8_t A1 = __builtin_bit_cast(bf16x8_t, u32x4_t{a1[0], a1[1], a1[2], a1[3]});
-      const bf16x8_t A2 = __builtin_bit_cast(bf16x8_t, u32x4_t{a2[0], a2[1], a2[2], a2[3]});
+        l_run += psum;
+        const bf16x8_t A1 = __builtin_bit_cast(bf16x8_t, u32x4_t{a1[0], a1[1], a1[2], a1[3]});
+        const bf16x8_t A2 = __builtin_bit_cast(bf16x8_t, u32x4_t{a2[0], a2[1], a2[2], a2[3]});
 
-      // ---- PV: B operands read transposed from the LDS V tiles
-      const int rr = col >> 2;
-      const int c4 = (col & 3) * 4;
-      typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
-      auto read_b = [&](int n) {
-        lds_bf16x4* p0 = (lds_bf16x4*)((__attribute__((address_space(3))) uint8_t*)&s_v[par][0][4 * quad + rr][2 * (16 * n + c4)]);
-        lds_bf16x4* p1 = (lds_bf16x4*)((__attribute__((address_space(3))) uint8_t*)&s_v[par][1][4 * quad + rr][2 * (16 * n + c4)]);
-        const u32x2_t w0 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p0));
-        const u32x2_t w1 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p1));
-        return __builtin_bit_cast(bf16x8_t, u32x4_t{w0[0], w0[1], w1[0], w1[1]});
-      };
-      bf16x8_t B0 = read_b(0);
+        // ---- PV: B operands read transposed from the LDS V tiles
+        const int rr = col >> 2;
+        const int c4 = (col & 3) * 4;
+        typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+        auto read_b = [&](int n) {
+          lds_bf16x4* p0 = (lds_bf16x4*)((__attribute__((address_space(3))) uint8_t*)&s_v[par][0][4 * quad + rr][2 * (16 * n + c4)]);
+          lds_bf16x4* p1 = (lds_bf16x4*)((__attribute__((address_space(3))) uint8_t*)&s_v[par][1][4 * quad + rr][2 * (16 * n + c4)]);
+          const u32x2_t w0 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p0));
+          const u32x2_t w1 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p1));
+          return __builtin_bit_cast(bf16x8_t, u32x4_t{w0[0], w0[1], w1[0], w1[1]});
+        };
+        bf16x8_t B0 = read_b(0);
 #pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const bf16x8_t C0 = (n + 1 < 8) ? read_b(n + 1) : B0;
-        O1[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B0, O1[n], 0, 0, 0);
-        O2[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, B0, O2[n], 0, 0, 0);
-        B0 = C0;
+        for (int n = 0; n < 8; ++n) {
+          const bf16x8_t C0 = (n + 1 < 8) ? read_b(n + 1) : B0;
+          O1[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B0, O1[n], 0, 0, 0);
+          O2[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, B0, O2[n], 0, 0, 0);
+          B0 = C0;
+        }
       }
       __syncthreads();
     }
@@ -327,19 +374,49 @@ __global__ __launch_bounds__(512) void extend_kernel(const DecodeParams p) {
       O1[n][i] = add_half_swap(O1[n][i]);
       O2[n][i] = add_half_swap(O2[n][i]);
     }
-  const size_t base = ((size_t)u * p.splits + split) * p.rows_pad + r0;
-  if (lane < 32) {
-#pragma unroll
-    for (int n = 0; n < 8; ++n)
+  if constexpr (GRP) {
+    // per member sequence: [B][hkv][splits][rows_seq] rows; rows past the
+    // group's members are not stored
+    auto dest = [&](int r) -> long long {
+      const int k = r / p.rows_seq;
+      if (r >= p.rows || k >= n_mem) return -1;
+      const int sq = p.grp_seq[m0 + k];
+      return (((long long)sq * p.hkv + kvh) * p.splits + split) * p.rows_seq + (r - k * p.rows_seq);
+    };
+    if (lane < 32) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p.ws_o[(base + 4 * quad + i) * kDX + 16 * n + col] = O1[n][i];
-        p.ws_o[(base + 8 + 4 * quad + i) * kDX + 16 * n + col] = O2[n][i];
+        const long long d1 = dest(r0 + 4 * quad + i);
+        const long long d2 = dest(r0 + 8 + 4 * quad + i);
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+          if (d1 >= 0) p.ws_o[d1 * kDX + 16 * n + col] = O1[n][i];
+          if (d2 >= 0) p.ws_o[d2 * kDX + 16 * n + col] = O2[n][i];
+        }
       }
-  }
-  if (lane < 16) {
-    p.ws_ml[(base + lane) * 2 + 0] = m_run;
-    p.ws_ml[(base + lane) * 2 + 1] = lrow;
+    }
+    if (lane < 16) {
+      const long long d = dest(r0 + lane);
+      if (d >= 0) {
+        p.ws_ml[d * 2 + 0] = m_run;
+        p.ws_ml[d * 2 + 1] = lrow;
+      }
+    }
+  } else {
+    const size_t base = ((size_t)u * p.splits + split) * p.rows_pad + r0;
+    if (lane < 32) {
+#pragma unroll
+      for (int n = 0; n < 8; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          p.ws_o[(base + 4 * quad + i) * kDX + 16 * n + col] = O1[n][i];
+          p.ws_o[(base + 8 + 4 * quad + i) * kDX + 16 * n + col] = O2[n][i];
+        }
+    }
+    if (lane < 16) {
+      p.ws_ml[(base + lane) * 2 + 0] = m_run;
+      p.ws_ml[(base + lane) * 2 + 1] = lrow;
+    }
   }
 }
 
@@ -362,7 +439,7 @@ int resident_blocks_x() {
   }
   int cus = 0, blocks = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, extend_kernel, 64 * kWX, 0) != hipSuccess) {
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, extend_kernel<false>, 64 * kWX, 0) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
@@ -375,9 +452,13 @@ int resident_blocks_x() {
 
 int plan_extend(const CacheGeom& c, int batch, int hq, int n_q, int max_context_len, uint32_t flags,
                 DecodePlan* plan) {
+  return plan_extend_rows(c, batch, (long long)(hq / c.hkv) * n_q, max_context_len, flags, plan);
+}
+
+int plan_extend_rows(const CacheGeom& c, int batch, long long rows, int max_context_len, uint32_t flags,
+                     DecodePlan* plan) {
   if (c.d != kDX || c.fmt != KVQ_FMT_FP4_E2M1) return KVQ_ERR_UNSUPPORTED;
-  const long long rows = (long long)(hq / c.hkv) * n_q;
-  if (rows > kMaxRowsX) return KVQ_ERR_UNSUPPORTED;
+  if (rows < 1 || rows > kMaxRowsX) return KVQ_ERR_UNSUPPORTED;
   const int row_blocks = (int)((rows + kRowsX - 1) / kRowsX);
   const int n_tiles = (max_context_len + 15) / 16;
   int splits = (int)((flags & KVQ_SPLITS_MASK) >> KVQ_SPLITS_SHIFT);
@@ -411,7 +492,7 @@ int plan_extend(const CacheGeom& c, int batch, int hq, int n_q, int max_context_
 }
 
 hipError_t launch_extend(const DecodeArgs& a, hipStream_t stream) {
-  DecodeParams p;
+  DecodeParams p{};
   p.kc = a.c.kc;
   p.ks = a.c.ks;
   p.vc = a.c.kv_shared ? a.c.kc : a.c.vc;
@@ -440,8 +521,17 @@ hipError_t launch_extend(const DecodeArgs& a, hipStream_t stream) {
   p.splits = a.plan.splits;
   p.tiles_per_split = a.plan.tiles_per_split;
   p.out = a.out;
+  p.tok_start = a.tok_start;
+  p.grp_ptr = a.grp_ptr;
+  p.grp_seq = a.grp_seq;
+  p.shared_lens = a.shared_lens;
+  p.rows_seq = a.rows_seq;
+  p.keep_partials = a.keep_partials;
+  const bool grp = a.grp_ptr != nullptr;
   const size_t units = (size_t)a.batch * a.c.hkv;
-  const size_t n_o = units * a.plan.splits * (size_t)p.rows_pad * kDX;
+  // partial rows: per unit and padded, or (prefix level) per member sequence
+  const size_t part_rows = grp ? (size_t)a.grp_seqs * a.c.hkv * a.rows_seq : units * p.rows_pad;
+  const size_t n_o = part_rows * a.plan.splits * kDX;
   uint8_t* ws = reinterpret_cast<uint8_t*>(a.workspace);
   p.qops = reinterpret_cast<uint32_t*>(ws);
   p.ws_o = reinterpret_cast<float*>(ws + a.plan.qops_bytes);
@@ -451,9 +541,12 @@ hipError_t launch_extend(const DecodeArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((size_t)p.splits * units * a.plan.row_tiles));
-  hipLaunchKernelGGL(extend_kernel, grid, dim3(64 * kWX), 0, stream, p);
+  if (grp)
+    hipLaunchKernelGGL(extend_kernel<true>, grid, dim3(64 * kWX), 0, stream, p);
+  else
+    hipLaunchKernelGGL(extend_kernel<false>, grid, dim3(64 * kWX), 0, stream, p);
   e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || a.keep_partials) return e;
   hipLaunchKernelGGL((merge_kernel<0, 2>), dim3(qblocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

@@ -70,6 +70,14 @@ struct DecodeArgs {
   int rotate_out;    // rotate the output back inside the kernel
   float* out;
   float* workspace;
+  // shared-prefix decode (kvq_shared.hip); null / zero in a plain call
+  const int32_t* tok_start = nullptr;    // suffix level: first token scanned per sequence
+  const int32_t* grp_ptr = nullptr;      // prefix level: units are prefix groups
+  const int32_t* grp_seq = nullptr;
+  const int32_t* shared_lens = nullptr;
+  int rows_seq = 0;                      // prefix level: rows per member sequence
+  int grp_seqs = 0;                      // prefix level: sequences (partials are stored per sequence)
+  int keep_partials = 0;                 // leave split partials, launch no merge
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
@@ -82,7 +90,28 @@ constexpr int kDecodeLatent = 2;  // head_dim 512 (kvq_decode512.hip)
 // many rows per KV head (extend / prefill chunks): kvq_extend.hip
 int plan_extend(const CacheGeom& c, int batch, int hq, int n_q, int max_context_len, uint32_t flags,
                 DecodePlan* plan);
+// the same plan for `units` (sequence or prefix group) x num_kv_heads units of
+// `rows` rows each
+int plan_extend_rows(const CacheGeom& c, int units, long long rows, int max_context_len, uint32_t flags,
+                     DecodePlan* plan);
 hipError_t launch_extend(const DecodeArgs& a, hipStream_t stream);
+constexpr int kExtendRowBlock = 128;   // rows per many-row block (padding unit of its rows)
+
+// shared-prefix decode, head_dim 128 FP4: kvq_shared.hip
+struct SharedPlan {
+  DecodePlan prefix;     // many-row kernel over the prefix groups
+  DecodePlan suffix;     // the row count's decode kernel over each sequence's suffix
+  size_t suffix_offset;  // workspace bytes before the suffix level's part
+  size_t workspace;      // bytes
+};
+int plan_shared(const CacheGeom& c, int batch, int hq, int n_q, const kvq_prefix_groups& g, uint32_t flags,
+                SharedPlan* plan);
+struct SharedArgs {
+  DecodeArgs base;  // the call's arguments (plan unused)
+  SharedPlan plan;
+  kvq_prefix_groups groups;
+};
+hipError_t launch_shared(const SharedArgs& a, hipStream_t stream);
 
 // head_dim 512 (latent width): planned and launched by kvq_decode512.hip
 int plan_decode512(const CacheGeom& c, int batch, int hq, int n_q, int max_context_len, uint32_t flags,

@@ -187,6 +187,72 @@ int kvq_decode_attn_fp8(const kvq_cache_desc *desc, const void *q,
                         void *workspace, size_t workspace_bytes,
                         kvq_stream_t stream);
 
+/* Prefix groups of a shared-prefix decode (kvq_decode_attn_fp4_shared).
+ * Agent traffic re-sends long prefixes, so many sequences of a batch start
+ * with the same cached pages ("Agentic serving: workload and setup": long
+ * shared prefixes, a high prefix-cache hit rate).  A group names such a
+ * prefix and the sequences that start with it:
+ *   num_groups       G >= 1
+ *   max_group_size   host-side bound: indptr[g + 1] - indptr[g] <= it for
+ *                    every g (sizes the grid)
+ *   indptr           int32 [G + 1] (device), non-decreasing, indptr[0] = 0
+ *   members          int32 [indptr[G]] (device): group g's sequences are
+ *                    members[indptr[g]] .. members[indptr[g + 1] - 1];
+ *                    listing them by decreasing shared_lens is fastest
+ *   prefix_tables    int32 [G][max_prefix_pages] (device): the physical pages
+ *                    of each group's prefix, in token order
+ *   max_prefix_pages row length of prefix_tables, >= 1
+ *   shared_lens      int32 [batch] (device): tokens 0 .. shared_lens[b] - 1
+ *                    of sequence b are tokens 0 .. shared_lens[b] - 1 of its
+ *                    group's prefix; a multiple of 16 (whole pages of any
+ *                    page size are), at most context_lens[b] and at most
+ *                    max_prefix_pages * page_size.  A sequence with
+ *                    shared_lens[b] > 0 is a member of exactly one group; one
+ *                    with 0 may be a member of none
+ *   max_suffix_len   host-side bound: context_lens[b] - shared_lens[b] <=
+ *                    it for every b (sizes the grid), >= 0
+ * Violations that only the device can see are undefined behaviour, as for
+ * the other contracts above. */
+typedef struct kvq_prefix_groups {
+  int32_t num_groups;
+  int32_t max_group_size;
+  const int32_t *indptr;
+  const int32_t *members;
+  const int32_t *prefix_tables;
+  int32_t max_prefix_pages;
+  const int32_t *shared_lens;
+  int32_t max_suffix_len;
+} kvq_prefix_groups;
+/* Workspace bytes of a shared-prefix decode with these sizes (0 when they
+ * are invalid or unsupported); the same rules as kvq_decode_workspace_bytes.
+ * Only the host-side fields of `groups` are read. */
+size_t kvq_decode_shared_workspace_bytes(const kvq_cache_desc *desc,
+                                         int32_t batch, int32_t num_q_heads,
+                                         int32_t n_q,
+                                         const kvq_prefix_groups *groups,
+                                         uint32_t flags);
+/* Shared-prefix (cascade) decode over an FP4 cache, head_dim 128: the same
+ * result as kvq_decode_attn_fp4 (up to fp32 rounding) when block_tables[b]
+ * starts with the pages of its group's prefix, but each group's prefix pages
+ * are read once for the query rows of all its members, and each sequence's
+ * own pages (tokens shared_lens[b] .. context_lens[b] - 1) once for its rows.
+ *   block_tables   int32 [batch][max_pages_per_seq]; entries of tokens below
+ *                  shared_lens[b] are not read
+ *   groups         see kvq_prefix_groups
+ *   other arguments as for kvq_decode_attn_fp4; rows per KV head (n_q *
+ *   num_q_heads / num_kv_heads) and rows per group (that times
+ *   max_group_size) are at most 65536; KVQ_SPLITS(n) forces the split count
+ *   of both levels (at most 32 each)
+ * Returns KVQ_OK, or KVQ_ERR_NULL / SHAPE / FORMAT / UNSUPPORTED (head_dim
+ * other than 128) / WORKSPACE / HIP. */
+int kvq_decode_attn_fp4_shared(const kvq_cache_desc *desc, const void *q,
+                               int32_t batch, int32_t num_q_heads, int32_t n_q,
+                               const int32_t *block_tables,
+                               int32_t max_pages_per_seq,
+                               const int32_t *context_lens,
+                               const kvq_prefix_groups *groups, float sm_scale,
+                               uint32_t flags, float *out, void *workspace,
+                               size_t workspace_bytes, kvq_stream_t stream);
 /* Dequantise n slots (for tests and export): fp32 [n][num_kv_heads][head_dim]
  * of code value * 2^(scale - 127), in the stored (rotated) basis.  v_out is
  * ignored (may be NULL) when kv_shared.  Slots must be in range.

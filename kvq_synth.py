@@ -136,9 +136,13 @@ class PagePlan:
         return int(self.block_tables.shape[1])
 
 
-def page_plan(wl: Workload) -> PagePlan:
+def page_plan(wl: Workload, lens: Optional[List[int]] = None,
+              shared_pages: Optional[List[int]] = None) -> PagePlan:
+    """The workload's page plan; ``lens`` and ``shared_pages`` (whole pages
+    sequence b takes from prefix b mod n_prefixes) override the drawn context
+    lengths and the shared fraction, for edge cases."""
     P = wl.page_size
-    L = context_lens(wl)
+    L = context_lens(wl) if lens is None else np.asarray(lens, dtype=np.int32)
     n_pages = [(int(l) + P - 1) // P for l in L]
     prefix_of = [-1] * wl.batch
     n_shared = [0] * wl.batch
@@ -147,7 +151,10 @@ def page_plan(wl: Workload) -> PagePlan:
         for b in range(wl.batch):
             p = b % wl.n_prefixes
             prefix_of[b] = p
-            n_shared[b] = int(math.floor(wl.shared_frac * n_pages[b]))
+            if shared_pages is None:
+                n_shared[b] = int(math.floor(wl.shared_frac * n_pages[b]))
+            else:
+                n_shared[b] = min(int(shared_pages[b]), int(L[b]) // P)
             prefix_need[p] = max(prefix_need[p], n_shared[b])
     total = sum(prefix_need) + sum(n_pages[b] - n_shared[b] for b in range(wl.batch))
     if wl.permute_pages:

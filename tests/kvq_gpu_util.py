@@ -76,6 +76,25 @@ class Filled:
         return fn(self.cache, q, self.block_tables, self.context_lens, self.max_context,
                   sm_scale=sm_scale, flags=flags)
 
+    def prefix_groups(self, shared_lens=None) -> kvq.PrefixGroups:
+        """The plan's shared prefixes as prefix groups: sequence b shares its
+        whole shared pages unless shared_lens says otherwise; a sequence that
+        shares nothing is in no group."""
+        plan, P = self.plan, self.wl.page_size
+        if shared_lens is None:
+            shared_lens = [plan.n_shared_pages[b] * P for b in range(self.wl.batch)]
+        n_groups = max(1, self.wl.n_prefixes)
+        groups = [[b for b in range(self.wl.batch) if plan.prefix_of[b] == g and shared_lens[b] > 0]
+                  for g in range(n_groups)]
+        pages = [plan.prefix_pages[g] if g < len(plan.prefix_pages) else [] for g in range(n_groups)]
+        return kvq.PrefixGroups.from_lists(groups, pages, [int(x) for x in shared_lens],
+                                           [int(x) for x in plan.context_lens])
+
+    def decode_shared(self, q: torch.Tensor, groups: Optional[kvq.PrefixGroups] = None, flags: int = 0):
+        groups = self.prefix_groups() if groups is None else groups
+        return kvq.decode_attn_fp4_shared(self.cache, q, self.block_tables, self.context_lens, groups,
+                                          flags=flags)
+
     def seq_slots(self, b: int) -> np.ndarray:
         L = int(self.plan.context_lens[b])
         t = np.arange(L)

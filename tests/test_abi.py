@@ -165,3 +165,65 @@ def test_binding_has_no_oracle_dependency():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(root, f)).read()
                 assert "oracle" not in text.lower().replace("no cpu fallback", ""), f
+
+
+def _groups(G=2, gmax=4, ptrs=True, maxpp=64, suffix=256):
+    x = ctypes.c_void_p(0x6000) if ptrs else None
+    return kvq.PrefixGroupsDesc(G, gmax, x, x, x, maxpp, x, suffix)
+
+
+def _shared(desc=None, q=0x10, B=8, hq=64, n_q=3, bt=0x20, maxp=128, cl=0x30, groups=None, sm=0.1, flags=0,
+            out=0x40, ws=0x50, wsb=1 << 34):
+    desc = _desc() if desc is None else desc
+    g = _groups() if groups is None else groups
+    return kvq.library().kvq_decode_attn_fp4_shared(ctypes.byref(desc), q, B, hq, n_q, bt, maxp, cl,
+                                                    ctypes.byref(g), sm, flags, out, ws, wsb, None)
+
+
+def test_shared_workspace_bytes():
+    L = kvq.library()
+    d = _desc()
+    ws = lambda desc=d, B=8, hq=64, n_q=3, g=None, flags=0: L.kvq_decode_shared_workspace_bytes(
+        ctypes.byref(desc), B, hq, n_q, ctypes.byref(g if g is not None else _groups()), flags)
+    need = ws()
+    assert need > 0
+    # the prefix level's operands alone need one 16-row operand block per 16 gathered rows
+    assert need > 2 * 8 * (4 * 24 + 127) // 128 * 128 // 16 * 4 * 64 * 8 * 4
+    assert ws(desc=_desc(fmt=2)) == 0                     # FP4 only
+    assert ws(desc=_desc(d=512, hkv=1, p=64, shared=1), hq=64, n_q=1) == 0
+    assert ws(g=_groups(G=0)) == 0
+    assert ws(g=_groups(gmax=0)) == 0
+    assert ws(g=_groups(maxpp=0)) == 0
+    assert ws(g=_groups(suffix=-1)) == 0
+    assert ws(g=_groups(gmax=2731)) == 0                  # 2731 x 24 rows > 65536
+    assert ws(g=_groups(gmax=2730)) > 0
+    assert ws(B=0) == 0
+    assert ws(g=_groups(suffix=0)) > 0                    # every token shared
+    # a forced split count applies to both levels, at most 32 each
+    assert ws(flags=kvq.splits_flag(40)) == ws(flags=kvq.splits_flag(32))
+
+
+def test_shared_argument_errors():
+    assert _shared(q=None) == -1
+    assert _shared(bt=None) == -1
+    assert _shared(cl=None) == -1
+    assert _shared(out=None) == -1
+    assert _shared(desc=_desc(ptrs=False)) == -1
+    assert _shared(groups=_groups(ptrs=False)) == -1
+    assert kvq.library().kvq_decode_attn_fp4_shared(ctypes.byref(_desc()), 0x10, 8, 64, 3, 0x20, 128, 0x30,
+                                                    None, 0.1, 0, 0x40, 0x50, 1 << 34, None) == -1
+    assert _shared(desc=_desc(fmt=2)) == -3
+    assert _shared(desc=_desc(d=64)) == -4
+    assert _shared(hq=12) == -2
+    assert _shared(n_q=0) == -2
+    assert _shared(sm=float("nan")) == -2
+    assert _shared(flags=0x8) == -2
+    assert _shared(groups=_groups(G=0)) == -2
+    assert _shared(groups=_groups(suffix=128 * 16 + 1)) == -2   # suffix longer than a block table row
+    assert _shared(groups=_groups(gmax=2731)) == -4
+    assert _shared(ws=None, wsb=0) == -5
+    L = kvq.library()
+    need = L.kvq_decode_shared_workspace_bytes(ctypes.byref(_desc()), 8, 64, 3, ctypes.byref(_groups()), 0)
+    assert _shared(wsb=need - 1) == -5
+    assert _shared(ws=0x58, wsb=need) == -5
+    assert _shared(B=0) == 0                     # empty batch: nothing enqueued

@@ -6,7 +6,8 @@ compared element by element (max |err| <= 2e-3, relative L2 <= 1e-3).
   b32_l32k       batch 32, 8 KV / 64 Q heads, d128, context 32768, page 16
                  (FP4 cache and the FP8 comparator)
   mtp_mixed_b32  batch 32, contexts 4K-128K log-uniform, 92% of pages shared
-                 from 4 prefixes, 3 MTP verify positions (24 rows per KV head)
+                 from 4 prefixes, 3 MTP verify positions (24 rows per KV head);
+                 plain and shared-prefix decode
   mla_b16_l128k  batch 16, one latent head of width 512 (K = V), 64 absorbed
                  query heads, context 131072, page 64
   extend         batch 4, 8 KV / 64 Q heads, context 32768 whose last 64
@@ -34,11 +35,11 @@ def _pairs(wl, n, seed):
     return sorted(pairs)
 
 
-def _check(name, fmt, n_pairs, seed):
+def _check(name, fmt, n_pairs, seed, shared=False):
     wl = syn.WORKLOADS[name]
     f = Filled(wl, fmt, gen_device="cuda")
     q = syn.queries(wl, "cuda")
-    out = f.decode(q).cpu().numpy()
+    out = (f.decode_shared(q) if shared else f.decode(q)).cpu().numpy()
     torch.cuda.synchronize()
     qh = syn.bf16_bits(q)
     g = wl.group
@@ -51,7 +52,8 @@ def _check(name, fmt, n_pairs, seed):
         worst = (max(worst[0], r[0]), max(worst[1], r[1]))
     # every output is finite, including the rows not sampled
     assert np.isfinite(out).all()
-    print("%s %s: %d pairs, worst max_abs %.3g rel_l2 %.3g" % (name, fmt, len(pairs), worst[0], worst[1]))
+    print("%s %s%s: %d pairs, worst max_abs %.3g rel_l2 %.3g" % (name, fmt, " shared-prefix" if shared else "",
+                                                                len(pairs), worst[0], worst[1]))
 
 
 @pytest.mark.parametrize("fmt", ["fp4", "fp8"])
@@ -61,6 +63,12 @@ def test_fullsize_b32_l32k_sampled(gpu, fmt):
 
 def test_fullsize_mtp_mixed_b32_sampled(gpu):
     _check("mtp_mixed_b32", "fp4", 16, 2)
+
+
+def test_fullsize_mtp_mixed_b32_shared_prefix_sampled(gpu):
+    """The same agentic mix through the shared-prefix entry point (each
+    prefix group's pages read once for all its members)."""
+    _check("mtp_mixed_b32", "fp4", 16, 5, shared=True)
 
 
 def test_fullsize_mla_b16_l128k_sampled(gpu):

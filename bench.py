@@ -310,9 +310,10 @@ def main():
         del src, dst
 
     # ---------------- agentic mix: shared prefixes, MTP verify positions
-    mix = None
+    mix = fork = None
     if not args.no_mix:
         mix = bench_mix(kvq, syn, dev, stream, max(args.steps // 2, 20), R)
+        fork = bench_mix(kvq, syn, dev, stream, max(args.steps // 2, 20), R, name="fork_b32_l32k")
 
     # ---------------- extend chunk (many query rows per KV head, MFMA-bound)
     ext = None
@@ -363,6 +364,7 @@ def main():
         "fp8_comparator": fp8,
         "append_bulk": append_bulk,
         "agentic_mix": mix,
+        "fork_prefix": fork,
         "extend_chunk": ext,
         "latent_512": mla,
         "cpu_baseline": cpu,
@@ -376,9 +378,12 @@ PEAK_BF16 = 2500.0
 
 
 def bench_mix(kvq, syn, dev, stream, steps, R, name="mtp_mixed_b32"):
-    """Decode over the agentic mix (batch 32, contexts 4K-128K, 92% of each
-    sequence's pages shared from 4 prefixes, 3 MTP verify positions):
-    mean HIP-event time of one FP4 decode call over cache replicas.
+    """Decode over a batch with shared prefixes and 3 MTP verify positions:
+    the agentic mix (mtp_mixed_b32: contexts 4K-128K, 92% of each sequence's
+    pages shared from 4 prefixes, so members share prefixes of different
+    lengths) or a fork (fork_b32_l32k: 32 sequences of 32K tokens whose first
+    30K tokens are one prefix).  Mean HIP-event time of one FP4 decode call
+    over cache replicas, plain and through the shared-prefix entry point.
     Reports logical KV bytes (every sequence's pages, shared ones counted
     per sequence) and unique bytes (each physical page once)."""
     import numpy as np
@@ -404,9 +409,29 @@ def bench_mix(kvq, syn, dev, stream, steps, R, name="mtp_mixed_b32"):
         b.record(stream)
     torch.cuda.synchronize()
     t = statistics.fmean([a.elapsed_time(b) for a, b in es])
+
+    # the same call through the shared-prefix entry point: each prefix's pages
+    # read once for all the sequences that share it
+    P = wl.page_size
+    shared = [plan.n_shared_pages[b] * P for b in range(B)]
+    groups = kvq.PrefixGroups.from_lists(
+        [[b for b in range(B) if plan.prefix_of[b] == g and shared[b] > 0] for g in range(wl.n_prefixes)],
+        plan.prefix_pages, shared, [int(x) for x in plan.context_lens], device=dev)
+    ws2 = torch.empty(kvq.decode_shared_workspace_bytes(c, B, HQ, NQ, groups), dtype=torch.uint8, device=dev)
+    out2 = torch.empty_like(out)
+    for i in range(5):
+        kvq.decode_attn_fp4_shared(cs[i % R], q, bt, cl, groups, out=out2, workspace=ws2, stream=stream)
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(es):
+        a.record(stream)
+        kvq.decode_attn_fp4_shared(cs[i % R], q, bt, cl, groups, out=out2, workspace=ws2, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t2 = statistics.fmean([a.elapsed_time(b) for a, b in es])
+    max_diff = float((out2 - out).abs().max())
+
     per_tok = (D // 2 + D // 32) * 2 * wl.num_kv_heads
     logical = int(plan.context_lens.astype(np.int64).sum()) * per_tok
-    P = wl.page_size
     used = set()
     for b in range(B):
         n = (int(plan.context_lens[b]) + P - 1) // P
@@ -420,6 +445,14 @@ def bench_mix(kvq, syn, dev, stream, steps, R, name="mtp_mixed_b32"):
         "unique_kv_bytes": unique,
         "logical_gbs": round(logical / (t * 1e-3) / 1e9, 1),
         "unique_gbs": round(unique / (t * 1e-3) / 1e9, 1),
+        "shared_prefix": {
+            "decode_ms_events_mean": round(t2, 4),
+            "speedup_vs_plain": round(t / t2, 3),
+            "logical_gbs": round(logical / (t2 * 1e-3) / 1e9, 1),
+            "unique_gbs": round(unique / (t2 * 1e-3) / 1e9, 1),
+            "max_abs_diff_vs_plain": max_diff,
+            "note": "kvq_decode_attn_fp4_shared, one group per prefix (%d)" % wl.n_prefixes,
+        },
     }
 
 

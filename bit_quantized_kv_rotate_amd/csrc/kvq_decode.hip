@@ -432,6 +432,16 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
   const int quad = lane >> 4;
   const int32_t* bt_row = p.block_tables + (size_t)b * p.max_pages;
   const bool has_work = t_end > t_begin;
+  if (!has_work && (p.splits > 1 || p.keep_partials)) {
+    // an empty split (a short sequence of a ragged batch): (m, l) = (-inf, 0)
+    // only; a merge never reads the O of a split with zero weight
+    if (lane < ROWS) {
+      const size_t base = (((size_t)b * p.hkv + kvh) * p.splits + split) * ROWS;
+      p.ws_ml[(base + lane) * 2 + 0] = -INFINITY;
+      p.ws_ml[(base + lane) * 2 + 1] = 0.0f;
+    }
+    return;
+  }
   const int n_pairs = has_work ? ((t_end - t_begin + 1) >> 1) : 0;
   constexpr int kRing = Ring<NT>::kN;
   const int n_iter = (n_pairs + kRing - 1) / kRing;

@@ -176,7 +176,8 @@ __device__ __forceinline__ void wave_fwht(float (&x)[C], int lane, float c) {
 constexpr int kMaxSplits = 64;
 
 // Combine the split partials of each query row: weights 2^(m_s - M),
-// normalise by the combined sum, rotate back, store.  One wave per row
+// normalise by the combined sum, rotate back, store.  A split of weight zero
+// (an empty one, which writes only its (m, l)) is not read.  One wave per row
 // (four per block, ROWS padded rows per (sequence, KV head), or p.rows_pad
 // when ROWS is 0); lane s < S
 // holds split s's (m, l), lane l accumulates channels C l .. C l + C - 1 of
@@ -215,6 +216,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeParams p) {
 #pragma unroll 4
   for (int sp = 0; sp < S; ++sp) {
     const float w = as_f32((uint32_t)__builtin_amdgcn_readlane((int)as_u32(ws), sp));
+    if (w == 0.0f) continue;  // an empty split stores no O
     const float* src = po + (size_t)sp * ROWS * D;
 #pragma unroll
     for (int i = 0; i < C; i += 2) {

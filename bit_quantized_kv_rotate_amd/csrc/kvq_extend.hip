@@ -142,13 +142,15 @@ __global__ __launch_bounds__(512) void extend_kernel(const DecodeParams p) {
   const int col = lane & 15;
   const int quad = lane >> 4;
   const bool hi_col = col < 8;
-  // 1-D grid: split fastest, then (sequence, KV head), then row block; the
-  // row blocks of one (unit, split) share its K/V tiles, and with a unit
-  // count divisible by 8 they land on one XCD (one L2)
+  // 1-D grid: split fastest, then (sequence or group, KV head), then row
+  // block.  Blocks go to the XCDs round-robin; when contexts are ragged only
+  // the low splits of a short unit have work, so the split index is rotated
+  // by (unit, row block): otherwise a split count divisible by 8 would put
+  // all of that work on a few XCDs
   const int units = p.hkv * p.batch;
-  const int split = blockIdx.x % p.splits;
   const int u = (blockIdx.x / p.splits) % units;
   const int rb = blockIdx.x / (p.splits * units);
+  const int split = (int)((blockIdx.x % p.splits + (unsigned)u + (unsigned)rb * units) % p.splits);
   const int kvh = u % p.hkv;
   const int b = u / p.hkv;  // sequence, or prefix group (GRP)
   const int r_last_blk = min(p.rows, (rb + 1) * kRowsX) - 1;
@@ -170,7 +172,31 @@ __global__ __launch_bounds__(512) void extend_kernel(const DecodeParams p) {
   const int t_end = min(t_begin + p.tiles_per_split, (blk_tok + 15) >> 4);
   const int tok_limit = min(blk_tok, t_end * 16);
   const int32_t* bt_row = p.block_tables + (size_t)b * p.max_pages;
-  const int n_pairs = (t_end > t_begin) ? ((t_end - t_begin + 1) >> 1) : 0;
+  // where row r of this unit stores its split partial: per unit, padded
+  // rows included, or (GRP) per member sequence (-1: no member)
+  auto part_row = [&](int r) -> long long {
+    if constexpr (GRP) {
+      const int k = r / p.rows_seq;
+      if (r >= p.rows || k >= n_mem) return -1;
+      const int sq = p.grp_seq[m0 + k];
+      return (((long long)sq * p.hkv + kvh) * p.splits + split) * p.rows_seq + (r - k * p.rows_seq);
+    } else {
+      return ((long long)u * p.splits + split) * p.rows_pad + r;
+    }
+  };
+  if (t_end <= t_begin) {
+    // an empty split: (m, l) = (-inf, 0) for the block's rows; a merge never
+    // reads the O of a split with zero weight
+    if (threadIdx.x < kRowsX) {
+      const long long d = part_row(rb * kRowsX + (int)threadIdx.x);
+      if (d >= 0) {
+        p.ws_ml[d * 2 + 0] = -INFINITY;
+        p.ws_ml[d * 2 + 1] = 0.0f;
+      }
+    }
+    return;
+  }
+  const int n_pairs = (t_end - t_begin + 1) >> 1;
   const int n_iter = (n_pairs + kRingX - 1) / kRingX;  // pairs padded to a multiple of kRingX
 
   // staging role: waves 0..3 stage K tile 0, K tile 1, V tile 0, V tile 1
@@ -201,7 +227,7 @@ __global__ __launch_bounds__(512) void extend_kernel(const DecodeParams p) {
   };
 
   Stage ring[kRingX];
-  if (stager && n_pairs > 0) {
+  if (stager) {
 #pragma unroll
     for (int k = 0; k < kRingX; ++k) fetch(k, ring[k]);
   }
@@ -248,7 +274,7 @@ __global__ __launch_bounds__(512) void extend_kernel(const DecodeParams p) {
     O2[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  if (stager && n_pairs > 0) {
+  if (stager) {
     stage(0, ring[0]);
     fetch(kRingX, ring[0]);
   }
@@ -374,48 +400,23 @@ __global__ __launch_bounds__(512) void extend_kernel(const DecodeParams p) {
       O1[n][i] = add_half_swap(O1[n][i]);
       O2[n][i] = add_half_swap(O2[n][i]);
     }
-  if constexpr (GRP) {
-    // per member sequence: [B][hkv][splits][rows_seq] rows; rows past the
-    // group's members are not stored
-    auto dest = [&](int r) -> long long {
-      const int k = r / p.rows_seq;
-      if (r >= p.rows || k >= n_mem) return -1;
-      const int sq = p.grp_seq[m0 + k];
-      return (((long long)sq * p.hkv + kvh) * p.splits + split) * p.rows_seq + (r - k * p.rows_seq);
-    };
-    if (lane < 32) {
+  if (lane < 32) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const long long d1 = dest(r0 + 4 * quad + i);
-        const long long d2 = dest(r0 + 8 + 4 * quad + i);
+    for (int i = 0; i < 4; ++i) {
+      const long long d1 = part_row(r0 + 4 * quad + i);
+      const long long d2 = part_row(r0 + 8 + 4 * quad + i);
 #pragma unroll
-        for (int n = 0; n < 8; ++n) {
-          if (d1 >= 0) p.ws_o[d1 * kDX + 16 * n + col] = O1[n][i];
-          if (d2 >= 0) p.ws_o[d2 * kDX + 16 * n + col] = O2[n][i];
-        }
+      for (int n = 0; n < 8; ++n) {
+        if (d1 >= 0) p.ws_o[d1 * kDX + 16 * n + col] = O1[n][i];
+        if (d2 >= 0) p.ws_o[d2 * kDX + 16 * n + col] = O2[n][i];
       }
     }
-    if (lane < 16) {
-      const long long d = dest(r0 + lane);
-      if (d >= 0) {
-        p.ws_ml[d * 2 + 0] = m_run;
-        p.ws_ml[d * 2 + 1] = lrow;
-      }
-    }
-  } else {
-    const size_t base = ((size_t)u * p.splits + split) * p.rows_pad + r0;
-    if (lane < 32) {
-#pragma unroll
-      for (int n = 0; n < 8; ++n)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p.ws_o[(base + 4 * quad + i) * kDX + 16 * n + col] = O1[n][i];
-          p.ws_o[(base + 8 + 4 * quad + i) * kDX + 16 * n + col] = O2[n][i];
-        }
-    }
-    if (lane < 16) {
-      p.ws_ml[(base + lane) * 2 + 0] = m_run;
-      p.ws_ml[(base + lane) * 2 + 1] = lrow;
+  }
+  if (lane < 16) {
+    const long long d = part_row(r0 + lane);
+    if (d >= 0) {
+      p.ws_ml[d * 2 + 0] = m_run;
+      p.ws_ml[d * 2 + 1] = lrow;
     }
   }
 }

@@ -23,6 +23,12 @@ namespace {
 
 constexpr int kDS = 128;
 constexpr int kMaxLevelSplits = kMaxSplits / 2;  // both levels share one wave's lanes in the merge
+// Tiles per split unless the caller forces the split count.  Prefix lengths
+// and suffix lengths are ragged, and only their maxima are known here: short
+// splits keep the longest ones from setting the time of the call (a split
+// with no tile of its sequence leaves at once).
+constexpr int kPrefixTilesPerSplit = 128;
+constexpr int kSuffixTilesPerSplit = 32;
 
 struct MergeParams {
   const float* o1;   // prefix partials [B][hkv][s1][rows_seq][D]
@@ -75,6 +81,7 @@ __global__ __launch_bounds__(256) void shared_merge_kernel(const MergeParams m) 
 #pragma unroll 4
   for (int sp = 0; sp < S; ++sp) {
     const float w = as_f32((uint32_t)__builtin_amdgcn_readlane((int)as_u32(ws), sp));
+    if (w == 0.0f) continue;  // an empty split stores no O
     const float* src = sp < S1 ? p1 + (size_t)sp * m.rows_seq * kDS : p2 + (size_t)(sp - S1) * m.rows2 * kDS;
     const f32x2_t o = *reinterpret_cast<const f32x2_t*>(src);
     acc[0] += w * o[0];
@@ -92,15 +99,21 @@ __global__ __launch_bounds__(256) void shared_merge_kernel(const MergeParams m) 
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Plan one level; a split count above what the merge holds is replanned at
-// that maximum.
+// Plan one level of n_tiles tiles at most: the caller's split count if it
+// forces one, else the kernel's own plan refined to at most max_per tiles per
+// split; never more splits than the merge holds.
 template <typename F>
-int plan_level(F plan_fn, uint32_t flags, DecodePlan* plan) {
+int plan_level(F plan_fn, uint32_t flags, int n_tiles, int max_per, DecodePlan* plan) {
+  const uint32_t base = flags & ~KVQ_SPLITS_MASK;
   const int forced = (int)((flags & KVQ_SPLITS_MASK) >> KVQ_SPLITS_SHIFT);
-  if (forced > kMaxLevelSplits) flags = (flags & ~KVQ_SPLITS_MASK) | KVQ_SPLITS(kMaxLevelSplits);
-  int st = plan_fn(flags, plan);
-  if (st != KVQ_OK || plan->splits <= kMaxLevelSplits) return st;
-  return plan_fn((flags & ~KVQ_SPLITS_MASK) | KVQ_SPLITS(kMaxLevelSplits), plan);
+  if (forced > 0) return plan_fn(base | KVQ_SPLITS(forced < kMaxLevelSplits ? forced : kMaxLevelSplits), plan);
+  int st = plan_fn(base, plan);
+  if (st != KVQ_OK) return st;
+  int want = plan->splits;
+  if (plan->tiles_per_split > max_per) want = (n_tiles + max_per - 1) / max_per;
+  if (want > kMaxLevelSplits) want = kMaxLevelSplits;
+  if (want == plan->splits) return KVQ_OK;
+  return plan_fn(base | KVQ_SPLITS(want), plan);
 }
 
 }  // namespace
@@ -110,11 +123,10 @@ int plan_shared(const CacheGeom& c, int batch, int hq, int n_q, const kvq_prefix
   if (c.d != kDS || c.fmt != KVQ_FMT_FP4_E2M1) return KVQ_ERR_UNSUPPORTED;
   const long long rows_seq = (long long)(hq / c.hkv) * n_q;
   const long long pre_rows = rows_seq * g.max_group_size;
+  const int prefix_len = g.max_prefix_pages * c.p;
   int st = plan_level(
-      [&](uint32_t f, DecodePlan* p) {
-        return plan_extend_rows(c, g.num_groups, pre_rows, g.max_prefix_pages * c.p, f, p);
-      },
-      flags, &plan->prefix);
+      [&](uint32_t f, DecodePlan* p) { return plan_extend_rows(c, g.num_groups, pre_rows, prefix_len, f, p); },
+      flags, (prefix_len + 15) / 16, kPrefixTilesPerSplit, &plan->prefix);
   if (st != KVQ_OK) return st;
   plan->prefix.kind = kDecodeMany;
   // prefix partials are stored per member sequence, not per padded unit
@@ -122,7 +134,7 @@ int plan_shared(const CacheGeom& c, int batch, int hq, int n_q, const kvq_prefix
       plan->prefix.qops_bytes + (size_t)batch * c.hkv * plan->prefix.splits * rows_seq * (kDS + 2) * sizeof(float);
   const int suffix_len = g.max_suffix_len > 0 ? g.max_suffix_len : 1;
   st = plan_level([&](uint32_t f, DecodePlan* p) { return plan_decode(c, batch, hq, n_q, suffix_len, f, p); },
-                  flags, &plan->suffix);
+                  flags, (suffix_len + 15) / 16, kSuffixTilesPerSplit, &plan->suffix);
   if (st != KVQ_OK) return st;
   plan->suffix_offset = align256(plan->prefix.workspace);
   plan->workspace = plan->suffix_offset + plan->suffix.workspace;

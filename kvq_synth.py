@@ -76,6 +76,12 @@ WORKLOADS: Dict[str, Workload] = {
                  description="batch 32 agentic mix, contexts log-uniform "
                              "4K-128K, 92% of pages from 4 shared prefixes, "
                              "3 MTP verify positions with causal mask"),
+        Workload("fork_b32_l32k", batch=32, num_kv_heads=8, num_q_heads=64,
+                 head_dim=128, page_size=16, context=32768, n_q=3,
+                 n_prefixes=1, shared_frac=0.9375,
+                 description="batch 32 forked from one prefix: context 32768, "
+                             "the first 30720 tokens shared by every sequence, "
+                             "3 MTP verify positions with causal mask"),
         Workload("mla_b16_l128k", batch=16, num_kv_heads=1, num_q_heads=64,
                  head_dim=512, page_size=64, context=131072, kv_shared=True,
                  std=math.sqrt(0.5), n_outliers=4, outlier_mult=16.0,

@@ -8,6 +8,9 @@ compared element by element (max |err| <= 2e-3, relative L2 <= 1e-3).
   mtp_mixed_b32  batch 32, contexts 4K-128K log-uniform, 92% of pages shared
                  from 4 prefixes, 3 MTP verify positions (24 rows per KV head);
                  plain and shared-prefix decode
+  fork_b32_l32k  batch 32, context 32768 whose first 30720 tokens are one
+                 prefix of every sequence, 3 MTP verify positions
+                 (shared-prefix decode)
   mla_b16_l128k  batch 16, one latent head of width 512 (K = V), 64 absorbed
                  query heads, context 131072, page 64
   extend         batch 4, 8 KV / 64 Q heads, context 32768 whose last 64
@@ -69,6 +72,12 @@ def test_fullsize_mtp_mixed_b32_shared_prefix_sampled(gpu):
     """The same agentic mix through the shared-prefix entry point (each
     prefix group's pages read once for all its members)."""
     _check("mtp_mixed_b32", "fp4", 16, 5, shared=True)
+
+
+def test_fullsize_fork_b32_l32k_shared_prefix_sampled(gpu):
+    """32 sequences forked from one 30K-token prefix, through the
+    shared-prefix entry point (768 gathered rows per KV head)."""
+    _check("fork_b32_l32k", "fp4", 16, 6, shared=True)
 
 
 def test_fullsize_mla_b16_l128k_sampled(gpu):

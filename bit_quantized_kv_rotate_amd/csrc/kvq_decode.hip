@@ -254,8 +254,13 @@ __device__ __forceinline__ void compute_pair(const DecodeParams& p, const int32_
     float mloc = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                        fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
     mloc = quad_max(mloc);
+    // lazy reference maximum: a row's reference moves only when its running
+    // maximum passes it by more than kLazyLog2, so most tiles skip the
+    // rescale; the weights stay below 2^kLazyLog2
     const float m_old = st.m_run[t];
-    const float m_new = fmaxf(m_old, mloc);
+    const float m_tgt = fmaxf(m_old, mloc);
+    const bool grow = m_tgt > m_old + kLazyLog2;
+    const float m_new = grow ? m_tgt : m_old;
     const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
     st.m_run[t] = m_new;
     float psum = 0.0f;
@@ -272,8 +277,8 @@ __device__ __forceinline__ void compute_pair(const DecodeParams& p, const int32_
       const uint32_t l = pack_bf16x2(p0 - as_f32(u0 & 0xFFFF0000u), p1 - as_f32(u1 & 0xFFFF0000u));
       pw[e] = hi_col ? h : l;
     }
-    if (__builtin_amdgcn_ballot_w64(m_new != m_old)) {
-      // a row max moved in some lane: rescale (rare once the scan settles)
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      // a row reference moved in some lane: rescale (rare once the scan settles)
       const float alpha = __builtin_amdgcn_exp2f(m_old - m_use);
       st.l_run[t] *= alpha;
       float ar[4];

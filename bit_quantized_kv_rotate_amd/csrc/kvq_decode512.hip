@@ -288,8 +288,12 @@ __global__ __launch_bounds__(512) void decode512_kernel(const DecodeParams p) {
     float mloc = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                        fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
     mloc = quad_max(mloc);
+    // lazy reference maximum (kLazyLog2): most pairs leave it, and so the
+    // output rows, unchanged
     const float m_old = m_run;
-    const float m_new = fmaxf(m_old, mloc);
+    const float m_tgt = fmaxf(m_old, mloc);
+    const bool grow = m_tgt > m_old + kLazyLog2;
+    const float m_new = grow ? m_tgt : m_old;
     const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
     m_run = m_new;
     float psum = 0.0f;
@@ -311,7 +315,7 @@ __global__ __launch_bounds__(512) void decode512_kernel(const DecodeParams p) {
     const float alpha = __builtin_amdgcn_exp2f(m_old - m_use);
     l_run = l_run * alpha + psum;
     if (lane < 8) s_alpha[par][8 * w + lane] = alpha;
-    const bool moved = __builtin_amdgcn_ballot_w64(m_new != m_old) != 0;
+    const bool moved = __builtin_amdgcn_ballot_w64(grow) != 0;
     if (lane == 0) s_flag[par][w] = moved ? 1 : 0;
   };
 

@@ -174,6 +174,11 @@ __device__ __forceinline__ void wave_fwht(float (&x)[C], int lane, float c) {
 }
 
 constexpr int kMaxSplits = 64;
+// The online softmax keeps a per-row reference maximum that may lag the
+// running maximum by up to 2^kLazyLog2 (weights exp2(s - ref) <= 2^8): a
+// rescale of the output is needed only when a row's maximum passes its
+// reference by more than that.  The split partials carry the reference as m.
+constexpr float kLazyLog2 = 8.0f;
 
 // Combine the split partials of each query row: weights 2^(m_s - M),
 // normalise by the combined sum, rotate back, store.  A split of weight zero

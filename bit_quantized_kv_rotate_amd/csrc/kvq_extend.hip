@@ -320,8 +320,13 @@ __global__ __launch_bounds__(512) void extend_kernel(const DecodeParams p) {
         float mloc = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                            fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
         mloc = quad_max(mloc);
+        // lazy reference maximum: a row's reference moves only when its
+        // running maximum passes it by more than kLazyLog2, so most pairs
+        // skip the rescale; weights stay below 2^kLazyLog2
         const float m_old = m_run;
-        const float m_new = fmaxf(m_old, mloc);
+        const float m_tgt = fmaxf(m_old, mloc);
+        const bool grow = m_tgt > m_old + kLazyLog2;
+        const float m_new = grow ? m_tgt : m_old;
         const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
         m_run = m_new;
         float psum = 0.0f;
@@ -341,20 +346,25 @@ __global__ __launch_bounds__(512) void extend_kernel(const DecodeParams p) {
         uint32_t a1[4], a2[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const uint32_t lr = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)l[e], 0x128, 0xF, 0xF, false);
-          const uint32_t hr = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)h[e], 0x128, 0xF, 0xF, false);
+          const uint32_t lr = (uint32_t)__builtin_amdgcn_mov_dpp((int)l[e], 0x128, 0xF, 0xF, false);
+          const uint32_t hr = (uint32_t)__builtin_amdgcn_mov_dpp((int)h[e], 0x128, 0xF, 0xF, false);
           a1[e] = hi_col ? h[e] : lr;
           a2[e] = hi_col ? hr : l[e];
         }
-        if (__builtin_amdgcn_ballot_w64(m_new != m_old)) {
-          // a row max moved: rescale; O1 lane (q, c) holds rows (4q + i) & 7,
-          // O2 rows 8 + ((4q + i) & 7)
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          // a row max moved: rescale.  Lane (q, c) of O1 holds rows
+          // (4q + i) & 7, of O2 rows 8 + ((4q + i) & 7): row i or 4 + i by the
+          // parity of q; lane c holds the factor of row c (in every quad)
           const float alpha = __builtin_amdgcn_exp2f(m_old - m_use);
           l_run *= alpha;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float al1 = __shfl(alpha, (4 * quad + i) & 7, 64);
-            const float al2 = __shfl(alpha, 8 + ((4 * quad + i) & 7), 64);
+            const float x0 = as_f32((uint32_t)__builtin_amdgcn_readlane((int)as_u32(alpha), i));
+            const float x1 = as_f32((uint32_t)__builtin_amdgcn_readlane((int)as_u32(alpha), 4 + i));
+            const float y0 = as_f32((uint32_t)__builtin_amdgcn_readlane((int)as_u32(alpha), 8 + i));
+            const float y1 = as_f32((uint32_t)__builtin_amdgcn_readlane((int)as_u32(alpha), 12 + i));
+            const float al1 = (quad & 1) ? x1 : x0;
+            const float al2 = (quad & 1) ? y1 : y0;
 #pragma unroll
             for (int n = 0; n < 8; ++n) {
               O1[n][i] *= al1;

@@ -12,7 +12,7 @@ import torch
 import bit_quantized_kv_rotate_amd as kvq
 import kvq_synth as syn
 import oracle
-from kvq_gpu_util import Filled, assert_close, oracle_decode_batch, to_dev_i32
+from kvq_gpu_util import SPLIT_ATOL, SPLIT_RTOL, Filled, assert_close, oracle_decode_batch, to_dev_i32
 
 pytestmark = pytest.mark.gpu
 
@@ -97,9 +97,7 @@ def test_decode_split_count_invariance(gpu):
     ref = f.decode(q, flags=kvq.splits_flag(1)).cpu().numpy()
     for s in (2, 3, 5, 8, 16):
         got = f.decode(q, flags=kvq.splits_flag(s)).cpu().numpy()
-        # only the fp32 summation order changes (per-split partial sums and
-        # their merge): a few ulp of the larger outputs
-        np.testing.assert_allclose(got, ref, rtol=1e-5, atol=2e-5)
+        np.testing.assert_allclose(got, ref, rtol=SPLIT_RTOL, atol=SPLIT_ATOL)
     want = oracle_decode_batch(f, syn.bf16_bits(q))
     assert_close(ref[0], want[0], "one split")
 
@@ -185,7 +183,7 @@ def test_decode_latent_512_split_invariance(gpu):
     ref = f.decode(q, flags=kvq.splits_flag(1)).cpu().numpy()
     for s in (2, 3, 7, 16):
         got = f.decode(q, flags=kvq.splits_flag(s)).cpu().numpy()
-        np.testing.assert_allclose(got, ref, rtol=1e-5, atol=5e-5)
+        np.testing.assert_allclose(got, ref, rtol=SPLIT_RTOL, atol=SPLIT_ATOL)
     want = oracle_decode_batch(f, syn.bf16_bits(q))
     assert_close(ref[0], want[0], "latent one split")
 
@@ -215,9 +213,7 @@ def test_decode_many_rows_split_invariance(gpu):
     ref = f.decode(q, flags=kvq.splits_flag(1)).cpu().numpy()
     for s in (2, 5, 11):
         got = f.decode(q, flags=kvq.splits_flag(s)).cpu().numpy()
-        # each split rounds its weights to bf16 hi + lo against its own running
-        # maximum (2^-17 relative per weight) besides reordering the fp32 sums
-        np.testing.assert_allclose(got, ref, rtol=5e-5, atol=1e-4)
+        np.testing.assert_allclose(got, ref, rtol=SPLIT_RTOL, atol=SPLIT_ATOL)
     want = oracle_decode_batch(f, syn.bf16_bits(q))
     for b in range(wl.batch):
         assert_close(ref[b], want[b], "many rows one split seq %d" % b)

@@ -264,6 +264,21 @@ def queries(wl: Workload, device="cpu") -> torch.Tensor:
                  [h // g for h in range(wl.num_q_heads)], device)
 
 
+def selected_positions(wl: Workload, plan: PagePlan, seq: int, n_groups: int = 512,
+                       group: int = 4, recent: int = 3) -> np.ndarray:
+    """Synthetic selection for one sequence, in the shape an index cache
+    returns: up to ``n_groups`` distinct pooled groups of ``group``
+    consecutive history tokens (in a random order, as a top-k list comes)
+    plus the last ``recent`` tokens.  int32 token positions."""
+    L = int(plan.context_lens[seq])
+    rec = min(recent, L)
+    n_hist = (L - rec) // group
+    g = _gen(wl, "select", seq, "cpu")
+    pick = torch.randperm(n_hist, generator=g)[: min(n_groups, n_hist)].numpy()
+    pos = (pick[:, None] * group + np.arange(group)[None, :]).reshape(-1)
+    return np.concatenate([pos, np.arange(L - rec, L)]).astype(np.int32)
+
+
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
     """bf16 tensor -> numpy uint16 bit patterns (on the host)."""
     return t.detach().to("cpu").contiguous().view(torch.int16).numpy().view(np.uint16)

@@ -252,6 +252,38 @@ def decode(q_bf16: np.ndarray, khat: np.ndarray, vhat, rotate: bool,
     return out
 
 
+def decode_selected(q_bf16: np.ndarray, khat: np.ndarray, vhat, sel, rotate: bool,
+                    sm_scale: float) -> np.ndarray:
+    """Attention of one query position over selected history positions only.
+    [GLM] "How the serving path works", "Sparse attention and K-pool
+    selection": a separate index picks the history each token attends to
+    (pooled four-token groups plus a few recent tokens); attention then reads
+    the cache rows of the picked positions alone.  sel: int positions into
+    the sequence's cache (a position listed twice counts twice).
+    q_bf16: uint16 [1, hq, d]; khat/vhat: [L, hkv, d] float32."""
+    idx = np.asarray(sel, dtype=np.int64)
+    k = np.ascontiguousarray(khat[idx])
+    v = None if vhat is None else np.ascontiguousarray(vhat[idx])
+    return decode(q_bf16, k, v, rotate, sm_scale)
+
+
+def reference_decode_selected(q_bf16, k_bf16, v_bf16, sel, fmt: str, rotate: bool,
+                              sm_scale: float) -> np.ndarray:
+    """Whole pipeline for one sequence and one query position: quantise the
+    cache, dequantise it, and attend over the selected positions."""
+    q = np.asarray(q_bf16)
+    assert q.shape[0] == 1, "one query position per selection"
+    if fmt != "fp4":
+        raise ValueError(fmt)
+    kc, ks = quantize_fp4(k_bf16, rotate)
+    khat = dequant_fp4(kc, ks)
+    vhat = None
+    if v_bf16 is not None:
+        vc, vs = quantize_fp4(v_bf16, rotate)
+        vhat = dequant_fp4(vc, vs)
+    return decode_selected(q, khat, vhat, sel, rotate, sm_scale)
+
+
 def reference_decode_seq(q_bf16, k_bf16, v_bf16, fmt: str, rotate: bool,
                          sm_scale: float) -> np.ndarray:
     """Whole pipeline for one sequence from bf16 inputs: quantise the cache

@@ -409,3 +409,62 @@ def test_decode_rotated_cache_matches_plain_attention():
     H = scipy.linalg.hadamard(d) / math.sqrt(d)
     want = _np_attention(qrot, khat, vhat, sm, 1) @ H
     np.testing.assert_allclose(got, want, rtol=0, atol=1e-11)
+
+
+# ------------------------------------------------------------ selected positions
+# [GLM] "How the serving path works", "Sparse attention and K-pool selection":
+# a separate index decides which history positions a token attends to; the
+# attention itself reads only those cache rows.
+
+def _selected_case(seed, L=40, d=64, hq=4, shared=False):
+    rng = np.random.default_rng(seed)
+    kb = _bf16(rng.standard_normal((L, 1, d)))
+    vb = None if shared else _bf16(rng.standard_normal((L, 1, d)))
+    qb = _bf16(rng.standard_normal((1, hq, d)))
+    kc, ks = oracle.quantize_fp4(kb, rotate=True)
+    khat = oracle.dequant_fp4(kc, ks)
+    vhat = None
+    if vb is not None:
+        vc, vs = oracle.quantize_fp4(vb, rotate=True)
+        vhat = oracle.dequant_fp4(vc, vs)
+    return qb, khat, vhat
+
+
+def test_selected_every_position_is_full_decode():
+    qb, khat, vhat = _selected_case(41)
+    sm = 1 / math.sqrt(64)
+    full = oracle.decode(qb, khat, vhat, True, sm)
+    got = oracle.decode_selected(qb, khat, vhat, np.arange(40), True, sm)
+    assert np.array_equal(got, full)
+    perm = np.random.default_rng(3).permutation(40)
+    np.testing.assert_allclose(oracle.decode_selected(qb, khat, vhat, perm, True, sm), full, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("shared", [False, True])
+def test_selected_single_position_returns_its_value_row(shared):
+    """One selected position has weight 1: every head's output is that
+    position's value row rotated back (H is its own inverse)."""
+    qb, khat, vhat = _selected_case(42, shared=shared)
+    H = scipy.linalg.hadamard(64) / math.sqrt(64)
+    for t in (0, 7, 39):
+        got = oracle.decode_selected(qb, khat, vhat, [t], True, 1 / 8)
+        row = (khat if vhat is None else vhat)[t, 0].astype(np.float64) @ H
+        for h in range(4):
+            np.testing.assert_allclose(got[0, h], row, rtol=0, atol=1e-12)
+
+
+def test_selected_matches_numpy_over_listed_rows():
+    """Independent restatement (numpy matmul, scipy softmax) over the listed
+    rows in any order; a position listed twice counts twice."""
+    qb, khat, vhat = _selected_case(43)
+    sel = [5, 3, 3, 20, 39, 0]
+    sm = 1 / 8
+    got = oracle.decode_selected(qb, khat, vhat, sel, True, sm)
+    qf = torch.from_numpy(qb.view(np.int16)).view(torch.bfloat16).float().numpy()
+    qrot = oracle.fwht_f32(qf).astype(np.float64)
+    H = scipy.linalg.hadamard(64) / math.sqrt(64)
+    want = _np_attention(qrot, khat[sel], vhat[sel], sm, 1) @ H
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-11)
+    # the duplicate matters: without it the result moves
+    other = oracle.decode_selected(qb, khat, vhat, [5, 3, 20, 39, 0], True, sm)
+    assert np.abs(other - got).max() > 1e-6

@@ -553,9 +553,38 @@ def bench_latent(kvq, syn, dev, stream, steps, R, name="mla_b16_l128k"):
     t_peak = qk_flops / (PEAK_FP4_FP6 * 1e12) + pv_flops / (PEAK_BF16 * 1e12)
     issued = qk_flops + pv_flops
     kv_bytes = tokens * (D // 2 + D // 32)
+
+    # selected-position decode over the same cache: per sequence 512 pooled
+    # four-token groups plus the 3 most recent tokens (2,051 positions)
+    sels = [syn.selected_positions(wl, plan, b) for b in range(B)]
+    max_sel = max(len(x) for x in sels)
+    sel = np.zeros((B, max_sel), dtype=np.int32)
+    for b, x in enumerate(sels):
+        sel[b, : len(x)] = x
+    sel_d = torch_from(sel, dev)
+    sel_lens = torch_from(np.array([len(x) for x in sels], dtype=np.int32), dev)
+    ws_s = torch.empty(kvq.decode_selected_workspace_bytes(c, B, HQ, max_sel), dtype=torch.uint8, device=dev)
+    out_s = torch.empty((B, 1, HQ, D), dtype=torch.float32, device=dev)
+    for i in range(10):
+        kvq.decode_attn_fp4_selected(cs[i % R], q, bt, sel_d, sel_lens, out=out_s, workspace=ws_s, stream=stream)
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(es):
+        a.record(stream)
+        kvq.decode_attn_fp4_selected(cs[i % R], q, bt, sel_d, sel_lens, out=out_s, workspace=ws_s, stream=stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+    t_sel = statistics.fmean([a.elapsed_time(b) for a, b in es])
+    n_sel = int(sum(len(x) for x in sels)) * wl.num_kv_heads
     del cs, c
     return {
         "workload": "%s: %s" % (wl.name, wl.description),
+        "selected": {
+            "positions_per_sequence": max_sel,
+            "decode_ms_events_mean": round(t_sel, 4),
+            "speedup_vs_full_scan": round(t / t_sel, 2),
+            "selected_kv_gbs": round(n_sel * (D // 2 + D // 32) / (t_sel * 1e-3) / 1e9, 1),
+            "note": "kvq_decode_attn_fp4_selected: 512 pooled four-token groups + 3 recent tokens per sequence",
+        },
         "decode_ms_events_mean": round(t, 4),
         "kv_gbs": round(kv_bytes / (t * 1e-3) / 1e9, 1),
         "hbm_frac": round(kv_bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

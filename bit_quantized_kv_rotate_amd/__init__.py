@@ -99,6 +99,9 @@ SIGNATURES = {
     "kvq_decode_shared_workspace_bytes": (_SZ, [_DESC, _I32, _I32, _I32, _GROUPS, _U32]),
     "kvq_decode_attn_fp4_shared": (ctypes.c_int, [_DESC, _P, _I32, _I32, _I32, _P, _I32, _P, _GROUPS,
                                                   ctypes.c_float, _U32, _P, _P, _SZ, _P]),
+    "kvq_decode_selected_workspace_bytes": (_SZ, [_DESC, _I32, _I32, _I32, _U32]),
+    "kvq_decode_attn_fp4_selected": (ctypes.c_int, [_DESC, _P, _I32, _I32, _P, _I32, _P, _P, _I32,
+                                                    ctypes.c_float, _U32, _P, _P, _SZ, _P]),
     "kvq_dequant": (ctypes.c_int, [_DESC, _P, _I32, _P, _P, _P]),
     "kvq_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "kvq_version": (ctypes.c_int, []),
@@ -355,6 +358,53 @@ def decode_attn_fp4_shared(cache: KVCache, q: torch.Tensor, block_tables: torch.
     _check(library().kvq_decode_attn_fp4_shared(cache.ref(), qp, B, hq, n_q, bp, int(block_tables.shape[1]), cp,
                                                  groups.ref(), float(sm_scale), int(flags), op, wp, wbytes,
                                                  _stream(stream)))
+    return out
+
+
+def decode_selected_workspace_bytes(cache: KVCache, batch: int, num_q_heads: int, max_selected: int,
+                                    flags: int = 0) -> int:
+    return int(library().kvq_decode_selected_workspace_bytes(cache.ref(), batch, num_q_heads, max_selected, flags))
+
+
+def decode_attn_fp4_selected(cache: KVCache, q: torch.Tensor, block_tables: torch.Tensor,
+                             sel: torch.Tensor, sel_lens: torch.Tensor,
+                             sm_scale: Optional[float] = None, flags: int = 0,
+                             out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                             stream=None) -> torch.Tensor:
+    """Attention of one query position per sequence over its selected
+    history positions: q bf16 [batch, 1, num_q_heads, head_dim], sel int32
+    [batch, max_selected], sel_lens int32 [batch]; returns fp32 like q."""
+    B, n_q, hq, d = (int(x) for x in q.shape)
+    if n_q != 1:
+        raise ValueError("one query position per sequence")
+    if d != cache.head_dim:
+        raise ValueError("q head_dim %d does not match the cache (%d)" % (d, cache.head_dim))
+    qp = _dev(q, torch.bfloat16, "q")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [batch, max_pages]")
+    bp = _dev(block_tables, torch.int32, "block_tables")
+    if sel.dim() != 2 or sel.shape[0] != B:
+        raise ValueError("sel must be [batch, max_selected]")
+    sp = _dev(sel, torch.int32, "sel")
+    _shape(sel_lens, (B,), "sel_lens")
+    lp = _dev(sel_lens, torch.int32, "sel_lens")
+    max_sel = int(sel.shape[1])
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, 1, hq, d), dtype=torch.float32, device=q.device)
+    _shape(out, (B, 1, hq, d), "out")
+    op = _dev(out, torch.float32, "out")
+    need = decode_selected_workspace_bytes(cache, B, hq, max_sel, flags)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wp, wbytes = None, 0
+    if workspace is not None:
+        wp = _dev(workspace, workspace.dtype, "workspace")
+        wbytes = workspace.numel() * workspace.element_size()
+    _check(library().kvq_decode_attn_fp4_selected(cache.ref(), qp, B, hq, bp, int(block_tables.shape[1]), sp, lp,
+                                                   max_sel, float(sm_scale), int(flags), op, wp, wbytes,
+                                                   _stream(stream)))
     return out
 
 

@@ -226,6 +226,59 @@ int kvq_decode_attn_fp4_shared(const kvq_cache_desc* desc, const void* q, int32_
   return hip_status(launch_shared(a, (hipStream_t)stream));
 }
 
+size_t kvq_decode_selected_workspace_bytes(const kvq_cache_desc* desc, int32_t batch, int32_t num_q_heads,
+                                           int32_t max_selected, uint32_t flags) {
+  CacheGeom g;
+  if (check_desc(desc, &g) != KVQ_OK || g.fmt != KVQ_FMT_FP4_E2M1 || g.d != 512) return 0;
+  if (batch <= 0 || num_q_heads <= 0 || max_selected < 0 || num_q_heads % g.hkv != 0) return 0;
+  DecodePlan plan;
+  if (plan_decode(g, batch, num_q_heads, 1, max_selected > 0 ? max_selected : 1, flags, &plan) != KVQ_OK) return 0;
+  return plan.workspace;
+}
+
+int kvq_decode_attn_fp4_selected(const kvq_cache_desc* desc, const void* q, int32_t batch, int32_t num_q_heads,
+                                 const int32_t* block_tables, int32_t max_pages_per_seq, const int32_t* sel,
+                                 const int32_t* sel_lens, int32_t max_selected, float sm_scale, uint32_t flags,
+                                 float* out, void* workspace, size_t workspace_bytes, kvq_stream_t stream) {
+  CacheGeom g;
+  int st = check_desc(desc, &g);
+  if (st != KVQ_OK) return st;
+  if (g.fmt != KVQ_FMT_FP4_E2M1) return KVQ_ERR_FORMAT;
+  st = check_cache_ptrs(desc);
+  if (st != KVQ_OK) return st;
+  if (!q || !block_tables || !sel || !sel_lens || !out) return KVQ_ERR_NULL;
+  if (batch < 0 || num_q_heads <= 0 || max_pages_per_seq <= 0 || max_selected < 0) return KVQ_ERR_SHAPE;
+  if (num_q_heads % g.hkv != 0) return KVQ_ERR_SHAPE;
+  if (!std::isfinite(sm_scale)) return KVQ_ERR_SHAPE;
+  if (flags & ~(KVQ_Q_PREROTATED | KVQ_OUT_ROTATED | KVQ_SPLITS_MASK)) return KVQ_ERR_SHAPE;
+  if (g.d != 512) return KVQ_ERR_UNSUPPORTED;
+  if (batch == 0) return KVQ_OK;
+  DecodePlan plan;
+  st = plan_decode(g, batch, num_q_heads, 1, max_selected > 0 ? max_selected : 1, flags, &plan);
+  if (st != KVQ_OK) return st;
+  if (!workspace || workspace_bytes < plan.workspace) return KVQ_ERR_WORKSPACE;
+  if ((uintptr_t)workspace & 15u) return KVQ_ERR_WORKSPACE;
+  DecodeArgs a;
+  a.c = g;
+  a.plan = plan;
+  a.q = (const uint16_t*)q;
+  a.batch = batch;
+  a.hq = num_q_heads;
+  a.n_q = 1;
+  a.group = num_q_heads / g.hkv;
+  a.block_tables = block_tables;
+  a.max_pages = max_pages_per_seq;
+  a.context_lens = sel_lens;  // the scan runs over each sequence's list
+  a.qscale = (float)((double)sm_scale * 1.4426950408889634);  // log2(e)
+  a.rotate_q = g.rotate && !(flags & KVQ_Q_PREROTATED);
+  a.rotate_out = g.rotate && !(flags & KVQ_OUT_ROTATED);
+  a.out = out;
+  a.workspace = (float*)workspace;
+  a.sel = sel;
+  a.sel_stride = max_selected > 0 ? max_selected : 1;
+  return hip_status(launch_decode(a, (hipStream_t)stream));
+}
+
 int kvq_decode_attn_fp4(const kvq_cache_desc* desc, const void* q, int32_t batch,
                         int32_t num_q_heads, int32_t n_q, const int32_t* block_tables,
                         int32_t max_pages_per_seq, const int32_t* context_lens,

@@ -34,10 +34,11 @@ constexpr int kW5 = 8;               // waves per block
 constexpr int kVRow5 = 2 * kD5 + 32;  // LDS bytes per bf16 token row (padded)
 constexpr int kMaxRG5 = 4;           // 16-row groups (64 rows)
 // tile pairs in flight per wave (one chunk each): three, fewer where the
-// accumulators of 64 rows (and a separate V chunk) leave no room
-template <int RG, bool SHARED>
+// accumulators of 64 rows (and a separate V chunk, or the per-lane addresses
+// of a gathered selection) leave no room
+template <int RG, bool SHARED, bool SEL>
 struct Ring5 {
-  static constexpr int kN = RG >= 4 ? (SHARED ? 2 : 1) : (SHARED || RG <= 2 ? 3 : 2);
+  static constexpr int kN = RG >= 4 ? (SHARED && !SEL ? 2 : 1) : (SHARED || RG <= 2 ? 3 : 2);
 };
 
 // Raw codes of the one (tile, 128-channel chunk) of a tile pair this wave
@@ -50,9 +51,32 @@ struct Chunk5 {
   uint32_t vsc;
 };
 
-template <bool SHARED>
-__device__ __forceinline__ void load_chunk5(const DecodeParams& p, const int32_t* bt_row, int kvh,
-                                            int tile, int chunk, int lane, Chunk5& t) {
+template <bool SHARED, bool SEL>
+__device__ __forceinline__ void load_chunk5(const DecodeParams& p, const int32_t* bt_row, const int32_t* sel_row,
+                                            int L, int kvh, int tile, int chunk, int lane, Chunk5& t) {
+  if constexpr (SEL) {
+    // list entry tile*16 + token of this lane (clamped to the list; entries
+    // past it are masked), gathered through the block table: every lane
+    // addresses its own page
+    const int j = min(tile * 16 + (lane & 15), L - 1);
+    const int pos = sel_row[j];
+    const int page = bt_row[pos >> p.p_shift];
+    const int in_page = pos & (p.P - 1);
+    const int grp = 4 * chunk + (lane >> 4);
+    const int64_t coff = (int64_t)page * p.c_page + (int64_t)kvh * p.c_head + ((int64_t)grp * p.P + in_page) * 16;
+    const int64_t soff = (int64_t)page * p.s_page + (int64_t)kvh * p.s_head + (int64_t)grp * p.P + in_page;
+    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(p.kc + coff);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) t.k[w] = a[w];
+    t.ksc = p.ks[soff];
+    if constexpr (!SHARED) {
+      const u32x4_t c = *reinterpret_cast<const u32x4_t*>(p.vc + coff);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) t.v[w] = c[w];
+      t.vsc = p.vs[soff];
+    }
+    return;
+  }
   const int tok = tile * 16;
   const int page = __builtin_amdgcn_readfirstlane(bt_row[tok >> p.p_shift]);
   const int in_page = tok & (p.P - 1);
@@ -171,7 +195,10 @@ __device__ __forceinline__ f32x4_t qk_chunk5(f32x4_t acc, const u32x4_t kc, int 
   return acc;
 }
 
-template <int RG, bool SHARED>
+// SEL: the scan runs over the list of selected positions of each sequence
+// (p.sel; context_lens are the list lengths), one query position per
+// sequence.
+template <int RG, bool SHARED, bool SEL>
 __global__ __launch_bounds__(512) void decode512_kernel(const DecodeParams p) {
   constexpr int ROWS = 16 * RG;
   constexpr int NO = 2 * RG;
@@ -201,8 +228,9 @@ __global__ __launch_bounds__(512) void decode512_kernel(const DecodeParams p) {
   const int col = lane & 15;
   const int quad = lane >> 4;
   const int32_t* bt_row = p.block_tables + (size_t)b * p.max_pages;
+  const int32_t* sel_row = SEL ? p.sel + (size_t)b * p.sel_stride : nullptr;
   const int n_pairs = (t_end > t_begin) ? ((t_end - t_begin + 1) >> 1) : 0;
-  constexpr int kRing5 = Ring5<RG, SHARED>::kN;
+  constexpr int kRing5 = Ring5<RG, SHARED, SEL>::kN;
   const int n_iter = (n_pairs + kRing5 - 1) / kRing5;  // pairs padded to a multiple of kRing5
   const bool owner = (NO == kW5) || w < NO;  // every wave owns rows at 64 rows
   const int mtile = w & 1;   // tile of each pair this wave stages
@@ -228,7 +256,7 @@ __global__ __launch_bounds__(512) void decode512_kernel(const DecodeParams p) {
   };
   // refill a ring slot with pair pi (clamped to the split's last tile)
   auto fetch = [&](int pi, Chunk5& c) {
-    load_chunk5<SHARED>(p, bt_row, kvh, min(t_begin + 2 * pi + mtile, t_end - 1), mchunk, lane, c);
+    load_chunk5<SHARED, SEL>(p, bt_row, sel_row, L, kvh, min(t_begin + 2 * pi + mtile, t_end - 1), mchunk, lane, c);
   };
 
   Chunk5 ring[kRing5];
@@ -429,7 +457,7 @@ int resident_blocks5(int dev) {
   }
   int cus = 0, blocks = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode512_kernel<RG, SHARED>, 512, 0) != hipSuccess) {
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode512_kernel<RG, SHARED, false>, 512, 0) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
@@ -453,27 +481,27 @@ int resident_slots5(int rg, bool shared) {
   }
 }
 
-template <int RG, bool SHARED>
+template <int RG, bool SHARED, bool SEL>
 hipError_t launch5(const DecodeParams& p, int batch, hipStream_t stream) {
   const unsigned qblocks = (unsigned)((size_t)batch * p.hkv * 16 * RG / 4);
   hipLaunchKernelGGL((qprep512_kernel<RG>), dim3(qblocks), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid((unsigned)p.splits, (unsigned)p.hkv, (unsigned)batch);
-  hipLaunchKernelGGL((decode512_kernel<RG, SHARED>), grid, dim3(64 * kW5), 0, stream, p);
+  hipLaunchKernelGGL((decode512_kernel<RG, SHARED, SEL>), grid, dim3(64 * kW5), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((merge_kernel<16 * RG, 8>), dim3(qblocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
-template <bool SHARED>
+template <bool SHARED, bool SEL>
 hipError_t launch5_rg(const DecodeParams& p, int rg, int batch, hipStream_t stream) {
   switch (rg) {
-    case 1: return launch5<1, SHARED>(p, batch, stream);
-    case 2: return launch5<2, SHARED>(p, batch, stream);
-    case 3: return launch5<3, SHARED>(p, batch, stream);
-    case 4: return launch5<4, SHARED>(p, batch, stream);
+    case 1: return launch5<1, SHARED, SEL>(p, batch, stream);
+    case 2: return launch5<2, SHARED, SEL>(p, batch, stream);
+    case 3: return launch5<3, SHARED, SEL>(p, batch, stream);
+    case 4: return launch5<4, SHARED, SEL>(p, batch, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -548,8 +576,14 @@ hipError_t launch_decode512(const DecodeArgs& a, hipStream_t stream) {
   p.qops = reinterpret_cast<uint32_t*>(ws);
   p.ws_o = reinterpret_cast<float*>(ws + a.plan.qops_bytes);
   p.ws_ml = p.ws_o + n_o;
-  if (a.c.kv_shared) return launch5_rg<true>(p, a.plan.row_tiles, a.batch, stream);
-  return launch5_rg<false>(p, a.plan.row_tiles, a.batch, stream);
+  p.sel = a.sel;
+  p.sel_stride = a.sel_stride;
+  if (a.sel) {
+    if (a.c.kv_shared) return launch5_rg<true, true>(p, a.plan.row_tiles, a.batch, stream);
+    return launch5_rg<false, true>(p, a.plan.row_tiles, a.batch, stream);
+  }
+  if (a.c.kv_shared) return launch5_rg<true, false>(p, a.plan.row_tiles, a.batch, stream);
+  return launch5_rg<false, false>(p, a.plan.row_tiles, a.batch, stream);
 }
 
 }  // namespace kvq

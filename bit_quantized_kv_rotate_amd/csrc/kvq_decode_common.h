@@ -49,6 +49,11 @@ struct DecodeParams {
   const int32_t* shared_lens;
   int rows_seq;
   int keep_partials;  // always leave split partials (a later merge combines them)
+  // Selected-position decode (latent kernel): the scan runs over the list
+  // sel[b * sel_stride + j], j < context_lens[b], of token positions instead
+  // of over the positions themselves.
+  const int32_t* sel;
+  int sel_stride;
 };
 
 template <int FMT>

@@ -78,6 +78,10 @@ struct DecodeArgs {
   int rows_seq = 0;                      // prefix level: rows per member sequence
   int grp_seqs = 0;                      // prefix level: sequences (partials are stored per sequence)
   int keep_partials = 0;                 // leave split partials, launch no merge
+  // selected-position decode (latent kernel): context_lens then holds the
+  // list lengths
+  const int32_t* sel = nullptr;          // [batch][sel_stride] token positions
+  int sel_stride = 0;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

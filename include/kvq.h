@@ -253,6 +253,42 @@ int kvq_decode_attn_fp4_shared(const kvq_cache_desc *desc, const void *q,
                                const kvq_prefix_groups *groups, float sm_scale,
                                uint32_t flags, float *out, void *workspace,
                                size_t workspace_bytes, kvq_stream_t stream);
+/* Decode attention over selected history positions of a latent-width FP4
+ * cache.  The page "GLM-5.3-Flash in MXFP4: A Lighter, Faster Checkpoint for
+ * AMD MI355X", section "How the serving path works" ("Sparse attention and
+ * K-pool selection"), has a separate index choose the history each token
+ * attends to (pooled four-token groups plus a few recent tokens, 2,051
+ * positions at most); building that index is the caller's.  This call
+ * attends over the chosen positions of the 512-wide latent cache only.
+ *   q             bf16 [batch][1][num_q_heads][head_dim]: one query position
+ *                 per sequence (its heads share the selection)
+ *   block_tables  int32 [batch][max_pages_per_seq]
+ *   sel           int32 [batch][max_selected] (device): sel[b][j] for
+ *                 j < sel_lens[b] are token positions of sequence b, each a
+ *                 written slot of its pages; any order; a position listed
+ *                 twice counts twice
+ *   sel_lens      int32 [batch] (device), 0 <= sel_lens[b] <= max_selected
+ *   max_selected  host-side row length of sel (sizes the grid), >= 0
+ *   out           fp32 [batch][1][num_q_heads][head_dim]; a sequence with no
+ *                 selected position gets zeros
+ *   other arguments as for kvq_decode_attn_fp4; rows per KV head
+ *   (num_q_heads / num_kv_heads) at most 64
+ * Returns KVQ_OK, or KVQ_ERR_NULL / SHAPE / FORMAT (cache is not FP4) /
+ * UNSUPPORTED (head_dim other than 512, more than 64 rows) / WORKSPACE / HIP. */
+int kvq_decode_attn_fp4_selected(const kvq_cache_desc *desc, const void *q,
+                                 int32_t batch, int32_t num_q_heads,
+                                 const int32_t *block_tables,
+                                 int32_t max_pages_per_seq,
+                                 const int32_t *sel, const int32_t *sel_lens,
+                                 int32_t max_selected, float sm_scale,
+                                 uint32_t flags, float *out, void *workspace,
+                                 size_t workspace_bytes, kvq_stream_t stream);
+/* Workspace bytes of a selected-position decode with these sizes (0 when
+ * they are invalid or unsupported); the rules of kvq_decode_workspace_bytes. */
+size_t kvq_decode_selected_workspace_bytes(const kvq_cache_desc *desc,
+                                           int32_t batch, int32_t num_q_heads,
+                                           int32_t max_selected,
+                                           uint32_t flags);
 /* Dequantise n slots (for tests and export): fp32 [n][num_kv_heads][head_dim]
  * of code value * 2^(scale - 127), in the stored (rotated) basis.  v_out is
  * ignored (may be NULL) when kv_shared.  Slots must be in range.

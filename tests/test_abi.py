@@ -227,3 +227,38 @@ def test_shared_argument_errors():
     assert _shared(wsb=need - 1) == -5
     assert _shared(ws=0x58, wsb=need) == -5
     assert _shared(B=0) == 0                     # empty batch: nothing enqueued
+
+
+def _selected(desc=None, q=0x10, B=4, hq=64, bt=0x20, maxp=64, sel=0x30, sel_lens=0x38, max_sel=2051, sm=0.1,
+              flags=0, out=0x40, ws=0x50, wsb=1 << 34):
+    desc = _desc(d=512, hkv=1, p=64, shared=1) if desc is None else desc
+    return kvq.library().kvq_decode_attn_fp4_selected(ctypes.byref(desc), q, B, hq, bt, maxp, sel, sel_lens, max_sel,
+                                                      sm, flags, out, ws, wsb, None)
+
+
+def test_selected_workspace_and_argument_errors():
+    L = kvq.library()
+    d512 = _desc(d=512, hkv=1, p=64, shared=1)
+    need = L.kvq_decode_selected_workspace_bytes(ctypes.byref(d512), 4, 64, 2051, 0)
+    assert need > 0
+    # the same plan as a one-position decode over a context of max_selected tokens
+    assert need == L.kvq_decode_workspace_bytes(ctypes.byref(d512), 4, 64, 1, 2051, 0)
+    assert L.kvq_decode_selected_workspace_bytes(ctypes.byref(_desc()), 4, 64, 2051, 0) == 0      # head_dim 128
+    assert L.kvq_decode_selected_workspace_bytes(ctypes.byref(d512), 4, 65, 2051, 0) == 0         # 65 rows
+    assert L.kvq_decode_selected_workspace_bytes(ctypes.byref(d512), 4, 64, -1, 0) == 0
+    assert L.kvq_decode_selected_workspace_bytes(ctypes.byref(d512), 4, 64, 0, 0) > 0
+    assert _selected(q=None) == -1
+    assert _selected(bt=None) == -1
+    assert _selected(sel=None) == -1
+    assert _selected(sel_lens=None) == -1
+    assert _selected(out=None) == -1
+    assert _selected(max_sel=-1) == -2
+    assert _selected(sm=float("inf")) == -2
+    assert _selected(flags=0x10) == -2
+    assert _selected(desc=_desc(fmt=2, d=512, hkv=1, p=64, shared=1)) == -3
+    assert _selected(desc=_desc(d=128)) == -4
+    assert _selected(hq=65) == -4
+    assert _selected(ws=None, wsb=0) == -5
+    assert _selected(wsb=need - 1) == -5
+    assert _selected(ws=0x58, wsb=need) == -5
+    assert _selected(B=0) == 0

@@ -34,7 +34,7 @@
 //    transposed with ds_read_b64_tr_b16 as the B operand of PV; P is split
 //    into bf16 hi + lo (8 rows each in the 16 MFMA rows).  fp32 accumulation.
 //  * Online softmax in base 2 with lane-swap reductions; the O rescale runs
-//    only when a row maximum moves.
+//    only when a row's maximum passes its lagging reference (kLazyLog2).
 //  * Codes are prefetched through a ring of kRing tile pairs held in
 //    registers; refills are unconditional (clamped to the last tile) so the
 //    memory wait counts stay exact.
@@ -53,8 +53,8 @@ constexpr int kQTerms = 4;           // FP6 (E2M3) terms of the pre-scaled query
 constexpr int kQMfma = kQTerms / 2;  // scaled MFMAs per tile and row tile
 constexpr int kVRow = 2 * kD + 32;   // LDS bytes per token row of V (bf16, padded)
 // tile pairs held in registers per wave: two, except one at 16 rows, where
-// that keeps two waves per SIMD (at 24 rows one wave fits either way, and the
-// deeper ring wins)
+// that keeps two waves per SIMD (at 24 rows, which only the FP8 cache runs
+// here, one wave fits either way, and the deeper ring wins)
 template <int NT>
 struct Ring {
   static constexpr int kN = NT == 2 ? 1 : 2;
@@ -653,7 +653,10 @@ int plan_decode(const CacheGeom& c, int batch, int hq, int n_q, int max_context_
   if (c.d != kD) return KVQ_ERR_UNSUPPORTED;
   const int group = hq / c.hkv;
   const long long rows_ll = (long long)group * n_q;
-  if (rows_ll > 24) {
+  // FP4 above 16 rows: the many-row kernel (32-row blocks of 2 waves, each
+  // wave 16 full rows per MFMA tile) needs about half the VALU work per score
+  // of one wave holding 24 rows in 8-row tiles (agentic mix 0.58 -> 0.51 ms)
+  if (rows_ll > 24 || (rows_ll > 16 && c.fmt == KVQ_FMT_FP4_E2M1)) {
     plan->kind = kDecodeMany;
     return plan_extend(c, batch, hq, n_q, max_context_len, flags, plan);
   }

@@ -1,6 +1,6 @@
 // Attention of many query rows per KV head over the FP4 cache, head_dim 128:
 // prefill / extend chunks (n_q new tokens already appended, position j of the
-// chunk sees tokens 0 .. L - n_q + j) and decode shapes with more than 24 rows
+// chunk sees tokens 0 .. L - n_q + j) and decode shapes with more than 16 rows
 // per KV head (wide query groups x MTP positions).
 //
 // Method: ROCm blog "UltraQuant on AMD Instinct", section "What is
@@ -26,9 +26,12 @@ namespace {
 
 constexpr int kDX = 128;
 constexpr int kTX = 4;                // FP6 query terms
-constexpr int kWX = 8;                // waves per block
-constexpr int kRowsX = 16 * kWX;      // rows per block
-static_assert(kRowsX == kExtendRowBlock, "row block of the many-row kernel");
+// Waves per block: 8 (128 rows) for hundreds of rows per KV head, 2 (32
+// rows) for a few dozen, where a 128-row block would mostly hold padding.
+constexpr int kWideX = 8;
+constexpr int kNarrowX = 2;
+constexpr int kNarrowMaxRows = 64;    // plain calls up to this many rows use 2-wave blocks
+static_assert(16 * kWideX == kExtendRowBlock, "row block of the many-row kernel");
 constexpr int kVRowX = 2 * kDX + 32;  // LDS bytes per bf16 token row (padded)
 constexpr int kRingX = 2;             // tile pairs in flight per staging wave
 
@@ -131,8 +134,10 @@ __device__ __forceinline__ void load_stage(const DecodeParams& p, const int32_t*
 // GRP: prefix level of a shared-prefix decode (units are prefix groups; see
 // DecodeParams); otherwise units are sequences, optionally scanned from
 // p.tok_start[b] on.
-template <bool GRP>
-__global__ __launch_bounds__(512) void extend_kernel(const DecodeParams p) {
+template <bool GRP, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void extend_kernel(const DecodeParams p) {
+  constexpr int kRowsX = 16 * WAVES;                // rows per block
+  constexpr int kJobs = WAVES >= 4 ? 1 : 4 / WAVES;  // staging jobs per staging wave
   __shared__ __attribute__((aligned(16))) u32x4_t s_k[2][2][64];
   __shared__ uint32_t s_ks[2][2][64];
   __shared__ __attribute__((aligned(16))) uint8_t s_v[2][2][16][kVRowX];
@@ -199,14 +204,16 @@ __global__ __launch_bounds__(512) void extend_kernel(const DecodeParams p) {
   const int n_pairs = (t_end - t_begin + 1) >> 1;
   const int n_iter = (n_pairs + kRingX - 1) / kRingX;  // pairs padded to a multiple of kRingX
 
-  // staging role: waves 0..3 stage K tile 0, K tile 1, V tile 0, V tile 1
+  // staging jobs j = 0..3: K tile 0, K tile 1, V tile 0, V tile 1; wave w
+  // takes jobs w + WAVES jj (jj < kJobs), so waves 0..3 of a wide block take
+  // one each and both waves of a narrow block take two
   const bool stager = w < 4;
-  const int st_tile = w & 1;
-  const bool st_v = (w >> 1) & 1;
-  auto fetch = [&](int pi, Stage& c) {
-    load_stage(p, bt_row, kvh, min(t_begin + 2 * pi + st_tile, t_end - 1), st_v, lane, c);
+  auto fetch = [&](int pi, int j, Stage& c) {
+    load_stage(p, bt_row, kvh, min(t_begin + 2 * pi + (j & 1), t_end - 1), j >= 2, lane, c);
   };
-  auto stage = [&](int pi, const Stage& c) {
+  auto stage = [&](int pi, int j, const Stage& c) {
+    const int st_tile = j & 1;
+    const bool st_v = j >= 2;
     const int par = pi & 1;
     if (!st_v) {
       s_k[par][st_tile][lane] = u32x4_t{c.c[0], c.c[1], c.c[2], c.c[3]};
@@ -226,10 +233,12 @@ __global__ __launch_bounds__(512) void extend_kernel(const DecodeParams p) {
     }
   };
 
-  Stage ring[kRingX];
+  Stage ring[kJobs][kRingX];
   if (stager) {
 #pragma unroll
-    for (int k = 0; k < kRingX; ++k) fetch(k, ring[k]);
+    for (int jj = 0; jj < kJobs; ++jj)
+#pragma unroll
+      for (int k = 0; k < kRingX; ++k) fetch(k, w + WAVES * jj, ring[jj][k]);
   }
 
   // this wave's 16 rows: query operands (four terms, one per MFMA)
@@ -275,8 +284,11 @@ __global__ __launch_bounds__(512) void extend_kernel(const DecodeParams p) {
   }
 
   if (stager) {
-    stage(0, ring[0]);
-    fetch(kRingX, ring[0]);
+#pragma unroll
+    for (int jj = 0; jj < kJobs; ++jj) {
+      stage(0, w + WAVES * jj, ring[jj][0]);
+      fetch(kRingX, w + WAVES * jj, ring[jj][0]);
+    }
   }
   __syncthreads();
 
@@ -291,8 +303,11 @@ __global__ __launch_bounds__(512) void extend_kernel(const DecodeParams p) {
       // previous barrier), refill the ring slot
       if (stager) {
         const int nk = (k + 1) % kRingX;
-        stage(pi + 1, ring[nk]);
-        fetch(pi + 1 + kRingX, ring[nk]);
+#pragma unroll
+        for (int jj = 0; jj < kJobs; ++jj) {
+          stage(pi + 1, w + WAVES * jj, ring[jj][nk]);
+          fetch(pi + 1 + kRingX, w + WAVES * jj, ring[jj][nk]);
+        }
       }
       if (tile * 16 <= wave_lim) {
         // ---- scores of the wave's 16 rows (past the last pair every score is
@@ -433,10 +448,11 @@ __global__ __launch_bounds__(512) void extend_kernel(const DecodeParams p) {
 
 constexpr int kMinTilesPerSplitX = 8;
 constexpr int kMaxTilesPerSplitX = 512;
-constexpr int kDefaultSlotsX = 256;  // one block per CU
+constexpr int kDefaultSlotsX = 256;  // wide blocks: one per CU (MI355X); narrow: four
 constexpr int kMaxDevicesX = 64;
 constexpr int kMaxRowsX = 1 << 16;
 
+template <int WAVES>
 int resident_blocks_x() {
   static std::atomic<int> cache[kMaxDevicesX];
   int dev = 0;
@@ -450,7 +466,7 @@ int resident_blocks_x() {
   }
   int cus = 0, blocks = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, extend_kernel<false>, 64 * kWX, 0) != hipSuccess) {
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, extend_kernel<false, WAVES>, 64 * WAVES, 0) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
@@ -467,17 +483,20 @@ int plan_extend(const CacheGeom& c, int batch, int hq, int n_q, int max_context_
 }
 
 int plan_extend_rows(const CacheGeom& c, int batch, long long rows, int max_context_len, uint32_t flags,
-                     DecodePlan* plan) {
+                     DecodePlan* plan, int block_rows) {
   if (c.d != kDX || c.fmt != KVQ_FMT_FP4_E2M1) return KVQ_ERR_UNSUPPORTED;
   if (rows < 1 || rows > kMaxRowsX) return KVQ_ERR_UNSUPPORTED;
+  if (block_rows == 0) block_rows = rows <= kNarrowMaxRows ? 16 * kNarrowX : 16 * kWideX;
+  if (block_rows != 16 * kNarrowX && block_rows != 16 * kWideX) return KVQ_ERR_UNSUPPORTED;
+  const int kRowsX = block_rows;
   const int row_blocks = (int)((rows + kRowsX - 1) / kRowsX);
   const int n_tiles = (max_context_len + 15) / 16;
   int splits = (int)((flags & KVQ_SPLITS_MASK) >> KVQ_SPLITS_SHIFT);
   if (splits <= 0) {
     // one round of blocks over the device, at least kMinTilesPerSplitX tiles
     // and at most kMaxTilesPerSplitX per split
-    int slots = resident_blocks_x();
-    if (slots <= 0) slots = kDefaultSlotsX;
+    int slots = block_rows == 16 * kNarrowX ? resident_blocks_x<kNarrowX>() : resident_blocks_x<kWideX>();
+    if (slots <= 0) slots = block_rows == 16 * kNarrowX ? 4 * kDefaultSlotsX : kDefaultSlotsX;
     const long long work = (long long)batch * c.hkv * row_blocks;
     long long want = work >= slots ? 1 : slots / work;
     const long long by_len = n_tiles / kMinTilesPerSplitX;
@@ -495,6 +514,7 @@ int plan_extend_rows(const CacheGeom& c, int batch, long long rows, int max_cont
   const size_t rows_pad = (size_t)row_blocks * kRowsX;
   plan->rows = (int)rows;
   plan->row_tiles = row_blocks;
+  plan->block_rows = block_rows;
   plan->splits = splits;
   plan->tiles_per_split = per;
   plan->qops_bytes = (size_t)batch * c.hkv * (rows_pad / 16) * kTX * 64 * 8 * sizeof(uint32_t);
@@ -521,7 +541,7 @@ hipError_t launch_extend(const DecodeArgs& a, hipStream_t stream) {
   p.n_q = a.n_q;
   p.group = a.group;
   p.rows = a.plan.rows;
-  p.rows_pad = a.plan.row_tiles * kRowsX;
+  p.rows_pad = a.plan.row_tiles * a.plan.block_rows;
   p.block_tables = a.block_tables;
   p.max_pages = a.max_pages;
   p.context_lens = a.context_lens;
@@ -552,10 +572,15 @@ hipError_t launch_extend(const DecodeArgs& a, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((size_t)p.splits * units * a.plan.row_tiles));
-  if (grp)
-    hipLaunchKernelGGL(extend_kernel<true>, grid, dim3(64 * kWX), 0, stream, p);
+  const bool narrow = a.plan.block_rows == 16 * kNarrowX;
+  if (grp && narrow)
+    hipLaunchKernelGGL((extend_kernel<true, kNarrowX>), grid, dim3(64 * kNarrowX), 0, stream, p);
+  else if (grp)
+    hipLaunchKernelGGL((extend_kernel<true, kWideX>), grid, dim3(64 * kWideX), 0, stream, p);
+  else if (narrow)
+    hipLaunchKernelGGL((extend_kernel<false, kNarrowX>), grid, dim3(64 * kNarrowX), 0, stream, p);
   else
-    hipLaunchKernelGGL(extend_kernel<false>, grid, dim3(64 * kWX), 0, stream, p);
+    hipLaunchKernelGGL((extend_kernel<false, kWideX>), grid, dim3(64 * kWideX), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess || a.keep_partials) return e;
   hipLaunchKernelGGL((merge_kernel<0, 2>), dim3(qblocks), dim3(256), 0, stream, p);

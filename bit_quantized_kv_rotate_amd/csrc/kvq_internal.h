@@ -51,6 +51,7 @@ struct DecodePlan {
   int tiles_per_split;   // 16-token tiles per split (even)
   size_t qops_bytes;     // query operands (first part of the workspace)
   size_t workspace;      // bytes
+  int block_rows = 0;    // many-row kernel: rows per block (16 per wave)
 };
 
 // Decide split count and workspace size; returns KVQ_OK or an error code.
@@ -87,7 +88,7 @@ struct DecodeArgs {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
 // which decode kernel family a plan uses
-constexpr int kDecodeFew = 0;     // head_dim 128, up to 24 rows per KV head (kvq_decode.hip)
+constexpr int kDecodeFew = 0;     // head_dim 128, up to 16 rows per KV head (FP8: 24) (kvq_decode.hip)
 constexpr int kDecodeMany = 1;    // head_dim 128, more rows (kvq_extend.hip)
 constexpr int kDecodeLatent = 2;  // head_dim 512 (kvq_decode512.hip)
 
@@ -95,11 +96,12 @@ constexpr int kDecodeLatent = 2;  // head_dim 512 (kvq_decode512.hip)
 int plan_extend(const CacheGeom& c, int batch, int hq, int n_q, int max_context_len, uint32_t flags,
                 DecodePlan* plan);
 // the same plan for `units` (sequence or prefix group) x num_kv_heads units of
-// `rows` rows each
+// `rows` rows each, in blocks of `block_rows` rows (32 or 128; 0: by the row
+// count)
 int plan_extend_rows(const CacheGeom& c, int units, long long rows, int max_context_len, uint32_t flags,
-                     DecodePlan* plan);
+                     DecodePlan* plan, int block_rows = 0);
 hipError_t launch_extend(const DecodeArgs& a, hipStream_t stream);
-constexpr int kExtendRowBlock = 128;   // rows per many-row block (padding unit of its rows)
+constexpr int kExtendRowBlock = 128;   // rows per wide many-row block
 
 // shared-prefix decode, head_dim 128 FP4: kvq_shared.hip
 struct SharedPlan {

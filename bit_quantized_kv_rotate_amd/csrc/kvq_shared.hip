@@ -176,7 +176,7 @@ hipError_t launch_shared(const SharedArgs& a, hipStream_t stream) {
   const size_t n_o1 = (size_t)a.base.batch * a.base.c.hkv * sp.prefix.splits * rows_seq * kDS;
   m.o1 = reinterpret_cast<const float*>(ws + sp.prefix.qops_bytes);
   m.ml1 = m.o1 + n_o1;
-  const int rows2 = sp.suffix.kind == kDecodeMany ? sp.suffix.row_tiles * kExtendRowBlock : 8 * sp.suffix.row_tiles;
+  const int rows2 = sp.suffix.kind == kDecodeMany ? sp.suffix.row_tiles * sp.suffix.block_rows : 8 * sp.suffix.row_tiles;
   const size_t n_o2 = (size_t)a.base.batch * a.base.c.hkv * sp.suffix.splits * rows2 * kDS;
   m.o2 = reinterpret_cast<const float*>(ws + sp.suffix_offset + sp.suffix.qops_bytes);
   m.ml2 = m.o2 + n_o2;

@@ -149,8 +149,8 @@ size_t kvq_decode_workspace_bytes(const kvq_cache_desc *desc, int32_t batch,
  *   num_q_heads     multiple of num_kv_heads; query head h reads KV head
  *                   h / (num_q_heads / num_kv_heads).  Rows per KV head =
  *                   n_q * num_q_heads / num_kv_heads: up to 65536 at
- *                   head_dim 128 (more than 24 rows run the many-row kernel
- *                   meant for prefill / extend chunks), up to 64 at
+ *                   head_dim 128 (more than 16 rows run the many-row kernel
+ *                   also meant for prefill / extend chunks), up to 64 at
  *                   head_dim 512; other head_dims: KVQ_ERR_UNSUPPORTED
  *   n_q             query positions per sequence (MTP verify: > 1); the last
  *                   n_q cached tokens are the verify tokens and position j

@@ -195,7 +195,7 @@ def test_decode_latent_512_split_invariance(gpu):
     (4, 130, (300, 2000)),    # 520 rows: a padded last row block
 ])
 def test_decode_many_rows(gpu, group, n_q, ctx):
-    """More than 24 rows per KV head: the many-row (extend / prefill) kernel,
+    """More than 16 rows per KV head: the many-row (extend / prefill) kernel,
     with the causal rule between chunk positions."""
     wl = syn.Workload("many_g%d_nq%d" % (group, n_q), batch=3, num_kv_heads=2, num_q_heads=2 * group,
                       head_dim=128, page_size=16, context=0, n_q=n_q, ctx_range=ctx)

@@ -27,7 +27,7 @@ constexpr int kMaxLevelSplits = kMaxSplits / 2;  // both levels share one wave's
 // and suffix lengths are ragged, and only their maxima are known here: short
 // splits keep the longest ones from setting the time of the call (a split
 // with no tile of its sequence leaves at once).
-constexpr int kPrefixTilesPerSplit = 128;
+constexpr int kPrefixTilesPerSplit = 256;
 constexpr int kSuffixTilesPerSplit = 32;
 
 struct MergeParams {
@@ -125,7 +125,10 @@ int plan_shared(const CacheGeom& c, int batch, int hq, int n_q, const kvq_prefix
   const long long pre_rows = rows_seq * g.max_group_size;
   const int prefix_len = g.max_prefix_pages * c.p;
   int st = plan_level(
-      [&](uint32_t f, DecodePlan* p) { return plan_extend_rows(c, g.num_groups, pre_rows, prefix_len, f, p); },
+      // 32-row blocks: a block holds about one member's rows, so it scans
+      // little beyond that member's shared length (members of one group may
+      // share prefixes of very different lengths)
+      [&](uint32_t f, DecodePlan* p) { return plan_extend_rows(c, g.num_groups, pre_rows, prefix_len, f, p, 32); },
       flags, (prefix_len + 15) / 16, kPrefixTilesPerSplit, &plan->prefix);
   if (st != KVQ_OK) return st;
   plan->prefix.kind = kDecodeMany;

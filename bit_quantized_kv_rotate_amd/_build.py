@@ -25,16 +25,19 @@ COMMON = [
 ]
 
 # per-file extra flags: the write path must round every fp32 op on its own
+# Decode kernels: -fno-honor-nans, because they produce no NaN (masks use
+# -inf, every inf - inf is guarded) and without NaN semantics an fmaxf of an
+# MFMA result needs no canonicalising v_max first.
 SOURCES = {
     "kvq_api.hip": [],
     "kvq_append.hip": ["-ffp-contract=off"],
     # keep MFMA accumulators in VGPRs: the softmax rescale touches them with
     # VALU ops, and AGPR placement costs a copy per access
-    "kvq_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "kvq_decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
     # head_dim 512: the accumulators need the AGPR half of the register file
-    "kvq_decode512.hip": [],
-    "kvq_extend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-    "kvq_shared.hip": [],
+    "kvq_decode512.hip": ["-fno-honor-nans"],
+    "kvq_extend.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans"],
+    "kvq_shared.hip": ["-fno-honor-nans"],
 }
 
 

@@ -324,14 +324,14 @@ __global__ __launch_bounds__(64 * WAVES) void extend_kernel(const DecodeParams p
             acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, qb[t], acc, 4, 2, 0, ksc, 0, qs[t]);
           S[s] = acc;
         }
+        // score (s, i) is token tile * 16 + 16 s + 4 quad + i: visible while
+        // 16 s + i <= rel
+        const int rel = row_lim - tile * 16 - 4 * quad;
         float sc[8];
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int tok = (tile + s) * 16 + 4 * quad + i;
-            sc[4 * s + i] = (tok <= row_lim) ? S[s][i] : -INFINITY;
-          }
+          for (int i = 0; i < 4; ++i) sc[4 * s + i] = (16 * s + i <= rel) ? S[s][i] : -INFINITY;
         float mloc = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                            fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
         mloc = quad_max(mloc);

@@ -52,6 +52,18 @@ def test_decode_query_groups_and_mtp(gpu, group, n_q):
         assert_close(out[b], want[b], "g%d n_q%d seq %d" % (group, n_q, b))
 
 
+@pytest.mark.parametrize("group,n_q", [(16, 1), (8, 3), (2, 5), (4, 3)])
+def test_decode_fp8_query_groups_and_mtp(gpu, group, n_q):
+    """The FP8 comparator keeps the one-wave kernel up to 24 rows (two and
+    three 8-row tiles), which FP4 leaves above 16 rows."""
+    wl = syn.Workload("fp8_grp%d_nq%d" % (group, n_q), batch=3, num_kv_heads=2, num_q_heads=2 * group,
+                      head_dim=128, page_size=16, context=0, n_q=n_q, ctx_range=(40, 700))
+    f, qh, out = _run(wl, "fp8")
+    want = oracle_decode_batch(f, qh)
+    for b in range(wl.batch):
+        assert_close(out[b], want[b], "fp8 g%d n_q%d seq %d" % (group, n_q, b))
+
+
 def test_decode_ragged_contexts(gpu):
     """Contexts that end anywhere inside a tile, tile pair or page, and a
     single token."""

@@ -96,6 +96,8 @@ SIGNATURES = {
                                            ctypes.c_float, _U32, _P, _P, _SZ, _P]),
     "kvq_decode_attn_fp8": (ctypes.c_int, [_DESC, _P, _I32, _I32, _I32, _P, _I32, _P, _I32,
                                            ctypes.c_float, _U32, _P, _P, _SZ, _P]),
+    "kvq_append_decode_attn_fp4": (ctypes.c_int, [_DESC, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _P, _I32, _P,
+                                                  _I32, ctypes.c_float, _U32, _P, _P, _SZ, _P]),
     "kvq_decode_shared_workspace_bytes": (_SZ, [_DESC, _I32, _I32, _I32, _GROUPS, _U32]),
     "kvq_decode_attn_fp4_shared": (ctypes.c_int, [_DESC, _P, _I32, _I32, _I32, _P, _I32, _P, _GROUPS,
                                                   ctypes.c_float, _U32, _P, _P, _SZ, _P]),
@@ -264,6 +266,52 @@ def decode_attn_fp4(cache: KVCache, q: torch.Tensor, block_tables: torch.Tensor,
     """q: bf16 [batch, n_q, num_q_heads, head_dim]; returns fp32 of that shape."""
     return _decode("kvq_decode_attn_fp4", cache, q, block_tables, context_lens, max_context_len,
                    sm_scale, flags, out, workspace, stream)
+
+
+def append_decode_attn_fp4(cache: KVCache, k_new: torch.Tensor, v_new: Optional[torch.Tensor],
+                           slot_mapping: torch.Tensor, q: torch.Tensor, block_tables: torch.Tensor,
+                           context_lens: torch.Tensor, max_context_len: int,
+                           sm_scale: Optional[float] = None, flags: int = 0,
+                           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """rotate_quantize_append(cache, k_new, v_new, slot_mapping) followed by
+    decode_attn_fp4(cache, q, ...), in one call."""
+    n = int(slot_mapping.shape[0])
+    kp = vp = sp = None
+    if n:
+        shp = (n, cache.num_kv_heads, cache.head_dim)
+        _shape(k_new, shp, "k_new")
+        kp = _dev(k_new, torch.bfloat16, "k_new")
+        if not cache.kv_shared:
+            _shape(v_new, shp, "v_new")
+            vp = _dev(v_new, torch.bfloat16, "v_new")
+        sp = _dev(slot_mapping, torch.int32, "slot_mapping")
+    B, n_q, hq, d = (int(x) for x in q.shape)
+    if d != cache.head_dim:
+        raise ValueError("q head_dim %d does not match the cache (%d)" % (d, cache.head_dim))
+    qp = _dev(q, torch.bfloat16, "q")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [batch, max_pages]")
+    bp = _dev(block_tables, torch.int32, "block_tables")
+    _shape(context_lens, (B,), "context_lens")
+    cp = _dev(context_lens, torch.int32, "context_lens")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty((B, n_q, hq, d), dtype=torch.float32, device=q.device)
+    _shape(out, (B, n_q, hq, d), "out")
+    op = _dev(out, torch.float32, "out")
+    need = decode_workspace_bytes(cache, B, hq, n_q, int(max_context_len), flags)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wp, wbytes = None, 0
+    if workspace is not None:
+        wp = _dev(workspace, workspace.dtype, "workspace")
+        wbytes = workspace.numel() * workspace.element_size()
+    _check(library().kvq_append_decode_attn_fp4(cache.ref(), kp, vp, sp, n, qp, B, hq, n_q, bp,
+                                                 int(block_tables.shape[1]), cp, int(max_context_len),
+                                                 float(sm_scale), int(flags), op, wp, wbytes, _stream(stream)))
+    return out
 
 
 def decode_attn_fp8(cache: KVCache, q: torch.Tensor, block_tables: torch.Tensor,

@@ -67,7 +67,7 @@ int decode_common(int want_fmt, const kvq_cache_desc* desc, const void* q, int32
                   int32_t num_q_heads, int32_t n_q, const int32_t* block_tables,
                   int32_t max_pages_per_seq, const int32_t* context_lens, int32_t max_context_len,
                   float sm_scale, uint32_t flags, float* out, void* workspace,
-                  size_t workspace_bytes, kvq_stream_t stream) {
+                  size_t workspace_bytes, kvq_stream_t stream, const AppendArgs* append = nullptr) {
   CacheGeom g;
   int st = check_desc(desc, &g);
   if (st != KVQ_OK) return st;
@@ -81,9 +81,12 @@ int decode_common(int want_fmt, const kvq_cache_desc* desc, const void* q, int32
   if ((int64_t)max_pages_per_seq * g.p < (int64_t)max_context_len) return KVQ_ERR_SHAPE;
   if (!std::isfinite(sm_scale)) return KVQ_ERR_SHAPE;
   if (flags & ~(KVQ_Q_PREROTATED | KVQ_OUT_ROTATED | KVQ_SPLITS_MASK)) return KVQ_ERR_SHAPE;
-  if (batch == 0 || max_context_len == 0) {
-    // Nothing to attend to: every position sees no token and gets zeros.
-    if (batch == 0) return KVQ_OK;
+  if (batch == 0) {
+    // nothing to attend to; an append still runs
+    if (append && append->n_tokens > 0)
+      return hip_status(launch_append(g, append->kc, append->ks, append->vc, append->vs, append->k_new,
+                                      append->v_new, append->slots, append->n_tokens, (hipStream_t)stream));
+    return KVQ_OK;
   }
   DecodePlan plan;
   st = plan_decode(g, batch, num_q_heads, n_q, max_context_len > 0 ? max_context_len : 1, flags, &plan);
@@ -106,6 +109,7 @@ int decode_common(int want_fmt, const kvq_cache_desc* desc, const void* q, int32
   a.rotate_out = g.rotate && !(flags & KVQ_OUT_ROTATED);
   a.out = out;
   a.workspace = (float*)workspace;
+  a.append = append;
   return hip_status(launch_decode(a, (hipStream_t)stream));
 }
 
@@ -277,6 +281,28 @@ int kvq_decode_attn_fp4_selected(const kvq_cache_desc* desc, const void* q, int3
   a.sel = sel;
   a.sel_stride = max_selected > 0 ? max_selected : 1;
   return hip_status(launch_decode(a, (hipStream_t)stream));
+}
+
+int kvq_append_decode_attn_fp4(const kvq_cache_desc* desc, const void* k_new, const void* v_new,
+                               const int32_t* slot_mapping, int32_t n_tokens, const void* q, int32_t batch,
+                               int32_t num_q_heads, int32_t n_q, const int32_t* block_tables,
+                               int32_t max_pages_per_seq, const int32_t* context_lens, int32_t max_context_len,
+                               float sm_scale, uint32_t flags, float* out, void* workspace,
+                               size_t workspace_bytes, kvq_stream_t stream) {
+  CacheGeom g;
+  const int st = check_desc(desc, &g);
+  if (st != KVQ_OK) return st;
+  if (n_tokens < 0) return KVQ_ERR_SHAPE;
+  if (n_tokens > 0) {
+    if (!k_new || !slot_mapping) return KVQ_ERR_NULL;
+    if (!g.kv_shared && !v_new) return KVQ_ERR_NULL;
+  }
+  const AppendArgs ap{(uint8_t*)desc->k_codes, (uint8_t*)desc->k_scales, (uint8_t*)desc->v_codes,
+                      (uint8_t*)desc->v_scales, (const uint16_t*)k_new, (const uint16_t*)v_new, slot_mapping,
+                      n_tokens};
+  return decode_common(KVQ_FMT_FP4_E2M1, desc, q, batch, num_q_heads, n_q, block_tables, max_pages_per_seq,
+                       context_lens, max_context_len, sm_scale, flags, out, workspace, workspace_bytes, stream,
+                       &ap);
 }
 
 int kvq_decode_attn_fp4(const kvq_cache_desc* desc, const void* q, int32_t batch,

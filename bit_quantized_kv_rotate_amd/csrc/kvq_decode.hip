@@ -43,6 +43,7 @@
 //    the split count that fills the device's resident wave slots once.
 #include <atomic>
 
+#include "kvq_append_dev.h"
 #include "kvq_decode_common.h"
 
 namespace kvq {
@@ -328,12 +329,10 @@ __device__ __forceinline__ void compute_pair(const DecodeParams& p, const int32_
 // pairs lane l with lane l ^ (h / 2); every stage is the fp32 add or
 // subtract of the append kernel's transform, in the same order.
 template <int FMT, int NT>
-__global__ __launch_bounds__(256) void qprep_kernel(const DecodeParams p) {
+__device__ __forceinline__ void qprep_row(const DecodeParams& p, int gr, int lane) {
   constexpr int ROWS = 8 * NT;
   constexpr int kS = QOpsLayout<FMT>::kSlots;
   constexpr int kW = QOpsLayout<FMT>::kDwords;
-  const int lane = threadIdx.x & 63;
-  const int gr = blockIdx.x * 4 + (threadIdx.x >> 6);  // grid covers exactly B * hkv * ROWS
   const int r = gr % ROWS;
   const int bh = gr / ROWS;
   const int kvh = bh % p.hkv;
@@ -407,6 +406,31 @@ __global__ __launch_bounds__(256) void qprep_kernel(const DecodeParams p) {
     dst[0] = h0 | (h1 << 16);
     dst[8 * kW] = l0 | (l1 << 16);
   }
+}
+
+template <int FMT, int NT>
+__global__ __launch_bounds__(256) void qprep_kernel(const DecodeParams p) {
+  // grid covers exactly B * hkv * 8 NT rows, four per block
+  qprep_row<FMT, NT>(p, blockIdx.x * 4 + (threadIdx.x >> 6), threadIdx.x & 63);
+}
+
+// The query prologue and the append of the step's new tokens in one launch
+// (head_dim 128, G = 4 groups): blocks below qblocks prepare query rows, the
+// others are append waves, axb blocks per (KV head, tensor).  The page scan,
+// the next launch on the stream, then finds the new tokens in the cache.
+template <int FMT, int NT>
+__global__ __launch_bounds__(256) void qprep_append_kernel(const DecodeParams p, const AppendParams ap,
+                                                           unsigned qblocks, unsigned axb) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  if (blockIdx.x < qblocks) {
+    qprep_row<FMT, NT>(p, blockIdx.x * 4 + wave, lane);
+    return;
+  }
+  const unsigned b2 = blockIdx.x - qblocks;
+  const unsigned ht = b2 / axb;
+  append_wave<kD / 32>(ap, (int)(b2 - ht * axb) * 4 + wave, (int)(ht % (unsigned)ap.c.hkv),
+                       (int)(ht / (unsigned)ap.c.hkv), lane);
 }
 
 template <int FMT, int NT>
@@ -582,10 +606,17 @@ constexpr int kDefaultWaveSlots = 2048;  // MI355X: 256 CUs x 8 resident waves
 constexpr int kMaxDevices = 64;
 
 template <int FMT, int NT>
-hipError_t launch_nt(const DecodeParams& p, int batch, hipStream_t stream) {
+hipError_t launch_nt(const DecodeParams& p, int batch, const AppendParams* ap, hipStream_t stream) {
   // 8 * NT rows per (sequence, KV head), four row-waves per block
   const unsigned qblocks = (unsigned)((size_t)batch * p.hkv * 8 * NT / 4);
-  hipLaunchKernelGGL((qprep_kernel<FMT, NT>), dim3(qblocks), dim3(256), 0, stream, p);
+  if (ap && ap->n_tokens > 0) {
+    const unsigned axb = (unsigned)((append_waves(ap->c, ap->n_tokens) + 3) / 4);
+    const unsigned ablocks = axb * (unsigned)p.hkv * (ap->c.kv_shared ? 1u : 2u);
+    hipLaunchKernelGGL((qprep_append_kernel<FMT, NT>), dim3(qblocks + ablocks), dim3(256), 0, stream, p, *ap,
+                       qblocks, axb);
+  } else {
+    hipLaunchKernelGGL((qprep_kernel<FMT, NT>), dim3(qblocks), dim3(256), 0, stream, p);
+  }
   hipError_t e0 = hipGetLastError();
   if (e0 != hipSuccess) return e0;
   const dim3 grid((unsigned)((size_t)p.splits * p.hkv * batch));
@@ -597,11 +628,11 @@ hipError_t launch_nt(const DecodeParams& p, int batch, hipStream_t stream) {
 }
 
 template <int FMT>
-hipError_t launch_fmt(const DecodeParams& p, int row_tiles, int batch, hipStream_t stream) {
+hipError_t launch_fmt(const DecodeParams& p, int row_tiles, int batch, const AppendParams* ap, hipStream_t stream) {
   switch (row_tiles) {
-    case 1: return launch_nt<FMT, 1>(p, batch, stream);
-    case 2: return launch_nt<FMT, 2>(p, batch, stream);
-    case 3: return launch_nt<FMT, 3>(p, batch, stream);
+    case 1: return launch_nt<FMT, 1>(p, batch, ap, stream);
+    case 2: return launch_nt<FMT, 2>(p, batch, ap, stream);
+    case 3: return launch_nt<FMT, 3>(p, batch, ap, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -704,6 +735,13 @@ int plan_decode(const CacheGeom& c, int batch, int hq, int n_q, int max_context_
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  if (a.append && a.append->n_tokens > 0 && a.plan.kind != kDecodeFew) {
+    // the other kernel families append in a launch of their own first
+    const AppendArgs& ap = *a.append;
+    const hipError_t e = launch_append(a.c, ap.kc, ap.ks, ap.vc, ap.vs, ap.k_new, ap.v_new, ap.slots,
+                                       ap.n_tokens, stream);
+    if (e != hipSuccess) return e;
+  }
   if (a.plan.kind == kDecodeLatent) return launch_decode512(a, stream);
   if (a.plan.kind == kDecodeMany) return launch_extend(a, stream);
   DecodeParams p{};
@@ -740,8 +778,14 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   p.qops = reinterpret_cast<uint32_t*>(ws);
   p.ws_o = reinterpret_cast<float*>(ws + a.plan.qops_bytes);
   p.ws_ml = p.ws_o + n_o;
-  if (a.c.fmt == KVQ_FMT_FP4_E2M1) return launch_fmt<KVQ_FMT_FP4_E2M1>(p, a.plan.row_tiles, a.batch, stream);
-  return launch_fmt<KVQ_FMT_FP8_E4M3>(p, a.plan.row_tiles, a.batch, stream);
+  AppendParams ap;
+  const AppendParams* app = nullptr;
+  if (a.append && a.append->n_tokens > 0) {
+    ap = make_append_params(a.c, *a.append);
+    app = &ap;
+  }
+  if (a.c.fmt == KVQ_FMT_FP4_E2M1) return launch_fmt<KVQ_FMT_FP4_E2M1>(p, a.plan.row_tiles, a.batch, app, stream);
+  return launch_fmt<KVQ_FMT_FP8_E4M3>(p, a.plan.row_tiles, a.batch, app, stream);
 }
 
 }  // namespace kvq

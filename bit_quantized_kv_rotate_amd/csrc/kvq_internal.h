@@ -35,6 +35,19 @@ struct CacheGeom {
 // fp32 rounding of 1/sqrt(d): the single multiply after the butterfly.
 float fwht_norm(int d);
 
+// New tokens to append (rotate, quantise, store) before a decode reads the
+// cache: kvq_rotate_quantize_append's arguments.
+struct AppendArgs {
+  uint8_t* kc;
+  uint8_t* ks;
+  uint8_t* vc;
+  uint8_t* vs;
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  const int32_t* slots;
+  int n_tokens;
+};
+
 hipError_t launch_append(const CacheGeom& c, uint8_t* kc, uint8_t* ks,
                          uint8_t* vc, uint8_t* vs, const uint16_t* k_new,
                          const uint16_t* v_new, const int32_t* slots,
@@ -83,6 +96,9 @@ struct DecodeArgs {
   // list lengths
   const int32_t* sel = nullptr;          // [batch][sel_stride] token positions
   int sel_stride = 0;
+  // tokens to append before the scan reads the cache (null: none); the
+  // one-wave FP4 path appends inside its query prologue launch
+  const AppendArgs* append = nullptr;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);

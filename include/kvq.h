@@ -175,6 +175,26 @@ int kvq_decode_attn_fp4(const kvq_cache_desc *desc, const void *q,
                         void *workspace, size_t workspace_bytes,
                         kvq_stream_t stream);
 
+/* One decode step in one call: kvq_rotate_quantize_append(desc, k_new,
+ * v_new, slot_mapping, n_tokens) followed by kvq_decode_attn_fp4(desc, q,
+ * ...) on the same stream, with identical results (the cache bytes and the
+ * output are the ones the two calls give).  Where the decode runs the
+ * one-wave kernel (head_dim 128, at most 16 rows per KV head) the append
+ * runs inside its first launch, beside the query prologue, which saves a
+ * launch per step; elsewhere it runs first, as its own launch.  Arguments as
+ * for the two calls; the appended tokens must belong to the sequences'
+ * contexts as context_lens states them.  Returns KVQ_OK, or the errors of
+ * either call. */
+int kvq_append_decode_attn_fp4(const kvq_cache_desc *desc, const void *k_new,
+                               const void *v_new, const int32_t *slot_mapping,
+                               int32_t n_tokens, const void *q, int32_t batch,
+                               int32_t num_q_heads, int32_t n_q,
+                               const int32_t *block_tables,
+                               int32_t max_pages_per_seq,
+                               const int32_t *context_lens,
+                               int32_t max_context_len, float sm_scale,
+                               uint32_t flags, float *out, void *workspace,
+                               size_t workspace_bytes, kvq_stream_t stream);
 /* The same decode over an FP8 (E4M3, per-32 UE8M0 scale) cache: the 8-bit
  * comparator of "UltraQuant vs 8-bit KV".  Identical arguments; returns
  * KVQ_ERR_FORMAT unless desc->format == KVQ_FMT_FP8_E4M3, and

@@ -262,3 +262,21 @@ def test_selected_workspace_and_argument_errors():
     assert _selected(wsb=need - 1) == -5
     assert _selected(ws=0x58, wsb=need) == -5
     assert _selected(B=0) == 0
+
+
+def test_append_decode_argument_errors():
+    L = kvq.library()
+    d = _desc()
+    call = lambda desc=d, k=0x60, v=0x68, s=0x70, n=4, q=0x10, B=2, out=0x40, ws=0x50, wsb=1 << 30: \
+        L.kvq_append_decode_attn_fp4(ctypes.byref(desc), k, v, s, n, q, B, 16, 1, 0x20, 8, 0x30, 128, 0.1, 0,
+                                     out, ws, wsb, None)
+    assert call(k=None) == -1
+    assert call(v=None) == -1
+    assert call(s=None) == -1
+    assert call(n=-1) == -2
+    assert call(q=None) == -1
+    assert call(out=None) == -1
+    assert call(desc=_desc(fmt=2)) == -3
+    assert call(ws=None, wsb=0) == -5
+    assert call(n=0, k=None, v=None, s=None, B=0) == 0      # nothing to append or attend
+    assert call(desc=_desc(d=96)) == -2

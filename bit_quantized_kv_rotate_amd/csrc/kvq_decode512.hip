@@ -19,7 +19,9 @@
 //    PV product puts hi and lo of P in the contraction (k = 16 tokens x
 //    {hi, lo}), so one accumulator holds 16 full rows.
 // P (as ready MFMA A operands), the rescale factors and V pass through LDS,
-// double-buffered by tile-pair parity: one barrier per pair.
+// double-buffered by tile-pair parity: one barrier per pair.  From 48 rows
+// on, decode512r_kernel splits the same work by role instead (four waves
+// score, four accumulate), with bitwise the same partials.
 #include <atomic>
 
 #include "kvq_decode_common.h"
@@ -33,6 +35,7 @@ constexpr int kM5 = kT5 / 2;         // scaled MFMAs per 128-channel block (two 
 constexpr int kW5 = 8;               // waves per block
 constexpr int kVRow5 = 2 * kD5 + 32;  // LDS bytes per bf16 token row (padded)
 constexpr int kMaxRG5 = 4;           // 16-row groups (64 rows)
+constexpr int kRoleSplitRG5 = 3;     // from 48 rows on, the role-split kernel
 // tile pairs in flight per wave (one chunk each): three, fewer where the
 // accumulators of 64 rows (and a separate V chunk, or the per-lane addresses
 // of a gathered selection) leave no room
@@ -235,7 +238,6 @@ __global__ __launch_bounds__(512) void decode512_kernel(const DecodeParams p) {
   const bool owner = (NO == kW5) || w < NO;  // every wave owns rows at 64 rows
   const int mtile = w & 1;   // tile of each pair this wave stages
   const int mchunk = w >> 1;  // ... and its 128-channel chunk
-  const int interior_limit = min(tok_limit, L - p.n_q + 1);
 
   // stage pair pi (codes in `c`): K codes and scales for the scores, V as
   // bf16 rows (zero past the context; branch-free)
@@ -444,6 +446,283 @@ __global__ __launch_bounds__(512) void decode512_kernel(const DecodeParams p) {
   }
 }
 
+// Role-split form of the kernel above for 33..64 rows, with the same
+// arithmetic per accumulator (its partials are bitwise those of
+// decode512_kernel).  Waves 0..3 score: wave s owns the 8-row owners 2s and
+// 2s + 1 (QK^T, online softmax, P hi / lo), so each K operand it reads from
+// LDS serves two owners.  Waves 4..7 own the output: wave 4 + v accumulates
+// O for all rows over channels 128v .. 128v + 127 and stages both tiles of
+// chunk v of each pair.  Waves go round-robin onto the four SIMDs, so every
+// SIMD holds one wave of each role: the softmax VALU of one runs beside the
+// PV MFMAs of the other, and the LDS reads per pair drop by a third (K read
+// by four owners' waves instead of eight, P by four output waves).  With
+// fewer rows the score waves' two softmax chains are the longer path and
+// the plain kernel is faster.
+template <int RG, bool SHARED, bool SEL>
+__global__ __launch_bounds__(512) void decode512r_kernel(const DecodeParams p) {
+  constexpr int ROWS = 16 * RG;
+  constexpr int NO = 2 * RG;
+  constexpr int kRing = 1;  // tile pairs in flight per staging wave (a deeper ring spills)
+  __shared__ __attribute__((aligned(16))) u32x4_t s_k[2][2][4][64];
+  __shared__ uint32_t s_ks[2][2][4][64];
+  __shared__ __attribute__((aligned(16))) uint8_t s_v[3][2][16][kVRow5];
+  __shared__ __attribute__((aligned(16))) u32x4_t s_p[2][RG][2][64];
+  __shared__ float s_alpha[2][ROWS];
+  __shared__ int s_flag[2][NO];
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int split = blockIdx.x;
+  const int kvh = blockIdx.y;
+  const int b = blockIdx.z;
+  const int bh = b * p.hkv + kvh;
+  const int L = p.context_lens[b];
+  const int n_tiles = (L + 15) >> 4;
+  const int t_begin = split * p.tiles_per_split;
+  const int t_end = min(n_tiles, t_begin + p.tiles_per_split);
+  const int tok_limit = min(L, t_end * 16);
+  const int col = lane & 15;
+  const int quad = lane >> 4;
+  const int32_t* bt_row = p.block_tables + (size_t)b * p.max_pages;
+  const int32_t* sel_row = SEL ? p.sel + (size_t)b * p.sel_stride : nullptr;
+  const int n_pairs = (t_end > t_begin) ? ((t_end - t_begin + 1) >> 1) : 0;
+  const int n_iter = (n_pairs + kRing - 1) / kRing;  // pairs padded to a multiple of kRing
+  const size_t base = ((size_t)bh * p.splits + split) * ROWS;
+
+  if (w < 4) {
+    // ---------------- score wave: owners 2w and 2w + 1
+    const int s = w;
+    const bool active = 2 * s < NO;
+    i32x8_t qb[2][4][kM5];
+    int qs[2][2] = {{0, 0}, {0, 0}};
+    if (active) {
+#pragma unroll
+      for (int o = 0; o < 2; ++o)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+#pragma unroll
+          for (int m = 0; m < kM5; ++m) {
+            const uint32_t* src = p.qops + (((((size_t)bh * NO + 2 * s + o) * 4 + c) * kM5 + m) * 64 + lane) * 8;
+            const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(src);
+            const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(src + 4);
+            qb[o][c][m] = i32x8_t{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], 0, 0};
+            qs[o][c >> 1] |= (int)((a1[2] & 0xFFu) << (8 * (2 * (c & 1) + m)));
+          }
+    }
+    int row_lim[2];
+    float m_run[2], l_run[2];
+#pragma unroll
+    for (int o = 0; o < 2; ++o) {
+      const int row = 8 * (2 * s + o) + (col & 7);
+      row_lim[o] = (active && row < p.rows) ? min(tok_limit - 1, L - p.n_q + row / p.group) : -1;
+      m_run[o] = -INFINITY;
+      l_run[o] = 0.0f;
+    }
+    const bool hi_col = col < 8;
+    auto scores = [&](int pi) {
+      const int par = pi & 1;
+      const int tile = t_begin + 2 * pi;
+      f32x4_t S[2][2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+        u32x4_t kc = s_k[par][t][0][lane];
+        int ksc = (int)s_ks[par][t][0][lane];
+        a0 = qk_chunk5<0>(a0, kc, ksc, qb[0], qs[0]);
+        a1 = qk_chunk5<0>(a1, kc, ksc, qb[1], qs[1]);
+        kc = s_k[par][t][1][lane];
+        ksc = (int)s_ks[par][t][1][lane];
+        a0 = qk_chunk5<1>(a0, kc, ksc, qb[0], qs[0]);
+        a1 = qk_chunk5<1>(a1, kc, ksc, qb[1], qs[1]);
+        kc = s_k[par][t][2][lane];
+        ksc = (int)s_ks[par][t][2][lane];
+        a0 = qk_chunk5<2>(a0, kc, ksc, qb[0], qs[0]);
+        a1 = qk_chunk5<2>(a1, kc, ksc, qb[1], qs[1]);
+        kc = s_k[par][t][3][lane];
+        ksc = (int)s_ks[par][t][3][lane];
+        a0 = qk_chunk5<3>(a0, kc, ksc, qb[0], qs[0]);
+        a1 = qk_chunk5<3>(a1, kc, ksc, qb[1], qs[1]);
+        S[0][t] = a0;
+        S[1][t] = a1;
+      }
+#pragma unroll
+      for (int o = 0; o < 2; ++o) {
+        float sc[8];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float x = S[o][t][i];
+            const int tok = (tile + t) * 16 + 4 * quad + i;
+            sc[4 * t + i] = (tok <= row_lim[o]) ? x + dpp_ror8(x) : -INFINITY;
+          }
+        }
+        float mloc = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                           fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+        mloc = quad_max(mloc);
+        const float m_old = m_run[o];
+        const float m_tgt = fmaxf(m_old, mloc);
+        const bool grow = m_tgt > m_old + kLazyLog2;
+        const float m_new = grow ? m_tgt : m_old;
+        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+        m_run[o] = m_new;
+        float psum = 0.0f;
+        uint32_t pw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(sc[2 * e] - m_use);
+          const float p1 = __builtin_amdgcn_exp2f(sc[2 * e + 1] - m_use);
+          psum += p0 + p1;
+          const uint32_t u0 = as_u32(p0), u1 = as_u32(p1);
+          const uint32_t h = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+          const uint32_t l = pack_bf16x2(p0 - as_f32(u0 & 0xFFFF0000u), p1 - as_f32(u1 & 0xFFFF0000u));
+          pw[e] = hi_col ? h : l;
+        }
+        const int kg = (quad & 1) + (hi_col ? 0 : 2);
+        s_p[par][s][quad >> 1][16 * kg + 8 * o + (col & 7)] = u32x4_t{pw[0], pw[1], pw[2], pw[3]};
+        const float alpha = __builtin_amdgcn_exp2f(m_old - m_use);
+        l_run[o] = l_run[o] * alpha + psum;
+        if (lane < 8) s_alpha[par][8 * (2 * s + o) + lane] = alpha;
+        const bool moved = __builtin_amdgcn_ballot_w64(grow) != 0;
+        if (lane == 0) s_flag[par][2 * s + o] = moved ? 1 : 0;
+      }
+    };
+    // barrier schedule of the staging waves: pairs 0 and 1 staged, then
+    // one barrier per pair
+    __syncthreads();
+    if (n_pairs > 0 && active) scores(0);
+    __syncthreads();
+#pragma unroll 1
+    for (int pi = 0; pi < n_iter * kRing; ++pi) {
+      // past the last pair the staged tiles lie beyond the context and
+      // every score is masked: the softmax state stays unchanged
+      if (active) scores(pi + 1);
+      __syncthreads();
+    }
+    if (active) {
+#pragma unroll
+      for (int o = 0; o < 2; ++o) {
+        const float lrow = quad_sum(l_run[o]);
+        if (lane < 8) {
+          p.ws_ml[(base + 8 * (2 * s + o) + lane) * 2 + 0] = m_run[o];
+          p.ws_ml[(base + 8 * (2 * s + o) + lane) * 2 + 1] = lrow;
+        }
+      }
+    }
+    return;
+  }
+
+  // ---------------- output wave: channels 128v .. 128v + 127, staging of chunk v
+  const int v = w - 4;
+  auto stage = [&](int pi, int t, const Chunk5& c) {
+    const int tile = t_begin + 2 * pi + t;
+    s_k[pi & 1][t][v][lane] = u32x4_t{c.k[0], c.k[1], c.k[2], c.k[3]};
+    s_ks[pi & 1][t][v][lane] = c.ksc;
+    const bool dead = tile * 16 + col >= tok_limit;
+    uint32_t vw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) vw[i] = dead ? 0u : (SHARED ? c.k[i] : c.v[i]);
+    const uint32_t vsc = dead ? 0u : (SHARED ? c.ksc : c.vsc);
+    uint32_t vb[16];
+    dequant_group<KVQ_FMT_FP4_E2M1>(vw, scale_operand(vsc), vb);
+    u32x4_t* dst = reinterpret_cast<u32x4_t*>(&s_v[pi % 3][t][col][2 * (128 * v + 32 * quad)]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = u32x4_t{vb[4 * i], vb[4 * i + 1], vb[4 * i + 2], vb[4 * i + 3]};
+  };
+  auto fetch = [&](int pi, int t, Chunk5& c) {
+    load_chunk5<SHARED, SEL>(p, bt_row, sel_row, L, kvh, min(t_begin + 2 * pi + t, t_end - 1), v, lane, c);
+  };
+  Chunk5 ring[kRing][2];
+  if (n_pairs > 0) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) {
+      fetch(u, 0, ring[u][0]);
+      fetch(u, 1, ring[u][1]);
+    }
+  }
+  f32x4_t O[RG][8];
+#pragma unroll
+  for (int g = 0; g < RG; ++g)
+#pragma unroll
+    for (int n = 0; n < 8; ++n) O[g][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (n_pairs > 0) {
+    stage(0, 0, ring[0][0]);
+    stage(0, 1, ring[0][1]);
+    fetch(kRing, 0, ring[0][0]);
+    fetch(kRing, 1, ring[0][1]);
+  }
+  __syncthreads();
+  if (n_pairs > 0) {
+    stage(1, 0, ring[1 % kRing][0]);
+    stage(1, 1, ring[1 % kRing][1]);
+    fetch(1 + kRing, 0, ring[1 % kRing][0]);
+    fetch(1 + kRing, 1, ring[1 % kRing][1]);
+  }
+  __syncthreads();
+
+  const int rr = col >> 2;
+  const int c4 = (col & 3) * 4;
+  typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+#pragma unroll 1
+  for (int it = 0; it < n_iter; ++it) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) {
+      const int pi = it * kRing + u;
+      const int par = pi & 1;
+      bf16x8_t A[RG][2];
+#pragma unroll
+      for (int g = 0; g < RG; ++g) {
+        if (s_flag[par][2 * g] | s_flag[par][2 * g + 1]) {
+          float ar[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ar[i] = s_alpha[par][16 * g + 4 * quad + i];
+#pragma unroll
+          for (int n = 0; n < 8; ++n)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) O[g][n][i] *= ar[i];
+        }
+        A[g][0] = __builtin_bit_cast(bf16x8_t, s_p[par][g][0][lane]);
+        A[g][1] = __builtin_bit_cast(bf16x8_t, s_p[par][g][1][lane]);
+      }
+      const int vb = pi % 3;
+      auto read_b = [&](int Q, int n) {
+        const int cb = 2 * (128 * v + 16 * n + c4);
+        lds_bf16x4* a0 = (lds_bf16x4*)((__attribute__((address_space(3))) uint8_t*)&s_v[vb][0][4 * Q + rr][cb]);
+        lds_bf16x4* a1 = (lds_bf16x4*)((__attribute__((address_space(3))) uint8_t*)&s_v[vb][1][4 * Q + rr][cb]);
+        const u32x2_t w0 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(a0));
+        const u32x2_t w1 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(a1));
+        return __builtin_bit_cast(bf16x8_t, u32x4_t{w0[0], w0[1], w1[0], w1[1]});
+      };
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const bf16x8_t B0 = read_b(quad & 1, n);
+        const bf16x8_t B1 = read_b(2 + (quad & 1), n);
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+          O[g][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][0], B0, O[g][n], 0, 0, 0);
+          O[g][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][1], B1, O[g][n], 0, 0, 0);
+        }
+      }
+      {
+        const int su = (u + 2) % kRing;
+        stage(pi + 2, 0, ring[su][0]);
+        stage(pi + 2, 1, ring[su][1]);
+        fetch(pi + 2 + kRing, 0, ring[su][0]);
+        fetch(pi + 2 + kRing, 1, ring[su][1]);
+      }
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < RG; ++g)
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        p.ws_o[(base + 16 * g + 4 * quad + i) * kD5 + 128 * v + 16 * n + col] = O[g][n][i];
+}
+
 constexpr int kMinTilesPerSplit5 = 8;
 constexpr int kDefaultSlots5 = 256;  // MI355X: 256 CUs x 1 block
 constexpr int kMaxDevices5 = 64;
@@ -456,8 +735,14 @@ int resident_blocks5(int dev) {
     if (v > 0) return v;
   }
   int cus = 0, blocks = 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode512_kernel<RG, SHARED, false>, 512, 0) != hipSuccess) {
+  hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess) {
+    if constexpr (RG >= kRoleSplitRG5)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode512r_kernel<RG, SHARED, false>, 512, 0);
+    else
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode512_kernel<RG, SHARED, false>, 512, 0);
+  }
+  if (e != hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
@@ -488,7 +773,10 @@ hipError_t launch5(const DecodeParams& p, int batch, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid((unsigned)p.splits, (unsigned)p.hkv, (unsigned)batch);
-  hipLaunchKernelGGL((decode512_kernel<RG, SHARED, SEL>), grid, dim3(64 * kW5), 0, stream, p);
+  if constexpr (RG >= kRoleSplitRG5)
+    hipLaunchKernelGGL((decode512r_kernel<RG, SHARED, SEL>), grid, dim3(64 * kW5), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode512_kernel<RG, SHARED, SEL>), grid, dim3(64 * kW5), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((merge_kernel<16 * RG, 8>), dim3(qblocks), dim3(256), 0, stream, p);

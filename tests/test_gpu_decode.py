@@ -173,9 +173,12 @@ def test_decode_repeatable(gpu):
     (16, 3, True, (100, 900)),     # MTP: 48 rows with the causal rule
     (20, 3, True, (64, 700)),      # 60 rows: padded last row group
     (8, 1, False, (50, 800)),      # separate V cache, 2 KV heads
+    (24, 2, False, (70, 900)),     # separate V cache at 48 rows (role-split kernel)
 ])
 def test_decode_latent_512(gpu, group, n_q, shared, ctx):
-    """head_dim 512 (latent width), page 64: the 8-wave kernel."""
+    """head_dim 512 (latent width), page 64: the 8-wave kernels (up to 32
+    rows one wave per 8 rows for both roles; from 48 rows four score waves
+    and four output waves)."""
     hkv = 1 if shared else 2
     wl = syn.Workload("lat_g%d_nq%d_%d" % (group, n_q, int(shared)), batch=3, num_kv_heads=hkv,
                       num_q_heads=group * hkv, head_dim=512, page_size=64, context=0, n_q=n_q,

@@ -16,34 +16,17 @@
 namespace kvq {
 namespace {
 
-// E2M1 code (bit 3 = sign) of y in a group with scale exponent e_s: round
-// |y| * 2^-e_s to the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6, a tie going to
-// the even code, saturating at 6.  The thresholds are the midpoints; ">="
-// where the upper neighbour has the even code, ">" where the lower one does.
-__device__ __forceinline__ uint32_t e2m1_code(float y, int e_s) {
-  const float a = fabsf(ldexpf(y, -e_s));
-  const uint32_t k = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
-                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
-                     (uint32_t)(a > 5.0f);
-  return k | ((as_u32(y) >> 31) << 3);
-}
-
-// E4M3FN code of y with scale exponent e_s: round to nearest even onto
-// subnormals m * 2^-9 or normals with 3 mantissa bits, saturating at 448.
-__device__ __forceinline__ uint32_t e4m3_code(float y, int e_s) {
-  const float a = fabsf(ldexpf(y, -e_s));
-  uint32_t code;
-  if (a < 0.015625f) {
-    code = (uint32_t)rintf(a * 512.0f);  // 0..8; 8 is the smallest normal
-  } else {
-    uint32_t u = as_u32(a);
-    u += 0x7FFFFu + ((u >> 20) & 1u);
-    const int e = (int)(u >> 23) - 127;
-    const uint32_t m = (u >> 20) & 7u;
-    code = (e > 8 || (e == 8 && m == 7)) ? 0x7Eu : (((uint32_t)(e + 7) << 3) | m);
-  }
-  return code | ((as_u32(y) >> 31) << 7);
-}
+// Codes come from the hardware conversions (v_cvt_scalef32_pk_fp4_f32 and
+// v_cvt_scalef32_pk_fp8_f32) with the group's scale 2^e_s as the scale
+// operand: they divide by it and round to nearest even onto the format's
+// grid, the sign copied (negative values that round to zero give the code of
+// -0).  E2M1 saturates at 6 by itself; E4M3FN does not, so values are first
+// clamped to +-448 * 2^e_s, which leaves every other code unchanged.  An
+// exhaustive comparison of these conversions with a software encoder of the
+// rounding rule (the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 with ties to the
+// even code, saturating; E4M3FN likewise with subnormals m * 2^-9), over all
+// 2^32 fp32 inputs at scale exponents -127 .. 127, found no difference on
+// gfx950.
 
 struct AppendParams {
   CacheGeom c;
@@ -147,29 +130,35 @@ __device__ __forceinline__ void append_wave(const AppendParams& p, int wave, int
   uint8_t* codes = (tensor == 0 ? p.kc : p.vc) + (int64_t)page * c.c_page + (int64_t)h * c.c_head + unit * c.cb;
   uint8_t* scales = (tensor == 0 ? p.ks : p.vs) + (int64_t)page * c.s_page + (int64_t)h * c.s_head;
   scales[unit] = (uint8_t)byte;
+  const float scale = as_f32((uint32_t)byte << 23);  // 2^e_s (field 0: 2^-127)
   if (fp4) {
+    // channel 2i in the low nibble of byte i
     u32x4_t w;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       uint32_t d = 0;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = 8 * k + 2 * e;
-        d |= (e2m1_code(x[i], e_s) | (e2m1_code(x[i + 1], e_s) << 4)) << (8 * e);
-      }
+      d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, x[8 * k + 0], x[8 * k + 1], scale, 0);
+      d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, x[8 * k + 2], x[8 * k + 3], scale, 1);
+      d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, x[8 * k + 4], x[8 * k + 5], scale, 2);
+      d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, x[8 * k + 6], x[8 * k + 7], scale, 3);
       w[k] = d;
     }
     *reinterpret_cast<u32x4_t*>(codes) = w;
   } else {
+    typedef __attribute__((ext_vector_type(2))) short s16x2_t;
+    const float lim = ldexpf(448.0f, e_s);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) x[i] = fminf(fmaxf(x[i], -lim), lim);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       u32x4_t w;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
-        uint32_t d = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) d |= e4m3_code(x[16 * half + 4 * k + e], e_s) << (8 * e);
-        w[k] = d;
+        const int i = 16 * half + 4 * k;
+        s16x2_t d = {0, 0};
+        d = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(d, x[i + 0], x[i + 1], scale, false);
+        d = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(d, x[i + 2], x[i + 3], scale, true);
+        w[k] = __builtin_bit_cast(uint32_t, d);
       }
       *reinterpret_cast<u32x4_t*>(codes + 16 * half) = w;
     }

@@ -277,13 +277,21 @@ def main():
             "byte_ratio": round(kv_fp8 / kv_fp4, 4),
         }
 
-    # ---------------- bulk append: one sequence's whole context, re-appended
-    # (rewrites identical codes), FP4
-    b0 = 0
-    n_sh0 = plan.n_shared_pages[b0] * P
-    L0 = int(plan.context_lens[b0]) - n_sh0
-    kv0 = {t: syn.private_tokens(wl, t, b0, L0, dev) for t in syn.tensor_names(wl)}
-    sl0 = torch_from(syn.slots_for(plan.private_pages[b0], L0, P), dev)
+    # ---------------- bulk append: the whole cache build in one call (every
+    # sequence's tokens, 4.29 GB of bf16 K and V in, 1.14 GB of FP4 codes and
+    # scales out), re-appended over a replica (rewrites identical codes)
+    parts = {t: [] for t in syn.tensor_names(wl)}
+    sl_parts = []
+    for b in range(B):
+        n_sh = plan.n_shared_pages[b] * P
+        Lb = int(plan.context_lens[b]) - n_sh
+        for t in parts:
+            parts[t].append(syn.private_tokens(wl, t, b, Lb, dev))
+        sl_parts.append(torch_from(syn.slots_for(plan.private_pages[b], Lb, P), dev))
+    kv0 = {t: torch.cat(x) for t, x in parts.items()}
+    sl0 = torch.cat(sl_parts)
+    del parts, sl_parts
+    L0 = int(sl0.numel())
     torch.cuda.synchronize()
     app_ms = []
     for r in range(12):
@@ -299,9 +307,9 @@ def main():
         "tokens": L0, "ms": round(app_t, 4),
         "bytes": app_bytes, "gbs": round(app_bytes / (app_t * 1e-3) / 1e9, 1),
         "hbm_frac": round(app_bytes / (app_t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "note": "bf16 K and V read, FP4 codes + scales written, slot ids read",
+        "note": "the whole cache build in one call: bf16 K and V read, FP4 codes + scales written, slot ids read",
     }
-    del kv0
+    del kv0, sl0
 
     if args.copy_calibration:
         # torch's elementwise kernel: reads 512 MiB, writes 512 MiB

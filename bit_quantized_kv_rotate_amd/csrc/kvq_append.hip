@@ -13,9 +13,15 @@
 namespace kvq {
 namespace {
 
+// 1-D grid, the (KV head, tensor) pair fastest: the blocks that run together
+// cover every head of the same tokens, so each token's bf16 row (all heads,
+// contiguous) is read whole at once rather than one head at a time
 template <int G>
-__global__ __launch_bounds__(256) void append_kernel(const AppendParams p) {
-  append_wave<G>(p, blockIdx.x * 4 + (threadIdx.x >> 6), blockIdx.y, blockIdx.z, threadIdx.x & 63);
+__global__ __launch_bounds__(256) void append_kernel(const AppendParams p, unsigned n_ht) {
+  const unsigned ht = blockIdx.x % n_ht;
+  const unsigned cb = blockIdx.x / n_ht;
+  append_wave<G>(p, (int)cb * 4 + (threadIdx.x >> 6), (int)(ht % (unsigned)p.c.hkv), (int)(ht / (unsigned)p.c.hkv),
+                 threadIdx.x & 63);
 }
 
 struct DequantParams {
@@ -80,14 +86,17 @@ hipError_t launch_append(const CacheGeom& c, uint8_t* kc, uint8_t* ks, uint8_t* 
   const AppendParams p = make_append_params(c, AppendArgs{kc, ks, vc, vs, k_new, v_new, slots, n_tokens});
   const int G = c.d / 32;
   const long long chunks = append_waves(c, n_tokens);  // waves per (head, tensor)
-  const dim3 grid((unsigned)((chunks + 3) / 4), (unsigned)c.hkv, c.kv_shared ? 1u : 2u);
+  const unsigned n_ht = (unsigned)c.hkv * (c.kv_shared ? 1u : 2u);
+  const long long blocks = (chunks + 3) / 4 * (long long)n_ht;
+  if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)blocks);
   switch (G) {
-    case 1: hipLaunchKernelGGL((append_kernel<1>), grid, dim3(256), 0, stream, p); break;
-    case 2: hipLaunchKernelGGL((append_kernel<2>), grid, dim3(256), 0, stream, p); break;
-    case 4: hipLaunchKernelGGL((append_kernel<4>), grid, dim3(256), 0, stream, p); break;
-    case 8: hipLaunchKernelGGL((append_kernel<8>), grid, dim3(256), 0, stream, p); break;
-    case 16: hipLaunchKernelGGL((append_kernel<16>), grid, dim3(256), 0, stream, p); break;
-    case 32: hipLaunchKernelGGL((append_kernel<32>), grid, dim3(256), 0, stream, p); break;
+    case 1: hipLaunchKernelGGL((append_kernel<1>), grid, dim3(256), 0, stream, p, n_ht); break;
+    case 2: hipLaunchKernelGGL((append_kernel<2>), grid, dim3(256), 0, stream, p, n_ht); break;
+    case 4: hipLaunchKernelGGL((append_kernel<4>), grid, dim3(256), 0, stream, p, n_ht); break;
+    case 8: hipLaunchKernelGGL((append_kernel<8>), grid, dim3(256), 0, stream, p, n_ht); break;
+    case 16: hipLaunchKernelGGL((append_kernel<16>), grid, dim3(256), 0, stream, p, n_ht); break;
+    case 32: hipLaunchKernelGGL((append_kernel<32>), grid, dim3(256), 0, stream, p, n_ht); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

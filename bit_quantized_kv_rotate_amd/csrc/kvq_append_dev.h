@@ -28,6 +28,14 @@ namespace {
 // 2^32 fp32 inputs at scale exponents -127 .. 127, found no difference on
 // gfx950.
 
+// The value x holds in lane l ^ s (s a power of two below 64): a DPP quad
+// permutation for s = 1 and 2, the LDS permute network above.
+__device__ __forceinline__ float xor_lane(float x, int s) {
+  if (s == 1) return as_f32((uint32_t)__builtin_amdgcn_mov_dpp((int)as_u32(x), 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
+  if (s == 2) return as_f32((uint32_t)__builtin_amdgcn_mov_dpp((int)as_u32(x), 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
+  return __shfl_xor(x, s, 64);
+}
+
 struct AppendParams {
   CacheGeom c;
   uint8_t* kc;
@@ -105,7 +113,7 @@ __device__ __forceinline__ void append_wave(const AppendParams& p, int wave, int
     for (int s = 1; s < G; s <<= 1) {
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
-        const float y = __shfl_xor(x[i], s, 64);
+        const float y = xor_lane(x[i], s);
         x[i] = (g & s) ? (y - x[i]) : (x[i] + y);
       }
     }

@@ -198,6 +198,64 @@ __device__ __forceinline__ f32x4_t qk_chunk5(f32x4_t acc, const u32x4_t kc, int 
   return acc;
 }
 
+// Online softmax of one 8-row score owner over a tile pair, from its scores
+// S (tile t, token 4 quad + i; column c of the MFMA output holds query-term
+// half c / 8 of row c & 7, so x + its ror-8 partner is the row's score):
+// masked past row_lim, lazy reference maximum (kLazyLog2), P split into bf16
+// hi (lanes c < 8) and lo (c >= 8) and stored as PV A operands in the
+// owner's slot of a 16-row group (`sp`: the group's two k-halves, `half`:
+// the owner's 8 rows within it); the rows' rescale factors go to alpha[0..7]
+// and whether any reference moved to *flag.
+__device__ __forceinline__ void owner_softmax(const f32x4_t (&S)[2], int tile, int row_lim, int lane, int half,
+                                              float& m_run, float& l_run, u32x4_t (*sp)[64], float* alpha,
+                                              int* flag) {
+  const int col = lane & 15;
+  const int quad = lane >> 4;
+  const bool hi_col = col < 8;
+  float sc[8];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float x = S[t][i];
+      const int tok = (tile + t) * 16 + 4 * quad + i;
+      sc[4 * t + i] = (tok <= row_lim) ? x + dpp_ror8(x) : -INFINITY;
+    }
+  }
+  float mloc = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                     fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+  mloc = quad_max(mloc);
+  // lazy reference maximum (kLazyLog2): most pairs leave it, and so the
+  // output rows, unchanged
+  const float m_old = m_run;
+  const float m_tgt = fmaxf(m_old, mloc);
+  const bool grow = m_tgt > m_old + kLazyLog2;
+  const float m_new = grow ? m_tgt : m_old;
+  const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+  m_run = m_new;
+  float psum = 0.0f;
+  uint32_t pw[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float p0 = __builtin_amdgcn_exp2f(sc[2 * e] - m_use);
+    const float p1 = __builtin_amdgcn_exp2f(sc[2 * e + 1] - m_use);
+    psum += p0 + p1;
+    const uint32_t u0 = as_u32(p0), u1 = as_u32(p1);
+    const uint32_t h = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+    const uint32_t l = pack_bf16x2(p0 - as_f32(u0 & 0xFFFF0000u), p1 - as_f32(u1 & 0xFFFF0000u));
+    pw[e] = hi_col ? h : l;
+  }
+  // A operand slot: k-half quad / 2 (token quads {0,1} or {2,3}); lane
+  // k-group (quad & 1) + 2 * lo, row 8 half + (col & 7)
+  const int kg = (quad & 1) + (hi_col ? 0 : 2);
+  sp[quad >> 1][16 * kg + 8 * half + (col & 7)] = u32x4_t{pw[0], pw[1], pw[2], pw[3]};
+  const float a = __builtin_amdgcn_exp2f(m_old - m_use);
+  l_run = l_run * a + psum;
+  if (lane < 8) alpha[lane] = a;
+  const bool moved = __builtin_amdgcn_ballot_w64(grow) != 0;
+  if (lane == 0) *flag = moved ? 1 : 0;
+}
+
 // SEL: the scan runs over the list of selected positions of each sequence
 // (p.sel; context_lens are the list lengths), one query position per
 // sequence.
@@ -287,7 +345,6 @@ __global__ __launch_bounds__(512) void decode512_kernel(const DecodeParams p) {
   const int row = 8 * w + (col & 7);  // owner's row in this lane
   // last token this lane's row may see (context end, MTP causal rule)
   const int row_lim = (owner && row < p.rows) ? min(tok_limit - 1, L - p.n_q + row / p.group) : -1;
-  const bool hi_col = col < 8;
   float m_run = -INFINITY, l_run = 0.0f;
 
   // owner: scores of pair pi, online softmax, P hi / lo as PV A operands,
@@ -305,48 +362,7 @@ __global__ __launch_bounds__(512) void decode512_kernel(const DecodeParams p) {
       acc = qk_chunk5<3>(acc, s_k[par][s][3][lane], (int)s_ks[par][s][3][lane], qb, qs);
       S[s] = acc;
     }
-    float sc[8];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = S[s][i];
-        const int tok = (tile + s) * 16 + 4 * quad + i;
-        sc[4 * s + i] = (tok <= row_lim) ? x + dpp_ror8(x) : -INFINITY;
-      }
-    }
-    float mloc = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                       fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-    mloc = quad_max(mloc);
-    // lazy reference maximum (kLazyLog2): most pairs leave it, and so the
-    // output rows, unchanged
-    const float m_old = m_run;
-    const float m_tgt = fmaxf(m_old, mloc);
-    const bool grow = m_tgt > m_old + kLazyLog2;
-    const float m_new = grow ? m_tgt : m_old;
-    const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-    m_run = m_new;
-    float psum = 0.0f;
-    uint32_t pw[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float p0 = __builtin_amdgcn_exp2f(sc[2 * e] - m_use);
-      const float p1 = __builtin_amdgcn_exp2f(sc[2 * e + 1] - m_use);
-      psum += p0 + p1;
-      const uint32_t u0 = as_u32(p0), u1 = as_u32(p1);
-      const uint32_t h = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
-      const uint32_t l = pack_bf16x2(p0 - as_f32(u0 & 0xFFFF0000u), p1 - as_f32(u1 & 0xFFFF0000u));
-      pw[e] = hi_col ? h : l;
-    }
-    // A operand slot: MFMA quad / 2 (token quads {0,1} or {2,3}); lane
-    // k-group (quad & 1) + 2 * lo, row 8 (w & 1) + (col & 7)
-    const int kg = (quad & 1) + (hi_col ? 0 : 2);
-    s_p[par][w >> 1][quad >> 1][16 * kg + 8 * (w & 1) + (col & 7)] = u32x4_t{pw[0], pw[1], pw[2], pw[3]};
-    const float alpha = __builtin_amdgcn_exp2f(m_old - m_use);
-    l_run = l_run * alpha + psum;
-    if (lane < 8) s_alpha[par][8 * w + lane] = alpha;
-    const bool moved = __builtin_amdgcn_ballot_w64(grow) != 0;
-    if (lane == 0) s_flag[par][w] = moved ? 1 : 0;
+    owner_softmax(S, tile, row_lim, lane, w & 1, m_run, l_run, s_p[par][w >> 1], &s_alpha[par][8 * w], &s_flag[par][w]);
   };
 
   f32x4_t O[RG][4];
@@ -518,7 +534,6 @@ __global__ __launch_bounds__(512) void decode512r_kernel(const DecodeParams p) {
       m_run[o] = -INFINITY;
       l_run[o] = 0.0f;
     }
-    const bool hi_col = col < 8;
     auto scores = [&](int pi) {
       const int par = pi & 1;
       const int tile = t_begin + 2 * pi;
@@ -546,46 +561,9 @@ __global__ __launch_bounds__(512) void decode512r_kernel(const DecodeParams p) {
         S[1][t] = a1;
       }
 #pragma unroll
-      for (int o = 0; o < 2; ++o) {
-        float sc[8];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float x = S[o][t][i];
-            const int tok = (tile + t) * 16 + 4 * quad + i;
-            sc[4 * t + i] = (tok <= row_lim[o]) ? x + dpp_ror8(x) : -INFINITY;
-          }
-        }
-        float mloc = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                           fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-        mloc = quad_max(mloc);
-        const float m_old = m_run[o];
-        const float m_tgt = fmaxf(m_old, mloc);
-        const bool grow = m_tgt > m_old + kLazyLog2;
-        const float m_new = grow ? m_tgt : m_old;
-        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-        m_run[o] = m_new;
-        float psum = 0.0f;
-        uint32_t pw[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(sc[2 * e] - m_use);
-          const float p1 = __builtin_amdgcn_exp2f(sc[2 * e + 1] - m_use);
-          psum += p0 + p1;
-          const uint32_t u0 = as_u32(p0), u1 = as_u32(p1);
-          const uint32_t h = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
-          const uint32_t l = pack_bf16x2(p0 - as_f32(u0 & 0xFFFF0000u), p1 - as_f32(u1 & 0xFFFF0000u));
-          pw[e] = hi_col ? h : l;
-        }
-        const int kg = (quad & 1) + (hi_col ? 0 : 2);
-        s_p[par][s][quad >> 1][16 * kg + 8 * o + (col & 7)] = u32x4_t{pw[0], pw[1], pw[2], pw[3]};
-        const float alpha = __builtin_amdgcn_exp2f(m_old - m_use);
-        l_run[o] = l_run[o] * alpha + psum;
-        if (lane < 8) s_alpha[par][8 * (2 * s + o) + lane] = alpha;
-        const bool moved = __builtin_amdgcn_ballot_w64(grow) != 0;
-        if (lane == 0) s_flag[par][2 * s + o] = moved ? 1 : 0;
-      }
+      for (int o = 0; o < 2; ++o)
+        owner_softmax(S[o], tile, row_lim[o], lane, o, m_run[o], l_run[o], s_p[par][s], &s_alpha[par][8 * (2 * s + o)],
+                      &s_flag[par][2 * s + o]);
     };
     // barrier schedule of the staging waves: pairs 0 and 1 staged, then
     // one barrier per pair

@@ -223,7 +223,6 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeParams p) {
 #pragma unroll
   for (int i = 0; i < C; ++i) acc[i] = 0.0f;
   const float* po = p.ws_o + row0 * D + C * lane;
-#pragma unroll 4
   for (int sp = 0; sp < S; ++sp) {
     const float w = as_f32((uint32_t)__builtin_amdgcn_readlane((int)as_u32(ws), sp));
     if (w == 0.0f) continue;  // an empty split stores no O

@@ -78,7 +78,6 @@ __global__ __launch_bounds__(256) void shared_merge_kernel(const MergeParams m) 
   float acc[C] = {0.0f, 0.0f};
   const float* p1 = m.o1 + ((size_t)bh * m.s1 * m.rows_seq + r) * kDS + C * lane;
   const float* p2 = m.o2 + ((size_t)bh * m.s2 * m.rows2 + r) * kDS + C * lane;
-#pragma unroll 4
   for (int sp = 0; sp < S; ++sp) {
     const float w = as_f32((uint32_t)__builtin_amdgcn_readlane((int)as_u32(ws), sp));
     if (w == 0.0f) continue;  // an empty split stores no O

@@ -19,9 +19,10 @@
 //    PV product puts hi and lo of P in the contraction (k = 16 tokens x
 //    {hi, lo}), so one accumulator holds 16 full rows.
 // P (as ready MFMA A operands), the rescale factors and V pass through LDS,
-// double-buffered by tile-pair parity: one barrier per pair.  From 48 rows
-// on, decode512r_kernel splits the same work by role instead (four waves
-// score, four accumulate), with bitwise the same partials.
+// double-buffered by tile-pair parity: one barrier per pair.  Above 32 rows
+// (three or four 16-row groups) decode512r_kernel splits the same work by
+// role instead (four waves score, four accumulate), with bitwise the same
+// partials.
 #include <atomic>
 
 #include "kvq_decode_common.h"
@@ -35,7 +36,7 @@ constexpr int kM5 = kT5 / 2;         // scaled MFMAs per 128-channel block (two 
 constexpr int kW5 = 8;               // waves per block
 constexpr int kVRow5 = 2 * kD5 + 32;  // LDS bytes per bf16 token row (padded)
 constexpr int kMaxRG5 = 4;           // 16-row groups (64 rows)
-constexpr int kRoleSplitRG5 = 3;     // from 48 rows on, the role-split kernel
+constexpr int kRoleSplitRG5 = 3;     // from three 16-row groups (33 rows) on, the role-split kernel
 // tile pairs in flight per wave (one chunk each): three, fewer where the
 // accumulators of 64 rows (and a separate V chunk, or the per-lane addresses
 // of a gathered selection) leave no room

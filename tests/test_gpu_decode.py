@@ -177,7 +177,7 @@ def test_decode_repeatable(gpu):
 ])
 def test_decode_latent_512(gpu, group, n_q, shared, ctx):
     """head_dim 512 (latent width), page 64: the 8-wave kernels (up to 32
-    rows one wave per 8 rows for both roles; from 48 rows four score waves
+    rows one wave per 8 rows for both roles; above 32 rows four score waves
     and four output waves)."""
     hkv = 1 if shared else 2
     wl = syn.Workload("lat_g%d_nq%d_%d" % (group, n_q, int(shared)), batch=3, num_kv_heads=hkv,

@@ -15,13 +15,18 @@ compared element by element (max |err| <= 2e-3, relative L2 <= 1e-3).
                  query heads, context 131072, page 64
   extend         batch 4, 8 KV / 64 Q heads, context 32768 whose last 64
                  tokens are a new chunk (512 rows per KV head)
+
+and the bulk append of the whole b32_l32k cache in one call, bit-exact on
+sampled tokens.
 """
 import numpy as np
 import pytest
 import torch
 
+import bit_quantized_kv_rotate_amd as kvq
 import kvq_synth as syn
-from kvq_gpu_util import Filled, assert_close, oracle_decode_pairs
+import oracle
+from kvq_gpu_util import Filled, assert_close, gather_codes, oracle_decode_pairs
 
 pytestmark = pytest.mark.gpu
 
@@ -91,3 +96,43 @@ def test_fullsize_extend_chunk_sampled(gpu):
                       page_size=16, context=32768, n_q=64)
     syn.WORKLOADS.setdefault(wl.name, wl)
     _check(wl.name, "fp4", 4, 4)
+
+
+def test_fullsize_b32_l32k_bulk_append_sampled(gpu):
+    """The whole b32_l32k cache (32 sequences x 32768 tokens x 8 KV heads)
+    built by one append call, the launch the benchmark times as its bulk
+    append: codes and scale bytes bit-exact against the oracle on the first
+    and last token of every sequence and 2,000 random tokens, every head and
+    both tensors."""
+    wl = syn.WORKLOADS["b32_l32k"]
+    plan = syn.page_plan(wl)
+    P = wl.page_size
+    cache = kvq.KVCache(kvq.FMT_FP4_E2M1, wl.num_kv_heads, wl.head_dim, P, plan.num_pages)
+    ks, vs, sls, starts = [], [], [], []
+    n = 0
+    for b in range(wl.batch):
+        L = int(plan.context_lens[b])
+        ks.append(syn.private_tokens(wl, "k", b, L, "cuda"))
+        vs.append(syn.private_tokens(wl, "v", b, L, "cuda"))
+        sls.append(syn.slots_for(plan.private_pages[b], L, P))
+        starts.append(n)
+        n += L
+    k, v = torch.cat(ks), torch.cat(vs)
+    slots = np.concatenate(sls)
+    del ks, vs
+    kvq.rotate_quantize_append(cache, k, v, torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    idx = set(rng.integers(n, size=2000).tolist())
+    for b in range(wl.batch):
+        idx.update((starts[b], starts[b] + int(plan.context_lens[b]) - 1))
+    idx = np.array(sorted(idx), dtype=np.int64)
+    sel = torch.from_numpy(idx).cuda()
+    for t, x in (("k", k), ("v", v)):
+        want_c, want_s = oracle.quantize_fp4(syn.bf16_bits(x[sel]), True)
+        got_c, got_s = gather_codes(cache, t, slots[idx])
+        bad_s = np.argwhere(got_s != want_s)
+        assert bad_s.size == 0, "%s: scale mismatch at %s" % (t, bad_s[:5].tolist())
+        bad_c = np.argwhere(got_c != want_c)
+        assert bad_c.size == 0, "%s: code mismatch at %s" % (t, bad_c[:5].tolist())
+    print("b32_l32k bulk append: %d tokens in one call, %d sampled tokens bit-exact" % (n, len(idx)))

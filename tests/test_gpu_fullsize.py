@@ -16,8 +16,9 @@ compared element by element (max |err| <= 2e-3, relative L2 <= 1e-3).
   extend         batch 4, 8 KV / 64 Q heads, context 32768 whose last 64
                  tokens are a new chunk (512 rows per KV head)
 
-and the bulk append of the whole b32_l32k cache in one call, bit-exact on
-sampled tokens.
+and, for b32_l32k, the bulk append of the whole cache in one call (bit-exact
+on sampled tokens) and the one-call step (append + decode) the benchmark
+times.
 """
 import numpy as np
 import pytest
@@ -136,3 +137,28 @@ def test_fullsize_b32_l32k_bulk_append_sampled(gpu):
         bad_c = np.argwhere(got_c != want_c)
         assert bad_c.size == 0, "%s: code mismatch at %s" % (t, bad_c[:5].tolist())
     print("b32_l32k bulk append: %d tokens in one call, %d sampled tokens bit-exact" % (n, len(idx)))
+
+
+def test_fullsize_b32_l32k_step_call(gpu):
+    """The benchmark's step at full size: one kvq_append_decode_attn_fp4 call
+    that re-appends the last token of every sequence, then attends.  The
+    tokens re-appended are the stored ones, so the cache keeps every byte,
+    and the output is bitwise that of the decode-only call (which the
+    sampled test above checks against the oracle)."""
+    wl = syn.WORKLOADS["b32_l32k"]
+    f = Filled(wl, "fp4", gen_device="cuda", keep_host=False)
+    q = syn.queries(wl, "cuda")
+    plain = f.decode(q)
+    k1, v1, s1 = [], [], []
+    for b in range(wl.batch):
+        L = int(f.plan.context_lens[b])
+        k1.append(syn.private_tokens(wl, "k", b, L, "cuda")[-1:])
+        v1.append(syn.private_tokens(wl, "v", b, L, "cuda")[-1:])
+        s1.append(syn.slots_for(f.plan.private_pages[b], L, wl.page_size)[-1:])
+    before = [x.clone() for x in (f.cache.k_codes, f.cache.k_scales, f.cache.v_codes, f.cache.v_scales)]
+    out = kvq.append_decode_attn_fp4(f.cache, torch.cat(k1), torch.cat(v1), torch.from_numpy(np.concatenate(s1)).cuda(),
+                                     q, f.block_tables, f.context_lens, f.max_context)
+    torch.cuda.synchronize()
+    after = (f.cache.k_codes, f.cache.k_scales, f.cache.v_codes, f.cache.v_scales)
+    assert all(torch.equal(x, y) for x, y in zip(before, after)), "the re-append changed the cache"
+    assert torch.equal(out, plain), "step call differs from the decode-only call"

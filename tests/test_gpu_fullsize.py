@@ -14,7 +14,8 @@ compared element by element (max |err| <= 2e-3, relative L2 <= 1e-3).
   mla_b16_l128k  batch 16, one latent head of width 512 (K = V), 64 absorbed
                  query heads, context 131072, page 64
   extend         batch 4, 8 KV / 64 Q heads, context 32768 whose last 64
-                 tokens are a new chunk (512 rows per KV head)
+                 tokens are a new chunk (512 rows per KV head); and the
+                 benchmark's 1024-token chunk on sampled positions
 
 and, for b32_l32k, the bulk append of the whole cache in one call (bit-exact
 on sampled tokens) and the one-call step (append + decode) the benchmark
@@ -97,6 +98,35 @@ def test_fullsize_extend_chunk_sampled(gpu):
                       page_size=16, context=32768, n_q=64)
     syn.WORKLOADS.setdefault(wl.name, wl)
     _check(wl.name, "fp4", 4, 4)
+
+
+def test_fullsize_extend_1024_chunk_sampled_rows(gpu):
+    """The benchmark's extend chunk exactly (batch 4, 8 KV / 64 query heads,
+    context 32768 whose last 1024 tokens are the chunk: 8192 rows per KV
+    head, one call): sampled chunk positions of two sequences, all 64 heads
+    each, against the oracle's attention over the tokens the position sees
+    (its own and every earlier one)."""
+    import math
+
+    wl = syn.Workload("extend_b4_l32k", batch=4, num_kv_heads=8, num_q_heads=64, head_dim=128,
+                      page_size=16, context=32768, n_q=1024)
+    f = Filled(wl, "fp4", gen_device="cuda")
+    q = syn.queries(wl, "cuda")
+    out = f.decode(q).cpu().numpy()
+    torch.cuda.synchronize()
+    assert np.isfinite(out).all()
+    qh = syn.bf16_bits(q)
+    worst = 0.0
+    for b in (0, wl.batch - 1):
+        L = int(f.plan.context_lens[b])
+        kc, ks = oracle.quantize_fp4(f.host["k"][b], True)
+        vc, vs = oracle.quantize_fp4(f.host["v"][b], True)
+        khat, vhat = oracle.dequant_fp4(kc, ks), oracle.dequant_fp4(vc, vs)
+        for j in (0, 1, 511, 766, 1022, 1023):
+            seen = L - wl.n_q + j + 1
+            want = oracle.decode(qh[b][j:j + 1], khat[:seen], vhat[:seen], True, 1.0 / math.sqrt(wl.head_dim))
+            worst = max(worst, assert_close(out[b][j], want[0], "extend chunk seq %d position %d" % (b, j))[0])
+    print("extend_b4_l32k (1024-token chunk): 12 sampled positions x 64 heads, worst max_abs %.3g" % worst)
 
 
 def test_fullsize_b32_l32k_bulk_append_sampled(gpu):

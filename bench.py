@@ -5,17 +5,22 @@ context 32768 tokens per sequence, page size 16 with randomly permuted block
 tables; keys/values/queries bf16 N(0,1) with 2 outlier channels x20 per KV
 head.  One step = append one new token per sequence to the FP4 cache
 (rotate + quantise + store) and one FP4 decode-attention pass over the whole
-cache, in one call (kvq_append_decode_attn_fp4).  The cache is replicated (as the layers of a model would be) and the
-steps rotate over the replicas, so no step finds its cache in the 256 MB
-last-level cache.  The FP8 (E4M3 + per-32 scale) comparator cache is built
-from the same bf16 inputs and timed in ABBA order against FP4.
+cache, in one call (kvq_append_decode_attn_fp4).  The cache is replicated
+(as the layers of a model would be) and the steps rotate over the replicas,
+so no step finds its cache in the 256 MB last-level cache.  The FP8 (E4M3 +
+per-32 scale) comparator cache is built from the same bf16 inputs and timed
+in ABBA order against FP4.
 
 Prints ONE JSON line.  `value` is KV-cache bytes streamed per second by the
 whole step (GB/s, inputs resident in HBM); `roofline` is that step call
-(query prologue with the append, page-scan and split-merge kernels) -
-algorithmic bytes per call over its mean HIP-event duration - against the
-8 TB/s HBM peak;
-`cpu_baseline` times the CPU oracle on a bounded sample.
+(query prologue with the append, page-scan and split-merge kernels):
+algorithmic bytes per call over its mean HIP-event duration, against the
+8 TB/s HBM peak, with the HBM traffic the committed counter summary records
+for these kernel sources; `cpu_baseline` times the CPU oracle on a bounded
+sample.  Further sections time the bulk append of the whole cache, the
+agentic MTP mix and a forked batch (plain and shared-prefix decode), an
+extend chunk and the latent workload (plain and selected positions); each
+can be left out with its --no-* flag.
 """
 import argparse
 import hashlib

@@ -448,7 +448,7 @@ __global__ __launch_bounds__(64 * WAVES) void extend_kernel(const DecodeParams p
 
 constexpr int kMinTilesPerSplitX = 8;
 constexpr int kMaxTilesPerSplitX = 512;
-constexpr int kDefaultSlotsX = 256;  // wide blocks: one per CU (MI355X); narrow: four
+constexpr int kDefaultSlotsX = 256;  // wide blocks: one per CU (MI355X); narrow: six
 constexpr int kMaxDevicesX = 64;
 constexpr int kMaxRowsX = 1 << 16;
 
@@ -496,7 +496,7 @@ int plan_extend_rows(const CacheGeom& c, int batch, long long rows, int max_cont
     // one round of blocks over the device, at least kMinTilesPerSplitX tiles
     // and at most kMaxTilesPerSplitX per split
     int slots = block_rows == 16 * kNarrowX ? resident_blocks_x<kNarrowX>() : resident_blocks_x<kWideX>();
-    if (slots <= 0) slots = block_rows == 16 * kNarrowX ? 4 * kDefaultSlotsX : kDefaultSlotsX;
+    if (slots <= 0) slots = block_rows == 16 * kNarrowX ? 6 * kDefaultSlotsX : kDefaultSlotsX;
     const long long work = (long long)batch * c.hkv * row_blocks;
     long long want = work >= slots ? 1 : slots / work;
     const long long by_len = n_tiles / kMinTilesPerSplitX;

@@ -448,6 +448,7 @@ __global__ __launch_bounds__(64 * WAVES) void extend_kernel(const DecodeParams p
 
 constexpr int kMinTilesPerSplitX = 8;
 constexpr int kMaxTilesPerSplitX = 512;
+constexpr int kNarrowTilesPerSplitX = 256;
 constexpr int kDefaultSlotsX = 256;  // wide blocks: one per CU (MI355X); narrow: six
 constexpr int kMaxDevicesX = 64;
 constexpr int kMaxRowsX = 1 << 16;
@@ -494,15 +495,26 @@ int plan_extend_rows(const CacheGeom& c, int batch, long long rows, int max_cont
   int splits = (int)((flags & KVQ_SPLITS_MASK) >> KVQ_SPLITS_SHIFT);
   if (splits <= 0) {
     // one round of blocks over the device, at least kMinTilesPerSplitX tiles
-    // and at most kMaxTilesPerSplitX per split
+    // and at most a cap per split (below)
     int slots = block_rows == 16 * kNarrowX ? resident_blocks_x<kNarrowX>() : resident_blocks_x<kWideX>();
     if (slots <= 0) slots = block_rows == 16 * kNarrowX ? 6 * kDefaultSlotsX : kDefaultSlotsX;
     const long long work = (long long)batch * c.hkv * row_blocks;
     long long want = work >= slots ? 1 : slots / work;
     const long long by_len = n_tiles / kMinTilesPerSplitX;
     if (want > by_len) want = by_len;
-    const long long by_cap = (n_tiles + kMaxTilesPerSplitX - 1) / kMaxTilesPerSplitX;
-    if (want < by_cap) want = by_cap;
+    // Only the longest context is known here.  Narrow blocks (decode-like
+    // rows, where batches are ragged) take a smaller cap, so the longest
+    // sequences of a ragged batch spread over more blocks; when the cap
+    // asks for more splits than one round holds, the count is rounded up to
+    // whole rounds (a partial last round would leave most of the device idle
+    // on a batch of equal contexts).
+    const int cap = block_rows == 16 * kNarrowX ? kNarrowTilesPerSplitX : kMaxTilesPerSplitX;
+    const long long by_cap = (n_tiles + cap - 1) / cap;
+    if (want < by_cap) {
+      want = by_cap;
+      const long long per_round = work >= slots ? 0 : slots / work;
+      if (per_round > 1) want = (want + per_round - 1) / per_round * per_round;
+    }
     splits = (int)(want < 1 ? 1 : want);
   }
   if (splits > kMaxSplits) splits = kMaxSplits;

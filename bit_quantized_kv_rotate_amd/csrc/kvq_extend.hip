@@ -502,18 +502,19 @@ int plan_extend_rows(const CacheGeom& c, int batch, long long rows, int max_cont
     long long want = work >= slots ? 1 : slots / work;
     const long long by_len = n_tiles / kMinTilesPerSplitX;
     if (want > by_len) want = by_len;
-    // Only the longest context is known here.  Narrow blocks (decode-like
-    // rows, where batches are ragged) take a smaller cap, so the longest
-    // sequences of a ragged batch spread over more blocks; when the cap
-    // asks for more splits than one round holds, the count is rounded up to
-    // whole rounds (a partial last round would leave most of the device idle
-    // on a batch of equal contexts).
-    const int cap = block_rows == 16 * kNarrowX ? kNarrowTilesPerSplitX : kMaxTilesPerSplitX;
-    const long long by_cap = (n_tiles + cap - 1) / cap;
-    if (want < by_cap) {
-      want = by_cap;
-      const long long per_round = work >= slots ? 0 : slots / work;
-      if (per_round > 1) want = (want + per_round - 1) / per_round * per_round;
+    // Only the longest context is known here.  A cap above one round's
+    // split count is rounded up to whole rounds (a partial last round would
+    // leave most of the device idle on a batch of equal contexts).  Narrow
+    // blocks (decode-like rows, where batches are ragged) also take a smaller
+    // cap when it asks for at least two rounds: the longest sequences of a
+    // ragged batch then spread over more blocks.
+    const long long per_round = work >= slots ? 1 : slots / work;
+    auto whole_rounds = [&](long long n) { return (n + per_round - 1) / per_round * per_round; };
+    const long long by_cap = (n_tiles + kMaxTilesPerSplitX - 1) / kMaxTilesPerSplitX;
+    if (want < by_cap) want = whole_rounds(by_cap);
+    if (block_rows == 16 * kNarrowX) {
+      const long long by_narrow = (n_tiles + kNarrowTilesPerSplitX - 1) / kNarrowTilesPerSplitX;
+      if (by_narrow >= 2 * per_round && want < by_narrow) want = whole_rounds(by_narrow);
     }
     splits = (int)(want < 1 ? 1 : want);
   }

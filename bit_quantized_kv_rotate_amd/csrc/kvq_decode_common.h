@@ -185,9 +185,50 @@ constexpr int kMaxSplits = 64;
 // reference by more than that.  The split partials carry the reference as m.
 constexpr float kLazyLog2 = 8.0f;
 
+// acc += w_s * O_s over the splits s < S (S >= 1) of one query row, in split
+// order: src(s) points at this lane's C channels of split s, and weights()
+// returns ws, whose lane s holds w_s.  The loads of eight splits are issued
+// before any is used, the first eight before weights() runs, so that they
+// share a memory round trip with the (m, l) loads weights() waits for (a loop
+// of one load and one wait per split pays a round trip per split).  Indexes
+// past S load split S - 1 again; a split of weight zero (an empty split,
+// which stores no O, or one past S) leaves acc as it is.
+template <int C, typename Src, typename Weights>
+__device__ __forceinline__ void merge_splits(float (&acc)[C], int S, Src src, Weights weights) {
+  constexpr int K = 8;
+  f32x2_t o[K][C / 2];
+  auto load = [&](int s0) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const float* ptr = src(min(s0 + k, S - 1));
+#pragma unroll
+      for (int i = 0; i < C; i += 2) o[k][i / 2] = *reinterpret_cast<const f32x2_t*>(ptr + i);
+    }
+  };
+  auto add = [&](int s0, float ws) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      const float w = as_f32((uint32_t)__builtin_amdgcn_readlane((int)as_u32(ws), s0 + k));
+#pragma unroll
+      for (int i = 0; i < C; ++i) {
+        const float f = __builtin_fmaf(w, o[k][i / 2][i & 1], acc[i]);
+        acc[i] = (w != 0.0f) ? f : acc[i];
+      }
+    }
+  };
+  load(0);
+  __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the waits in weights()
+  const float ws = weights();
+  add(0, ws);
+  for (int s0 = K; s0 < S; s0 += K) {
+    load(s0);
+    add(s0, ws);
+  }
+}
+
 // Combine the split partials of each query row: weights 2^(m_s - M),
 // normalise by the combined sum, rotate back, store.  A split of weight zero
-// (an empty one, which writes only its (m, l)) is not read.  One wave per row
+// (an empty one, which writes only its (m, l)) adds nothing.  One wave per row
 // (four per block, ROWS padded rows per (sequence, KV head), or p.rows_pad
 // when ROWS is 0); lane s < S
 // holds split s's (m, l), lane l accumulates channels C l .. C l + C - 1 of
@@ -211,29 +252,21 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeParams p) {
     ms = p.ws_ml[(row0 + (size_t)lane * ROWS) * 2 + 0];
     ls = p.ws_ml[(row0 + (size_t)lane * ROWS) * 2 + 1];
   }
-  float M = ms;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-  const float ws = (M != -INFINITY) ? __builtin_amdgcn_exp2f(ms - M) : 0.0f;
-  float lsum = ws * ls;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) lsum += __shfl_xor(lsum, o, 64);
-
+  float lsum = 0.0f;
   float acc[C];
 #pragma unroll
   for (int i = 0; i < C; ++i) acc[i] = 0.0f;
   const float* po = p.ws_o + row0 * D + C * lane;
-  for (int sp = 0; sp < S; ++sp) {
-    const float w = as_f32((uint32_t)__builtin_amdgcn_readlane((int)as_u32(ws), sp));
-    if (w == 0.0f) continue;  // an empty split stores no O
-    const float* src = po + (size_t)sp * ROWS * D;
+  merge_splits<C>(acc, S, [&](int sp) { return po + (size_t)sp * ROWS * D; }, [&] {
+    float M = ms;
 #pragma unroll
-    for (int i = 0; i < C; i += 2) {
-      const f32x2_t o = *reinterpret_cast<const f32x2_t*>(src + i);
-      acc[i] += w * o[0];
-      acc[i + 1] += w * o[1];
-    }
-  }
+    for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    const float ws = (M != -INFINITY) ? __builtin_amdgcn_exp2f(ms - M) : 0.0f;
+    lsum = ws * ls;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) lsum += __shfl_xor(lsum, o, 64);
+    return ws;
+  });
   const float inv = (lsum > 0.0f) ? 1.0f / lsum : 0.0f;
 #pragma unroll
   for (int i = 0; i < C; ++i) acc[i] *= inv;

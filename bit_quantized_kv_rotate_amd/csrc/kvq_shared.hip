@@ -67,25 +67,24 @@ __global__ __launch_bounds__(256) void shared_merge_kernel(const MergeParams m) 
     ms = ml[0];
     ls = ml[1];
   }
-  float M = ms;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-  const float ws = (M != -INFINITY) ? __builtin_amdgcn_exp2f(ms - M) : 0.0f;
-  float lsum = ws * ls;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) lsum += __shfl_xor(lsum, o, 64);
-
+  float lsum = 0.0f;
   float acc[C] = {0.0f, 0.0f};
   const float* p1 = m.o1 + ((size_t)bh * m.s1 * m.rows_seq + r) * kDS + C * lane;
   const float* p2 = m.o2 + ((size_t)bh * m.s2 * m.rows2 + r) * kDS + C * lane;
-  for (int sp = 0; sp < S; ++sp) {
-    const float w = as_f32((uint32_t)__builtin_amdgcn_readlane((int)as_u32(ws), sp));
-    if (w == 0.0f) continue;  // an empty split stores no O
-    const float* src = sp < S1 ? p1 + (size_t)sp * m.rows_seq * kDS : p2 + (size_t)(sp - S1) * m.rows2 * kDS;
-    const f32x2_t o = *reinterpret_cast<const f32x2_t*>(src);
-    acc[0] += w * o[0];
-    acc[1] += w * o[1];
-  }
+  // S >= 1: the suffix level has at least one split
+  merge_splits<C>(
+      acc, S,
+      [&](int sp) { return sp < S1 ? p1 + (size_t)sp * m.rows_seq * kDS : p2 + (size_t)(sp - S1) * m.rows2 * kDS; },
+      [&] {
+        float M = ms;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+        const float ws = (M != -INFINITY) ? __builtin_amdgcn_exp2f(ms - M) : 0.0f;
+        lsum = ws * ls;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) lsum += __shfl_xor(lsum, o, 64);
+        return ws;
+      });
   const float inv = (lsum > 0.0f) ? 1.0f / lsum : 0.0f;
   acc[0] *= inv;
   acc[1] *= inv;

@@ -185,30 +185,36 @@ constexpr int kMaxSplits = 64;
 // reference by more than that.  The split partials carry the reference as m.
 constexpr float kLazyLog2 = 8.0f;
 
-// acc += w_s * O_s over the splits s < S (S >= 1) of one query row, in split
-// order: src(s) points at this lane's C channels of split s, and weights()
-// returns ws, whose lane s holds w_s.  The loads of eight splits are issued
-// before any is used, the first eight before weights() runs, so that they
-// share a memory round trip with the (m, l) loads weights() waits for (a loop
-// of one load and one wait per split pays a round trip per split).  Indexes
-// past S load split S - 1 again; a split of weight zero (an empty split,
-// which stores no O, or one past S) leaves acc as it is.
+// acc += w_s * O_s over the splits s < S (1 <= S <= 64) of one query row, in
+// split order, skipping splits of weight zero (an empty split stores no O):
+// src(s) points at this lane's C channels of split s, and weights() returns
+// ws, whose lane s holds w_s.  The loads of eight splits are issued before
+// any is used (a loop of one load and one wait per split pays a memory round
+// trip per split).  The first eight splits are loaded before weights() runs,
+// so that their loads share a round trip with the (m, l) loads it waits for;
+// of the others only those of nonzero weight are loaded.
 template <int C, typename Src, typename Weights>
 __device__ __forceinline__ void merge_splits(float (&acc)[C], int S, Src src, Weights weights) {
   constexpr int K = 8;
   f32x2_t o[K][C / 2];
-  auto load = [&](int s0) {
+  int idx[K];
+  // the next K splits of the wave-uniform mask todo, in ascending order;
+  // past its last split, idx = -1 and split idx[0] is loaded again
+  auto load = [&](uint64_t& todo) {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      const float* ptr = src(min(s0 + k, S - 1));
+      idx[k] = todo ? __builtin_ctzll(todo) : -1;
+      todo &= todo - 1;
+      const float* ptr = src(idx[k] >= 0 ? idx[k] : idx[0]);
 #pragma unroll
       for (int i = 0; i < C; i += 2) o[k][i / 2] = *reinterpret_cast<const f32x2_t*>(ptr + i);
     }
   };
-  auto add = [&](int s0, float ws) {
+  auto add = [&](float ws) {
 #pragma unroll
     for (int k = 0; k < K; ++k) {
-      const float w = as_f32((uint32_t)__builtin_amdgcn_readlane((int)as_u32(ws), s0 + k));
+      const float wl = as_f32((uint32_t)__builtin_amdgcn_readlane((int)as_u32(ws), idx[k] & 63));
+      const float w = idx[k] >= 0 ? wl : 0.0f;
 #pragma unroll
       for (int i = 0; i < C; ++i) {
         const float f = __builtin_fmaf(w, o[k][i / 2][i & 1], acc[i]);
@@ -216,13 +222,15 @@ __device__ __forceinline__ void merge_splits(float (&acc)[C], int S, Src src, We
       }
     }
   };
-  load(0);
+  uint64_t todo = S >= K ? (1ull << K) - 1 : (1ull << S) - 1;
+  load(todo);
   __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the waits in weights()
   const float ws = weights();
-  add(0, ws);
-  for (int s0 = K; s0 < S; s0 += K) {
-    load(s0);
-    add(s0, ws);
+  add(ws);
+  todo = __ballot(ws != 0.0f) & ~((1ull << K) - 1);
+  while (todo) {
+    load(todo);
+    add(ws);
   }
 }
 

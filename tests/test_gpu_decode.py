@@ -114,6 +114,30 @@ def test_decode_split_count_invariance(gpu):
     assert_close(ref[0], want[0], "one split")
 
 
+@pytest.mark.parametrize("group,n_q", [(8, 1), (8, 3)])
+def test_decode_ragged_many_splits(gpu, group, n_q):
+    """Ragged contexts (52 .. 7425 tokens) under forced split counts up to 64:
+    the short sequences' splits past the first few are empty (weight zero),
+    the longest has 59 live splits, so the merge takes its later splits in
+    rounds of eight nonzero-weight ones, the last round partly filled.  8 rows
+    run the one-wave kernel, 24 the many-row kernel."""
+    wl = syn.Workload("ragged_splits", batch=6, num_kv_heads=1, num_q_heads=group,
+                      head_dim=128, page_size=16, context=0, n_q=n_q, ctx_range=(40, 9000), seed=1)
+    f = Filled(wl, "fp4")
+    assert list(f.plan.context_lens) == [362, 52, 1020, 7425, 1578, 1489]
+    q = syn.queries(wl).cuda()
+    want = oracle_decode_batch(f, syn.bf16_bits(q))
+    ref = None
+    for s in (1, 12, 40, 64):
+        got = f.decode(q, flags=kvq.splits_flag(s)).cpu().numpy()
+        for b in range(wl.batch):
+            assert_close(got[b], want[b], "ragged %d rows, %d splits, seq %d" % (group * n_q, s, b))
+        if ref is None:
+            ref = got
+        else:
+            np.testing.assert_allclose(got, ref, rtol=SPLIT_RTOL, atol=SPLIT_ATOL)
+
+
 def test_decode_page_permutation_invariance(gpu):
     wl = syn.WORKLOADS["tiny_b1_l256"]
     a = Filled(wl, "fp4")

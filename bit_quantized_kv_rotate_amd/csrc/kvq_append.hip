@@ -15,13 +15,24 @@ namespace {
 
 // 1-D grid, the (KV head, tensor) pair fastest: the blocks that run together
 // cover every head of the same tokens, so each token's bf16 row (all heads,
-// contiguous) is read whole at once rather than one head at a time
+// contiguous) is read whole at once rather than one head at a time.  When the
+// pair count n_ht is a multiple of 4, the four waves of a block take four
+// consecutive pairs of the same tokens (1 KB of each token's row per block,
+// and neighbouring heads' scale bytes, which share cache lines, written from
+// one compute unit): the whole b32_l32k cache build 4.77 -> 5.19 TB/s against
+// four consecutive token ranges of one pair per block.
 template <int G>
 __global__ __launch_bounds__(256) void append_kernel(const AppendParams p, unsigned n_ht) {
-  const unsigned ht = blockIdx.x % n_ht;
-  const unsigned cb = blockIdx.x / n_ht;
-  append_wave<G>(p, (int)cb * 4 + (threadIdx.x >> 6), (int)(ht % (unsigned)p.c.hkv), (int)(ht / (unsigned)p.c.hkv),
-                 threadIdx.x & 63);
+  unsigned ht, w;  // (KV head, tensor) pair, wave index within the pair's tokens
+  if ((n_ht & 3u) == 0) {
+    const unsigned q = n_ht >> 2;
+    ht = (blockIdx.x % q) * 4 + (threadIdx.x >> 6);
+    w = blockIdx.x / q;
+  } else {
+    ht = blockIdx.x % n_ht;
+    w = (blockIdx.x / n_ht) * 4 + (threadIdx.x >> 6);
+  }
+  append_wave<G>(p, (int)w, (int)(ht % (unsigned)p.c.hkv), (int)(ht / (unsigned)p.c.hkv), threadIdx.x & 63);
 }
 
 struct DequantParams {
@@ -87,7 +98,7 @@ hipError_t launch_append(const CacheGeom& c, uint8_t* kc, uint8_t* ks, uint8_t* 
   const int G = c.d / 32;
   const long long chunks = append_waves(c, n_tokens);  // waves per (head, tensor)
   const unsigned n_ht = (unsigned)c.hkv * (c.kv_shared ? 1u : 2u);
-  const long long blocks = (chunks + 3) / 4 * (long long)n_ht;
+  const long long blocks = (n_ht & 3u) == 0 ? chunks * (long long)(n_ht / 4) : (chunks + 3) / 4 * (long long)n_ht;
   if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
   const dim3 grid((unsigned)blocks);
   switch (G) {

@@ -47,7 +47,10 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=50)
+    # the page scan's time settles over the first ~150 back-to-back steps of a
+    # run (the device's clocks under sustained HBM load: 175-260 us per call at
+    # first, 176-181 us once settled), so the untimed warmup runs past that
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--replicas", type=int, default=3,
                     help="cache copies the steps rotate over (defeats last-level-cache reuse)")

@@ -105,6 +105,9 @@ def test_decode_argument_errors():
     assert _decode(fn="kvq_decode_attn_fp8", hq=8 * 32) == -4
     assert kvq.library().kvq_decode_workspace_bytes(ctypes.byref(_desc()), 2, 8 * 32, 1, 128, 0) > 0
     assert kvq.library().kvq_decode_workspace_bytes(ctypes.byref(_desc()), 2, 8 * 8193, 8, 128, 0) == 0
+    # the many-row kernel's limit, 65,536 rows per KV head, exactly: accepted; one more: not
+    assert kvq.library().kvq_decode_workspace_bytes(ctypes.byref(_desc()), 2, 8 * 8192, 8, 128, 0) > 0
+    assert kvq.library().kvq_decode_workspace_bytes(ctypes.byref(_desc()), 2, 8 * 65537, 1, 128, 0) == 0
     # latent width 512: FP4 up to 64 rows per KV head; no FP8 kernel at 512
     d512 = _desc(d=512, hkv=1, p=64, shared=1)
     L = kvq.library()

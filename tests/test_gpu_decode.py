@@ -138,6 +138,17 @@ def test_decode_ragged_many_splits(gpu, group, n_q):
             np.testing.assert_allclose(got, ref, rtol=SPLIT_RTOL, atol=SPLIT_ATOL)
 
 
+def test_decode_max_rows_per_kv_head(gpu):
+    """The many-row kernel at its limit of 65,536 query rows per KV head:
+    8,192 query heads on one KV head, 8 MTP positions (causal), 300 tokens."""
+    wl = syn.Workload("max_rows", batch=1, num_kv_heads=1, num_q_heads=8192, head_dim=128, page_size=16,
+                      context=300, n_q=8)
+    assert wl.group * wl.n_q == 65536
+    f, qh, out = _run(wl, "fp4")
+    want = oracle_decode_batch(f, qh)
+    print("65536 rows", assert_close(out[0], want[0], "65536 rows per KV head"))
+
+
 def test_decode_page_permutation_invariance(gpu):
     wl = syn.WORKLOADS["tiny_b1_l256"]
     a = Filled(wl, "fp4")

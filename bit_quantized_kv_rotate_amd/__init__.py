@@ -99,7 +99,7 @@ SIGNATURES = {
     "kvq_append_decode_attn_fp4": (ctypes.c_int, [_DESC, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _P, _I32, _P,
                                                   _I32, ctypes.c_float, _U32, _P, _P, _SZ, _P]),
     "kvq_decode_shared_workspace_bytes": (_SZ, [_DESC, _I32, _I32, _I32, _GROUPS, _U32]),
-    "kvq_decode_attn_fp4_shared": (ctypes.c_int, [_DESC, _P, _I32, _I32, _I32, _P, _I32, _P, _GROUPS,
+    "kvq_decode_attn_fp4_shared": (ctypes.c_int, [_DESC, _P, _I32, _I32, _I32, _P, _I32, _P, _I32, _GROUPS,
                                                   ctypes.c_float, _U32, _P, _P, _SZ, _P]),
     "kvq_decode_selected_workspace_bytes": (_SZ, [_DESC, _I32, _I32, _I32, _U32]),
     "kvq_decode_attn_fp4_selected": (ctypes.c_int, [_DESC, _P, _I32, _I32, _P, _I32, _P, _P, _I32,
@@ -113,13 +113,24 @@ _lib = None
 
 
 def library(path: str = LIB_PATH):
-    """Load libkvq.so (building it first only if it does not exist)."""
+    """Load libkvq.so: build it first if it does not exist; raise if it was
+    built from sources other than the ones in the tree now (a stale build
+    would run old kernels)."""
     global _lib
     if _lib is not None:
         return _lib
+    from . import _build
     if not os.path.exists(path):
-        from . import _build
         _build.build()
+    if os.path.abspath(path) == os.path.abspath(LIB_PATH):
+        try:
+            with open(_build.HASH_PATH) as f:
+                built = f.read().strip()
+        except OSError:
+            built = None
+        if built != _build.source_hash():
+            raise RuntimeError("%s is stale: it was not built from the current csrc/ and include/ "
+                               "sources; rebuild it (python __graft_entry__.py)" % path)
     L = ctypes.CDLL(path)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(L, name)
@@ -328,7 +339,8 @@ class PrefixGroups:
     host-side bounds (the fields of kvq_prefix_groups)."""
 
     def __init__(self, indptr: torch.Tensor, members: torch.Tensor, prefix_tables: torch.Tensor,
-                 shared_lens: torch.Tensor, max_group_size: int, max_suffix_len: int):
+                 shared_lens: torch.Tensor, max_group_size: int, max_suffix_len: int,
+                 max_context_len: Optional[int] = None):
         if prefix_tables.dim() != 2 or prefix_tables.shape[0] != indptr.numel() - 1:
             raise ValueError("prefix_tables must be [num_groups, max_prefix_pages]")
         if members.numel() == 0:  # no member at all: a valid pointer is still passed
@@ -336,6 +348,8 @@ class PrefixGroups:
         self.indptr, self.members = indptr, members
         self.prefix_tables, self.shared_lens = prefix_tables, shared_lens
         self.max_group_size, self.max_suffix_len = int(max_group_size), int(max_suffix_len)
+        # the longest context of the batch, if known (a default for the decode call)
+        self.max_context_len = None if max_context_len is None else int(max_context_len)
         self._desc = PrefixGroupsDesc(
             int(indptr.numel() - 1), self.max_group_size, _dev(indptr, torch.int32, "indptr"),
             _dev(members, torch.int32, "members"),
@@ -361,7 +375,8 @@ class PrefixGroups:
         suffix = max((int(L) - int(s) for L, s in zip(context_lens, shared_lens)), default=0)
         as_dev = lambda x: torch.as_tensor(x, dtype=torch.int32).to(device)
         return cls(as_dev(indptr), as_dev(members), tables.to(device), as_dev(list(shared_lens)),
-                   max(1, max(len(g) for g in groups)), max(suffix, 0))
+                   max(1, max(len(g) for g in groups)), max(suffix, 0),
+                   max((int(L) for L in context_lens), default=0))
 
     def ref(self):
         return ctypes.byref(self._desc)
@@ -377,9 +392,14 @@ def decode_attn_fp4_shared(cache: KVCache, q: torch.Tensor, block_tables: torch.
                            context_lens: torch.Tensor, groups: PrefixGroups,
                            sm_scale: Optional[float] = None, flags: int = 0,
                            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                           stream=None) -> torch.Tensor:
+                           stream=None, max_context_len: Optional[int] = None) -> torch.Tensor:
     """Shared-prefix decode: the result of decode_attn_fp4 with each group's
-    prefix pages read once for all its members."""
+    prefix pages read once for all its members.  max_context_len defaults to
+    the one the groups were built with."""
+    if max_context_len is None:
+        max_context_len = groups.max_context_len
+    if max_context_len is None:
+        raise ValueError("max_context_len is needed (the groups do not know it)")
     B, n_q, hq, d = (int(x) for x in q.shape)
     if d != cache.head_dim:
         raise ValueError("q head_dim %d does not match the cache (%d)" % (d, cache.head_dim))
@@ -404,7 +424,8 @@ def decode_attn_fp4_shared(cache: KVCache, q: torch.Tensor, block_tables: torch.
         wp = _dev(workspace, workspace.dtype, "workspace")
         wbytes = workspace.numel() * workspace.element_size()
     _check(library().kvq_decode_attn_fp4_shared(cache.ref(), qp, B, hq, n_q, bp, int(block_tables.shape[1]), cp,
-                                                 groups.ref(), float(sm_scale), int(flags), op, wp, wbytes,
+                                                 int(max_context_len), groups.ref(), float(sm_scale), int(flags),
+                                                 op, wp, wbytes,
                                                  _stream(stream)))
     return out
 

@@ -17,6 +17,11 @@ thread_local char g_msg[256];
 
 bool pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
 
+// Largest host-side token bound a call takes (max_context_len, max_selected,
+// a prefix's tokens): tile and token counts derived from it stay far from
+// int32 overflow on the host and on the device.
+constexpr int64_t kMaxTokens = (int64_t)1 << 30;
+
 // Validate a description; fills geometry.  Pointers are checked by callers
 // that use them.
 int check_desc(const kvq_cache_desc* d, CacheGeom* g) {
@@ -77,6 +82,7 @@ int decode_common(int want_fmt, const kvq_cache_desc* desc, const void* q, int32
   if (!q || !block_tables || !context_lens || !out) return KVQ_ERR_NULL;
   if (batch < 0 || num_q_heads <= 0 || n_q < 1 || max_pages_per_seq <= 0 || max_context_len < 0)
     return KVQ_ERR_SHAPE;
+  if (max_context_len > kMaxTokens) return KVQ_ERR_SHAPE;
   if (num_q_heads % g.hkv != 0) return KVQ_ERR_SHAPE;
   if ((int64_t)max_pages_per_seq * g.p < (int64_t)max_context_len) return KVQ_ERR_SHAPE;
   if (!std::isfinite(sm_scale)) return KVQ_ERR_SHAPE;
@@ -122,7 +128,8 @@ int plan_shared_call(const CacheGeom& g, int32_t batch, int32_t num_q_heads, int
       groups->max_suffix_len < 0)
     return KVQ_ERR_SHAPE;
   if (flags & ~(KVQ_Q_PREROTATED | KVQ_OUT_ROTATED | KVQ_SPLITS_MASK)) return KVQ_ERR_SHAPE;
-  if ((int64_t)groups->max_prefix_pages * g.p > INT32_MAX) return KVQ_ERR_SHAPE;
+  if ((int64_t)groups->max_prefix_pages * g.p > kMaxTokens || groups->max_suffix_len > kMaxTokens)
+    return KVQ_ERR_SHAPE;
   if (g.d != 128) return KVQ_ERR_UNSUPPORTED;
   const int64_t rows_seq = (int64_t)(num_q_heads / g.hkv) * n_q;
   if (rows_seq > 65536 || rows_seq * groups->max_group_size > 65536) return KVQ_ERR_UNSUPPORTED;
@@ -169,7 +176,7 @@ size_t kvq_decode_workspace_bytes(const kvq_cache_desc* desc, int32_t batch, int
                                   int32_t n_q, int32_t max_context_len, uint32_t flags) {
   CacheGeom g;
   if (check_desc(desc, &g) != KVQ_OK) return 0;
-  if (batch <= 0 || num_q_heads <= 0 || n_q < 1 || max_context_len < 0) return 0;
+  if (batch <= 0 || num_q_heads <= 0 || n_q < 1 || max_context_len < 0 || max_context_len > kMaxTokens) return 0;
   if (num_q_heads % g.hkv != 0) return 0;
   DecodePlan plan;
   // the decode call plans a context of at least one token, as here
@@ -189,7 +196,7 @@ size_t kvq_decode_shared_workspace_bytes(const kvq_cache_desc* desc, int32_t bat
 
 int kvq_decode_attn_fp4_shared(const kvq_cache_desc* desc, const void* q, int32_t batch,
                                int32_t num_q_heads, int32_t n_q, const int32_t* block_tables,
-                               int32_t max_pages_per_seq, const int32_t* context_lens,
+                               int32_t max_pages_per_seq, const int32_t* context_lens, int32_t max_context_len,
                                const kvq_prefix_groups* groups, float sm_scale, uint32_t flags, float* out,
                                void* workspace, size_t workspace_bytes, kvq_stream_t stream) {
   CacheGeom g;
@@ -201,13 +208,17 @@ int kvq_decode_attn_fp4_shared(const kvq_cache_desc* desc, const void* q, int32_
   if (!q || !block_tables || !context_lens || !out || !groups) return KVQ_ERR_NULL;
   if (!groups->indptr || !groups->members || !groups->prefix_tables || !groups->shared_lens)
     return KVQ_ERR_NULL;
-  if (batch < 0 || max_pages_per_seq <= 0) return KVQ_ERR_SHAPE;
+  if (batch < 0 || max_pages_per_seq <= 0 || max_context_len < 0 || max_context_len > kMaxTokens)
+    return KVQ_ERR_SHAPE;
   if (!std::isfinite(sm_scale)) return KVQ_ERR_SHAPE;
   if (batch == 0) return KVQ_OK;
   SharedPlan plan;
   st = plan_shared_call(g, batch, num_q_heads, n_q, groups, flags, &plan);
   if (st != KVQ_OK) return st;
-  if ((int64_t)max_pages_per_seq * g.p < (int64_t)groups->max_suffix_len) return KVQ_ERR_SHAPE;
+  // the suffix scan indexes block_tables[b] by token position up to
+  // context_lens[b] - 1, so a row must cover the longest context
+  if ((int64_t)max_pages_per_seq * g.p < (int64_t)max_context_len) return KVQ_ERR_SHAPE;
+  if (groups->max_suffix_len > max_context_len) return KVQ_ERR_SHAPE;
   if (!workspace || workspace_bytes < plan.workspace) return KVQ_ERR_WORKSPACE;
   if ((uintptr_t)workspace & 15u) return KVQ_ERR_WORKSPACE;
   SharedArgs a;
@@ -234,7 +245,9 @@ size_t kvq_decode_selected_workspace_bytes(const kvq_cache_desc* desc, int32_t b
                                            int32_t max_selected, uint32_t flags) {
   CacheGeom g;
   if (check_desc(desc, &g) != KVQ_OK || g.fmt != KVQ_FMT_FP4_E2M1 || g.d != 512) return 0;
-  if (batch <= 0 || num_q_heads <= 0 || max_selected < 0 || num_q_heads % g.hkv != 0) return 0;
+  if (batch <= 0 || num_q_heads <= 0 || max_selected < 0 || max_selected > kMaxTokens ||
+      num_q_heads % g.hkv != 0)
+    return 0;
   DecodePlan plan;
   if (plan_decode(g, batch, num_q_heads, 1, max_selected > 0 ? max_selected : 1, flags, &plan) != KVQ_OK) return 0;
   return plan.workspace;
@@ -251,7 +264,8 @@ int kvq_decode_attn_fp4_selected(const kvq_cache_desc* desc, const void* q, int3
   st = check_cache_ptrs(desc);
   if (st != KVQ_OK) return st;
   if (!q || !block_tables || !sel || !sel_lens || !out) return KVQ_ERR_NULL;
-  if (batch < 0 || num_q_heads <= 0 || max_pages_per_seq <= 0 || max_selected < 0) return KVQ_ERR_SHAPE;
+  if (batch < 0 || num_q_heads <= 0 || max_pages_per_seq <= 0 || max_selected < 0 || max_selected > kMaxTokens)
+    return KVQ_ERR_SHAPE;
   if (num_q_heads % g.hkv != 0) return KVQ_ERR_SHAPE;
   if (!std::isfinite(sm_scale)) return KVQ_ERR_SHAPE;
   if (flags & ~(KVQ_Q_PREROTATED | KVQ_OUT_ROTATED | KVQ_SPLITS_MASK)) return KVQ_ERR_SHAPE;

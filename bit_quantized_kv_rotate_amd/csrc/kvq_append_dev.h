@@ -21,12 +21,49 @@ namespace {
 // operand: they divide by it and round to nearest even onto the format's
 // grid, the sign copied (negative values that round to zero give the code of
 // -0).  E2M1 saturates at 6 by itself; E4M3FN does not, so values are first
-// clamped to +-448 * 2^e_s, which leaves every other code unchanged.  An
-// exhaustive comparison of these conversions with a software encoder of the
-// rounding rule (the nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 with ties to the
-// even code, saturating; E4M3FN likewise with subnormals m * 2^-9), over all
-// 2^32 fp32 inputs at scale exponents -127 .. 127, found no difference on
-// gfx950.
+// clamped to +-448 * 2^e_s, which leaves every other code unchanged.  The
+// GPU test test_gpu_convert_sweep.py compares encode_fp4_group and
+// encode_fp8_group below with the test suite's independent CPU encoders:
+// every finite fp32 input with |x| < 8 at scale 2^0 (E2M1), the grid values,
+// the ties between them and their neighbours at the extreme and middle scale
+// bytes, and random inputs over each format's whole range.
+
+// The 16 code bytes of one 32-value group at scale 2^e_s (scale: the fp32
+// whose exponent field is the group's scale byte): channel 2i in the low
+// nibble of byte i.
+__device__ __forceinline__ u32x4_t encode_fp4_group(const float (&x)[32], float scale) {
+  u32x4_t w;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    uint32_t d = 0;
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, x[8 * k + 0], x[8 * k + 1], scale, 0);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, x[8 * k + 2], x[8 * k + 3], scale, 1);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, x[8 * k + 4], x[8 * k + 5], scale, 2);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, x[8 * k + 6], x[8 * k + 7], scale, 3);
+    w[k] = d;
+  }
+  return w;
+}
+
+// The 32 E4M3 bytes of one group at scale 2^e_s, after the clamp to
+// +-448 * 2^e_s (x is clamped in place); w[0] holds channels 0..15.
+__device__ __forceinline__ void encode_fp8_group(float (&x)[32], int e_s, float scale, u32x4_t (&w)[2]) {
+  typedef __attribute__((ext_vector_type(2))) short s16x2_t;
+  const float lim = ldexpf(448.0f, e_s);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) x[i] = fminf(fmaxf(x[i], -lim), lim);
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int i = 16 * half + 4 * k;
+      s16x2_t d = {0, 0};
+      d = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(d, x[i + 0], x[i + 1], scale, false);
+      d = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(d, x[i + 2], x[i + 3], scale, true);
+      w[half][k] = __builtin_bit_cast(uint32_t, d);
+    }
+  }
+}
 
 // The value x holds in lane l ^ s (s a power of two below 64): a DPP quad
 // permutation for s = 1 and 2, the LDS permute network above.
@@ -140,36 +177,12 @@ __device__ __forceinline__ void append_wave(const AppendParams& p, int wave, int
   scales[unit] = (uint8_t)byte;
   const float scale = as_f32((uint32_t)byte << 23);  // 2^e_s (field 0: 2^-127)
   if (fp4) {
-    // channel 2i in the low nibble of byte i
-    u32x4_t w;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      uint32_t d = 0;
-      d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, x[8 * k + 0], x[8 * k + 1], scale, 0);
-      d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, x[8 * k + 2], x[8 * k + 3], scale, 1);
-      d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, x[8 * k + 4], x[8 * k + 5], scale, 2);
-      d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, x[8 * k + 6], x[8 * k + 7], scale, 3);
-      w[k] = d;
-    }
-    *reinterpret_cast<u32x4_t*>(codes) = w;
+    *reinterpret_cast<u32x4_t*>(codes) = encode_fp4_group(x, scale);
   } else {
-    typedef __attribute__((ext_vector_type(2))) short s16x2_t;
-    const float lim = ldexpf(448.0f, e_s);
-#pragma unroll
-    for (int i = 0; i < 32; ++i) x[i] = fminf(fmaxf(x[i], -lim), lim);
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      u32x4_t w;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int i = 16 * half + 4 * k;
-        s16x2_t d = {0, 0};
-        d = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(d, x[i + 0], x[i + 1], scale, false);
-        d = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(d, x[i + 2], x[i + 3], scale, true);
-        w[k] = __builtin_bit_cast(uint32_t, d);
-      }
-      *reinterpret_cast<u32x4_t*>(codes + 16 * half) = w;
-    }
+    u32x4_t w[2];
+    encode_fp8_group(x, e_s, scale, w);
+    *reinterpret_cast<u32x4_t*>(codes) = w[0];
+    *reinterpret_cast<u32x4_t*>(codes + 16) = w[1];
   }
 }
 

@@ -694,7 +694,7 @@ int plan_decode(const CacheGeom& c, int batch, int hq, int n_q, int max_context_
   plan->kind = kDecodeFew;
   const int rows = (int)rows_ll;
   const int row_tiles = (rows + 7) / 8;
-  const int n_tiles = (max_context_len + 15) / 16;
+  const int n_tiles = (int)(((long long)max_context_len + 15) / 16);
   int splits = (int)((flags & KVQ_SPLITS_MASK) >> KVQ_SPLITS_SHIFT);
   if (splits <= 0) {
     // One round of waves: as many splits as fill the device's resident wave

@@ -779,11 +779,13 @@ int plan_decode512(const CacheGeom& c, int batch, int hq, int n_q, int max_conte
                    DecodePlan* plan) {
   if (c.d != kD5) return KVQ_ERR_UNSUPPORTED;
   if (c.fmt != KVQ_FMT_FP4_E2M1) return KVQ_ERR_UNSUPPORTED;
-  const int group = hq / c.hkv;
-  const int rows = group * n_q;
+  // 64-bit before any narrowing: an int product of group and n_q could wrap
+  // to a small row count
+  const long long rows_ll = (long long)(hq / c.hkv) * n_q;
+  if (rows_ll < 1 || rows_ll > 16LL * kMaxRG5) return KVQ_ERR_UNSUPPORTED;
+  const int rows = (int)rows_ll;
   const int rg = (rows + 15) / 16;
-  if (rg > kMaxRG5) return KVQ_ERR_UNSUPPORTED;
-  const int n_tiles = (max_context_len + 15) / 16;
+  const int n_tiles = (int)(((long long)max_context_len + 15) / 16);
   int splits = (int)((flags & KVQ_SPLITS_MASK) >> KVQ_SPLITS_SHIFT);
   if (splits <= 0) {
     // one round of blocks over the device (one block per compute unit)

@@ -491,7 +491,7 @@ int plan_extend_rows(const CacheGeom& c, int batch, long long rows, int max_cont
   if (block_rows != 16 * kNarrowX && block_rows != 16 * kWideX) return KVQ_ERR_UNSUPPORTED;
   const int kRowsX = block_rows;
   const int row_blocks = (int)((rows + kRowsX - 1) / kRowsX);
-  const int n_tiles = (max_context_len + 15) / 16;
+  const int n_tiles = (int)(((long long)max_context_len + 15) / 16);
   int splits = (int)((flags & KVQ_SPLITS_MASK) >> KVQ_SPLITS_SHIFT);
   if (splits <= 0) {
     // one round of blocks over the device, at least kMinTilesPerSplitX tiles

@@ -127,7 +127,7 @@ int plan_shared(const CacheGeom& c, int batch, int hq, int n_q, const kvq_prefix
       // little beyond that member's shared length (members of one group may
       // share prefixes of very different lengths)
       [&](uint32_t f, DecodePlan* p) { return plan_extend_rows(c, g.num_groups, pre_rows, prefix_len, f, p, 32); },
-      flags, (prefix_len + 15) / 16, kPrefixTilesPerSplit, &plan->prefix);
+      flags, (int)(((long long)prefix_len + 15) / 16), kPrefixTilesPerSplit, &plan->prefix);
   if (st != KVQ_OK) return st;
   plan->prefix.kind = kDecodeMany;
   // prefix partials are stored per member sequence, not per padded unit
@@ -135,7 +135,7 @@ int plan_shared(const CacheGeom& c, int batch, int hq, int n_q, const kvq_prefix
       plan->prefix.qops_bytes + (size_t)batch * c.hkv * plan->prefix.splits * rows_seq * (kDS + 2) * sizeof(float);
   const int suffix_len = g.max_suffix_len > 0 ? g.max_suffix_len : 1;
   st = plan_level([&](uint32_t f, DecodePlan* p) { return plan_decode(c, batch, hq, n_q, suffix_len, f, p); },
-                  flags, (suffix_len + 15) / 16, kSuffixTilesPerSplit, &plan->suffix);
+                  flags, (int)(((long long)suffix_len + 15) / 16), kSuffixTilesPerSplit, &plan->suffix);
   if (st != KVQ_OK) return st;
   plan->suffix_offset = align256(plan->prefix.workspace);
   plan->workspace = plan->suffix_offset + plan->suffix.workspace;

@@ -157,7 +157,8 @@ size_t kvq_decode_workspace_bytes(const kvq_cache_desc *desc, int32_t batch,
  *                   sees tokens 0 .. context_lens[b] - n_q + j
  *   block_tables    int32 [batch][max_pages_per_seq] physical page ids
  *   context_lens    int32 [batch] (device) tokens in each sequence's cache
- *   max_context_len host-side upper bound of context_lens (sizes the grid)
+ *   max_context_len host-side upper bound of context_lens (sizes the grid),
+ *                   at most 2^30; max_pages_per_seq * page_size >= it
  *   sm_scale        softmax scale (usually 1/sqrt(head_dim))
  *   flags           KVQ_Q_PREROTATED, KVQ_OUT_ROTATED, KVQ_SPLITS(n)
  *   out             fp32 [batch][n_q][num_q_heads][head_dim]
@@ -221,7 +222,8 @@ int kvq_decode_attn_fp8(const kvq_cache_desc *desc, const void *q,
  *                    listing them by decreasing shared_lens is fastest
  *   prefix_tables    int32 [G][max_prefix_pages] (device): the physical pages
  *                    of each group's prefix, in token order
- *   max_prefix_pages row length of prefix_tables, >= 1
+ *   max_prefix_pages row length of prefix_tables, >= 1, with
+ *                    max_prefix_pages * page_size at most 2^30
  *   shared_lens      int32 [batch] (device): tokens 0 .. shared_lens[b] - 1
  *                    of sequence b are tokens 0 .. shared_lens[b] - 1 of its
  *                    group's prefix; a multiple of 16 (whole pages of any
@@ -256,8 +258,13 @@ size_t kvq_decode_shared_workspace_bytes(const kvq_cache_desc *desc,
  * starts with the pages of its group's prefix, but each group's prefix pages
  * are read once for the query rows of all its members, and each sequence's
  * own pages (tokens shared_lens[b] .. context_lens[b] - 1) once for its rows.
- *   block_tables   int32 [batch][max_pages_per_seq]; entries of tokens below
- *                  shared_lens[b] are not read
+ *   block_tables   int32 [batch][max_pages_per_seq]; row b covers the
+ *                  ceil(context_lens[b] / page_size) pages of sequence b,
+ *                  indexed by token position (entries of tokens below
+ *                  shared_lens[b] are not read)
+ *   max_context_len host-side upper bound of context_lens, at most 2^30,
+ *                  with max_pages_per_seq * page_size >= max_context_len
+ *                  and max_suffix_len <= max_context_len
  *   groups         see kvq_prefix_groups
  *   other arguments as for kvq_decode_attn_fp4; rows per KV head (n_q *
  *   num_q_heads / num_kv_heads) and rows per group (that times
@@ -270,6 +277,7 @@ int kvq_decode_attn_fp4_shared(const kvq_cache_desc *desc, const void *q,
                                const int32_t *block_tables,
                                int32_t max_pages_per_seq,
                                const int32_t *context_lens,
+                               int32_t max_context_len,
                                const kvq_prefix_groups *groups, float sm_scale,
                                uint32_t flags, float *out, void *workspace,
                                size_t workspace_bytes, kvq_stream_t stream);
@@ -288,7 +296,7 @@ int kvq_decode_attn_fp4_shared(const kvq_cache_desc *desc, const void *q,
  *                 written slot of its pages; any order; a position listed
  *                 twice counts twice
  *   sel_lens      int32 [batch] (device), 0 <= sel_lens[b] <= max_selected
- *   max_selected  host-side row length of sel (sizes the grid), >= 0
+ *   max_selected  host-side row length of sel (sizes the grid), 0 to 2^30
  *   out           fp32 [batch][1][num_q_heads][head_dim]; a sequence with no
  *                 selected position gets zeros
  *   other arguments as for kvq_decode_attn_fp4; rows per KV head

@@ -43,6 +43,8 @@ _SIGNATURES = {
     "orc_e2m1_encode": (_I, [_F, _I]),
     "orc_e4m3_value": (_D, [_I]),
     "orc_e4m3_encode": (_I, [_F, _I]),
+    "orc_e2m1_encode_n": (None, [_P, _I64, _I, _P]),
+    "orc_e4m3_encode_n": (None, [_P, _I64, _I, _P]),
     "orc_quantize_fp4_n": (None, [_P, _I64, _I, _I, _P, _P]),
     "orc_quantize_fp8_n": (None, [_P, _I64, _I, _I, _P, _P]),
     "orc_dequant_fp4_n": (None, [_P, _P, _I64, _I, _P]),
@@ -153,6 +155,16 @@ def e4m3_encode(y: float, e_s: int) -> int:
 
 
 # ---------------------------------------------------------------- vectors
+
+def encode_n(y: np.ndarray, e_s: int, fmt: str) -> np.ndarray:
+    """Codes (uint8, one per value) of fp32 values y at scale exponent e_s:
+    the E2M1 (fmt 'fp4') or E4M3 ('fp8') encoder applied to each value."""
+    y = np.ascontiguousarray(y, dtype=np.float32)
+    out = np.empty(y.shape, dtype=np.uint8)
+    fn = lib().orc_e2m1_encode_n if fmt == "fp4" else lib().orc_e4m3_encode_n
+    fn(_ptr(y), y.size, int(e_s), _ptr(out))
+    return out
+
 
 def fwht_f32(x: np.ndarray) -> np.ndarray:
     """Rotate every length-d row of ``x`` (float32, d a power of two)."""

@@ -188,6 +188,17 @@ int orc_e4m3_encode(float y, int e_s) {
   return best | (signbit(y) ? 0x80 : 0);
 }
 
+/* The two encoders over n values at one scale exponent (a loop of the
+ * single-value functions above, for sweeps over many inputs): out[i] is the
+ * code of y[i]. */
+void orc_e2m1_encode_n(const float *y, int64_t n, int e_s, uint8_t *out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)orc_e2m1_encode(y[i], e_s);
+}
+
+void orc_e4m3_encode_n(const float *y, int64_t n, int e_s, uint8_t *out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = (uint8_t)orc_e4m3_encode(y[i], e_s);
+}
+
 /* ------------------------------------------------------------------ */
 /* One head vector: rotate, then quantise group by group               */
 /* ------------------------------------------------------------------ */

@@ -118,6 +118,14 @@ def test_decode_argument_errors():
     assert _decode(fn="kvq_decode_attn_fp8", desc=_desc(fmt=2, d=512, hkv=1, p=64, shared=1), hq=64) == -4
     assert _decode(desc=d512, hq=65) == -4
     assert _decode(B=0) == 0                     # empty batch: nothing enqueued
+    # host bounds: at most 2^30 tokens of context
+    assert _decode(maxl=(1 << 30) + 1, maxp=(1 << 26) + 1) == -2
+    assert kvq.library().kvq_decode_workspace_bytes(ctypes.byref(_desc()), 2, 16, 1, (1 << 30) + 1, 0) == 0
+    # latent width: the row count in 64 bits (an int product of group and
+    # n_q that wraps must not pass as a small count)
+    assert _decode(desc=d512, hq=64, n_q=(1 << 26) + 1) == -4
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(d512), 2, 64, (1 << 26) + 1, 1024, 0) == 0
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(d512), 2, 1 << 16, 1 << 16, 1024, 0) == 0
 
 
 def test_misaligned_code_array_is_rejected():
@@ -175,11 +183,11 @@ def _groups(G=2, gmax=4, ptrs=True, maxpp=64, suffix=256):
     return kvq.PrefixGroupsDesc(G, gmax, x, x, x, maxpp, x, suffix)
 
 
-def _shared(desc=None, q=0x10, B=8, hq=64, n_q=3, bt=0x20, maxp=128, cl=0x30, groups=None, sm=0.1, flags=0,
-            out=0x40, ws=0x50, wsb=1 << 34):
+def _shared(desc=None, q=0x10, B=8, hq=64, n_q=3, bt=0x20, maxp=128, cl=0x30, maxl=2048, groups=None, sm=0.1,
+            flags=0, out=0x40, ws=0x50, wsb=1 << 34):
     desc = _desc() if desc is None else desc
     g = _groups() if groups is None else groups
-    return kvq.library().kvq_decode_attn_fp4_shared(ctypes.byref(desc), q, B, hq, n_q, bt, maxp, cl,
+    return kvq.library().kvq_decode_attn_fp4_shared(ctypes.byref(desc), q, B, hq, n_q, bt, maxp, cl, maxl,
                                                     ctypes.byref(g), sm, flags, out, ws, wsb, None)
 
 
@@ -213,7 +221,7 @@ def test_shared_argument_errors():
     assert _shared(out=None) == -1
     assert _shared(desc=_desc(ptrs=False)) == -1
     assert _shared(groups=_groups(ptrs=False)) == -1
-    assert kvq.library().kvq_decode_attn_fp4_shared(ctypes.byref(_desc()), 0x10, 8, 64, 3, 0x20, 128, 0x30,
+    assert kvq.library().kvq_decode_attn_fp4_shared(ctypes.byref(_desc()), 0x10, 8, 64, 3, 0x20, 128, 0x30, 2048,
                                                     None, 0.1, 0, 0x40, 0x50, 1 << 34, None) == -1
     assert _shared(desc=_desc(fmt=2)) == -3
     assert _shared(desc=_desc(d=64)) == -4
@@ -222,7 +230,13 @@ def test_shared_argument_errors():
     assert _shared(sm=float("nan")) == -2
     assert _shared(flags=0x8) == -2
     assert _shared(groups=_groups(G=0)) == -2
-    assert _shared(groups=_groups(suffix=128 * 16 + 1)) == -2   # suffix longer than a block table row
+    assert _shared(groups=_groups(suffix=128 * 16 + 1), maxl=128 * 16 + 1) == -2  # longer than a table row
+    assert _shared(groups=_groups(suffix=300), maxl=299) == -2  # a suffix longer than the longest context
+    # a table row must cover the whole context (the suffix scan indexes it by
+    # token position), not just the suffix
+    assert _shared(groups=_groups(suffix=256), maxp=20, maxl=20 * 16 + 1) == -2
+    assert _shared(maxl=-1) == -2
+    assert _shared(maxl=(1 << 30) + 1, maxp=(1 << 26) + 1) == -2
     assert _shared(groups=_groups(gmax=2731)) == -4
     assert _shared(ws=None, wsb=0) == -5
     L = kvq.library()
@@ -283,3 +297,19 @@ def test_append_decode_argument_errors():
     assert call(ws=None, wsb=0) == -5
     assert call(n=0, k=None, v=None, s=None, B=0) == 0      # nothing to append or attend
     assert call(desc=_desc(d=96)) == -2
+
+
+def test_library_refuses_a_stale_build(monkeypatch):
+    """library() raises, rather than loading old kernels, when libkvq.so was
+    not built from the sources in the tree (the build records their hash)."""
+    from bit_quantized_kv_rotate_amd import _build
+    with open(_build.HASH_PATH) as f:
+        assert f.read().strip() == _build.source_hash()   # the tree's build is current
+    saved = kvq._lib
+    try:
+        kvq._lib = None
+        monkeypatch.setattr(_build, "source_hash", lambda: "0" * 64)
+        with pytest.raises(RuntimeError, match="stale"):
+            kvq.library()
+    finally:
+        kvq._lib = saved

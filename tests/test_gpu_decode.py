@@ -267,3 +267,42 @@ def test_decode_many_rows_split_invariance(gpu):
     want = oracle_decode_batch(f, syn.bf16_bits(q))
     for b in range(wl.batch):
         assert_close(ref[b], want[b], "many rows one split seq %d" % b)
+
+
+@pytest.mark.parametrize("kind", ["few", "many", "latent", "shared"])
+def test_decode_ragged_splits_stale_workspace(gpu, kind):
+    """The merges skip the partial outputs of empty (zero-weight) splits, which
+    an empty split never writes: with the workspace filled with 0xFF bytes (a
+    NaN pattern) before the call, ragged contexts under forced split counts
+    still match the oracle, for the one-wave, many-row, latent-width and
+    shared-prefix kernels."""
+    if kind == "latent":
+        wl = syn.Workload("ragged_nan_latent", batch=5, num_kv_heads=1, num_q_heads=64, head_dim=512,
+                          page_size=64, context=0, ctx_range=(40, 6000), kv_shared=True, std=math.sqrt(0.5),
+                          n_outliers=4, outlier_mult=16.0, seed=2)
+    elif kind == "shared":
+        wl = syn.Workload("ragged_nan_shared", batch=6, num_kv_heads=2, num_q_heads=16, head_dim=128,
+                          page_size=16, context=0, n_q=3, ctx_range=(300, 6000), n_prefixes=2,
+                          shared_frac=0.6, seed=3)
+    else:
+        wl = syn.Workload("ragged_nan_%s" % kind, batch=6, num_kv_heads=1,
+                          num_q_heads=8, head_dim=128, page_size=16, context=0,
+                          n_q=1 if kind == "few" else 3, ctx_range=(40, 9000), seed=1)
+    f = Filled(wl, "fp4")
+    q = syn.queries(wl).cuda()
+    want = oracle_decode_batch(f, syn.bf16_bits(q.cpu()))
+    for s in (12, 40, 64) if kind != "shared" else (8, 32):
+        flags = kvq.splits_flag(s)
+        if kind == "shared":
+            groups = f.prefix_groups()
+            need = kvq.decode_shared_workspace_bytes(f.cache, wl.batch, wl.num_q_heads, wl.n_q, groups, flags)
+            ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+            got = kvq.decode_attn_fp4_shared(f.cache, q, f.block_tables, f.context_lens, groups, flags=flags,
+                                             workspace=ws).cpu().numpy()
+        else:
+            need = kvq.decode_workspace_bytes(f.cache, wl.batch, wl.num_q_heads, wl.n_q, f.max_context, flags)
+            ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+            got = kvq.decode_attn_fp4(f.cache, q, f.block_tables, f.context_lens, f.max_context, flags=flags,
+                                      workspace=ws).cpu().numpy()
+        for b in range(wl.batch):
+            assert_close(got[b], want[b], "%s, %d splits, seq %d, stale workspace" % (kind, s, b))

@@ -468,3 +468,17 @@ def test_selected_matches_numpy_over_listed_rows():
     # the duplicate matters: without it the result moves
     other = oracle.decode_selected(qb, khat, vhat, [5, 3, 20, 39, 0], True, sm)
     assert np.abs(other - got).max() > 1e-6
+
+
+def test_batch_encoders_are_the_single_value_encoders():
+    """encode_n (the sweep's batch form) is the per-value encoder applied to
+    each input, at several scale exponents, both formats."""
+    rng = np.random.default_rng(7)
+    for e in (-127, -3, 0, 5, 127):
+        x = (rng.standard_normal(300) * 4.0 * 2.0 ** e).astype(np.float32)
+        x[:3] = [0.0, -0.0, np.float32(2.5 * 2.0 ** e)]
+        np.testing.assert_array_equal(oracle.encode_n(x, e, "fp4"),
+                                      [oracle.e2m1_encode(float(v), e) for v in x])
+        y = (x.astype(np.float64) * 60.0)
+        y = y[np.abs(y) < np.finfo(np.float32).max].astype(np.float32)
+        np.testing.assert_array_equal(oracle.encode_n(y, e, "fp8"), [oracle.e4m3_encode(float(v), e) for v in y])

@@ -55,14 +55,18 @@ def parse():
     ap.add_argument("--replicas", type=int, default=3,
                     help="cache copies the steps rotate over (defeats last-level-cache reuse)")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
-                    help="target CPU time of each oracle baseline sample")
+                    help="target time of the single-threaded oracle sample")
     ap.add_argument("--cpu-threads", type=int, default=0,
-                    help="threads of the parallel oracle sample (0: host cores, at most 16)")
+                    help="threads of the parallel oracle leg (0: every CPU this process may run on)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-fp8", action="store_true")
     ap.add_argument("--no-mla", action="store_true", help="skip the head_dim 512 latent decode")
     ap.add_argument("--no-mix", action="store_true", help="skip the shared-prefix MTP mix")
     ap.add_argument("--no-extend", action="store_true", help="skip the extend-chunk attention")
+    ap.add_argument("--clock-trace", action="store_true",
+                    help="sample the shader clock (one side-stream wave) during the warmup and "
+                         "timed steps, and record clocks and socket power over 2.5 s of "
+                         "sustained FP4 steps and FP8 calls (needs bench_clock.so)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain fp32 elementwise kernel over 2 x 512 MiB "
                          "(reference for the HBM byte counters)")
@@ -149,6 +153,160 @@ def replicate(kvq, c, n):
             r.v_scales.copy_(c.v_scales)
         reps.append(r)
     return reps
+
+
+def abba(stream, fa, fb, n):
+    """Paired timing in ABBA order (a, b, b, a), three repeats: returns the
+    median of the paired means of a and b (ms per call, each the median of
+    n HIP-event timed calls) and the median of the paired ratios b / a."""
+    import torch
+
+    def timed(fn):
+        es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for i, (x, y) in enumerate(es):
+            x.record(stream)
+            fn(i)
+            y.record(stream)
+        torch.cuda.synchronize()
+        return statistics.median([x.elapsed_time(y) for x, y in es])
+
+    ta, tb, ratios = [], [], []
+    for _ in range(3):
+        a1 = timed(fa)
+        b1 = timed(fb)
+        b2 = timed(fb)
+        a2 = timed(fa)
+        ta.append((a1 + a2) / 2)
+        tb.append((b1 + b2) / 2)
+        ratios.append(tb[-1] / ta[-1])
+    return statistics.median(ta), statistics.median(tb), statistics.median(ratios)
+
+
+class ClockSampler:
+    """Shader clock over time: one wave of bench_clock.so on a side stream (at
+    the default priority) records (wall clock, shader clock) pairs every 5 us
+    while the work under test runs on the main stream."""
+
+    def __init__(self, dev, stream):
+        import ctypes
+        import torch
+        path = os.path.join(ROOT, "bench_clock.so")
+        if not os.path.exists(path):
+            raise RuntimeError("--clock-trace needs bench_clock.so (run __graft_entry__.build())")
+        self.lib = ctypes.CDLL(path)
+        self.lib.bench_clock_launch.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_ulonglong, ctypes.c_void_p]
+        khz = ctypes.c_int(0)
+        if self.lib.bench_clock_wall_khz(ctypes.byref(khz)) != 0 or khz.value <= 0:
+            raise RuntimeError("wall-clock rate unavailable")
+        self.wall_khz = khz.value
+        self.dev, self.stream = dev, stream
+        self.side = torch.cuda.Stream(device=dev)
+        # first launch (module load, side queue) before anything is timed
+        buf = torch.zeros(2, dtype=torch.int64, device=dev)
+        if self.lib.bench_clock_launch(ctypes.c_void_p(buf.data_ptr()), 1, 1,
+                                       ctypes.c_void_p(self.side.cuda_stream)) != 0:
+            raise RuntimeError("bench_clock_launch failed")
+        torch.cuda.synchronize()
+
+    def start(self, ms):
+        import ctypes
+        import torch
+        self.interval = max(1, self.wall_khz // 200)          # 5 us
+        self.n = int(ms * 200)
+        self.buf = torch.zeros(2 * self.n, dtype=torch.int64, device=self.dev)
+        self.base = torch.cuda.Event(enable_timing=True)
+        self.base.record(self.stream)
+        self.side.wait_stream(self.stream)
+        rc = self.lib.bench_clock_launch(ctypes.c_void_p(self.buf.data_ptr()), self.n, self.interval,
+                                         ctypes.c_void_p(self.side.cuda_stream))
+        if rc != 0:
+            raise RuntimeError("bench_clock_launch failed (%d)" % rc)
+        time.sleep(0.001)   # let the sampling wave start before the work under test
+
+    def finish(self, window_ms=1.0):
+        import torch
+        torch.cuda.synchronize()
+        s = self.buf.view(self.n, 2).cpu().numpy().astype("float64")
+        k = max(1, int(window_ms * 200))
+        out = []
+        for i in range(0, self.n - k, k):
+            dw = s[i + k, 0] - s[i, 0]
+            out.append(round((s[i + k, 1] - s[i, 1]) / dw * self.wall_khz / 1000.0) if dw > 0 else None)
+        return out
+
+
+def cold_start_trace(fn, stream, sampler, idle_s, n):
+    """After idle_s seconds of idle device, n calls of fn back to back with
+    the shader clock sampled beside them: the clock per 1 ms window and each
+    call's HIP-event time, on one time base (ms from the sampler's start)."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    time.sleep(idle_s)
+    sampler.start(max(40.0, 0.5 * n))
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        fn(i)
+        b.record(stream)
+    stream.synchronize()
+    return {
+        "idle_s_before": idle_s,
+        "sclk_mhz_per_ms": sampler.finish(),
+        "call_ms": [round(a.elapsed_time(b), 4) for a, b in ev],
+        "call_start_ms": [round(sampler.base.elapsed_time(a), 3) for a, _ in ev],
+        "note": "shader clock from one sampling wave on a side stream, per 1 ms window; "
+                "call_start_ms on the same time base",
+    }
+
+
+def sustained(fn, stream, seconds, sampler=None):
+    """Call fn back to back for about `seconds`; report the mean time per
+    call, the mean shader clock (sampling wave) and the socket power and
+    clocks the SMU reports (amdsmi, updated about once a second) after the
+    first second."""
+    import torch
+    smi = None
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        smi = (amdsmi, amdsmi.amdsmi_get_processor_handles()[0])
+    except Exception:
+        smi = None
+    if sampler:
+        sampler.start(seconds * 1000.0 + 50.0)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    n, power, gfx = 0, [], []
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(50):
+            fn(n)
+            n += 1
+        stream.synchronize()   # not the device: the sampling wave runs on another stream
+        if smi and time.perf_counter() - t0 > 1.0:
+            try:
+                m = smi[0].amdsmi_get_gpu_metrics_info(smi[1])
+                ts = m.get("firmware_timestamp")
+                if not power or ts != power[-1][0]:
+                    power.append((ts, m.get("current_socket_power")))
+                    gfx.append(sum(m["current_gfxclks"]) / len(m["current_gfxclks"]))
+            except Exception:
+                pass
+    e1.record(stream)
+    stream.synchronize()
+    res = {"calls": n, "ms_per_call": round(e0.elapsed_time(e1) / n, 4)}
+    if sampler:
+        clk = [x for x in sampler.finish(window_ms=100.0) if x]
+        res["sclk_mhz_mean"] = round(statistics.fmean(clk[10:])) if len(clk) > 10 else None
+    if power:
+        res["socket_power_w"] = [p for _, p in power]
+        res["smi_gfxclk_mhz"] = [round(g) for g in gfx]
+    if smi:
+        try:
+            smi[0].amdsmi_shut_down()
+        except Exception:
+            pass
+    return res
 
 
 def main():
@@ -250,37 +408,17 @@ def main():
     # ---------------- FP4 vs FP8, ABBA (median of three paired-mean ratios)
     fp8 = None
     if c8 is not None:
-        def timed(fn, n):
-            es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(n)]
-            for i, (a, b) in enumerate(es):
-                a.record(stream)
-                fn(i)
-                b.record(stream)
-            torch.cuda.synchronize()
-            return statistics.median([a.elapsed_time(b) for a, b in es])
         for i in range(5):
             dec8(i)
         torch.cuda.synchronize()
-        ratios, t4s, t8s = [], [], []
-        n = max(args.steps // 2, 24)
-        for _ in range(3):
-            a1 = timed(dec4, n)
-            b1 = timed(dec8, n)
-            b2 = timed(dec8, n)
-            a2 = timed(dec4, n)
-            t4, t8 = (a1 + a2) / 2, (b1 + b2) / 2
-            t4s.append(t4)
-            t8s.append(t8)
-            ratios.append(t8 / t4)
-        t8m, t4m = statistics.median(t8s), statistics.median(t4s)
+        t4m, t8m, ratio = abba(stream, dec4, dec8, max(args.steps // 2, 24))
         fp8 = {
             "decode_ms": round(t8m, 4),
             "kv_gbs": round(kv_fp8 / (t8m * 1e-3) / 1e9, 1),
             "hbm_frac": round(kv_fp8 / (t8m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
             "fp4_decode_ms": round(t4m, 4),
             "fp4_kv_gbs": round(kv_fp4 / (t4m * 1e-3) / 1e9, 1),
-            "speedup_fp4_vs_fp8": round(statistics.median(ratios), 3),
+            "speedup_fp4_vs_fp8": round(ratio, 3),
             "kv_bytes": kv_fp8,
             "byte_ratio": round(kv_fp8 / kv_fp4, 4),
         }
@@ -328,10 +466,15 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # ---------------- 8K context: FP4 vs FP8 (ABBA), replicas past the last-level cache
+    small = None
+    if not args.no_fp8:
+        small = bench_small(kvq, syn, dev, stream, max(args.steps // 2, 24))
+
     # ---------------- agentic mix: shared prefixes, MTP verify positions
     mix = fork = None
     if not args.no_mix:
-        mix = bench_mix(kvq, syn, dev, stream, max(args.steps // 2, 20), R)
+        mix = bench_mix(kvq, syn, dev, stream, max(args.steps // 2, 20), R, fp8=not args.no_fp8)
         fork = bench_mix(kvq, syn, dev, stream, max(args.steps // 2, 20), R, name="fork_b32_l32k")
 
     # ---------------- extend chunk (many query rows per KV head, MFMA-bound)
@@ -343,6 +486,20 @@ def main():
     mla = None
     if not args.no_mla:
         mla = bench_latent(kvq, syn, dev, stream, max(args.steps // 2, 20), R)
+
+    # ---------------- shader clock of a cold start, clocks and socket power
+    # under sustained calls (diagnostic: after the timed region)
+    clock_trace = None
+    if args.clock_trace:
+        sampler = ClockSampler(dev, stream)
+        clock_trace = {"cold_start": cold_start_trace(step, stream, sampler, 1.5, 5 + 100)}
+        time.sleep(1.0)
+        clock_trace["sustained_fp4_step"] = sustained(step, stream, 2.5, sampler)
+        time.sleep(1.0)
+        if c8 is not None:
+            # without the sampling wave: at 252 registers two FP8 decode waves
+            # fill a SIMD's register file, so the sampler would take a slot
+            clock_trace["sustained_fp8_decode"] = sustained(dec8, stream, 2.5)
 
     # ---------------- CPU oracle baseline on a bounded sample
     cpu = None
@@ -380,6 +537,7 @@ def main():
             "bytes_per_launch": dec_alg,
         },
         "fp8_comparator": fp8,
+        "context_8k": small,
         "append_bulk": append_bulk,
         "agentic_mix": mix,
         "fork_prefix": fork,
@@ -387,6 +545,8 @@ def main():
         "latent_512": mla,
         "cpu_baseline": cpu,
     }
+    if clock_trace:
+        res["clock_trace"] = clock_trace
     print(json.dumps(res), flush=True)
 
 
@@ -395,7 +555,85 @@ PEAK_FP4_FP6 = 10100.0
 PEAK_BF16 = 2500.0
 
 
-def bench_mix(kvq, syn, dev, stream, steps, R, name="mtp_mixed_b32"):
+def mfma_roofline(D, row_tokens, t_ms):
+    """MFMA roofline of an attention call over row_tokens (query row, token)
+    pairs at head_dim D.  Algorithmic work: 2 D flops for the score and 2 D
+    for the value product per pair, each priced at the dense MFMA peak of the
+    type it runs in (scores: FP4 cache x FP6 query, 10.1 PF/s; values: bf16,
+    2.5 PF/s).  frac = the time that work needs at those peaks over the
+    measured time.  The flops the kernels issue are larger (four FP6 query
+    terms, P as bf16 hi + lo): their fraction is issued_frac."""
+    t = t_ms * 1e-3
+    qk, pv = 2.0 * D * row_tokens, 2.0 * D * row_tokens
+    t_alg = qk / (PEAK_FP4_FP6 * 1e12) + pv / (PEAK_BF16 * 1e12)
+    qk_i, pv_i = qk * 4, pv * 2
+    t_iss = qk_i / (PEAK_FP4_FP6 * 1e12) + pv_i / (PEAK_BF16 * 1e12)
+    return {
+        "bound": "mfma", "unit": "TFLOP/s",
+        "achieved": round((qk + pv) / t / 1e12, 1),
+        "peak": round((qk + pv) / t_alg / 1e12, 1),
+        "frac": round(t_alg / t, 4),
+        "traffic": None,
+        "issued_tflops": round((qk_i + pv_i) / t / 1e12, 1),
+        "issued_frac": round(t_iss / t, 4),
+        "note": "algorithmic flops (4 D per row-token: QK^T at the FP4 x FP6 peak 10.1 PF/s, PV at the "
+                "bf16 peak 2.5 PF/s); issued: four FP6 query terms and bf16 hi + lo P",
+    }
+
+
+def bench_small(kvq, syn, dev, stream, steps, name="b8_l8k", min_bytes=512e6):
+    """FP4 against FP8 decode at 8K context (batch 8, 8 KV / 64 query heads,
+    head_dim 128, permuted pages): ABBA timings of one decode call, each
+    format rotating over enough cache replicas that they total more than
+    512 MB, so that no call finds its cache (71 MB FP4, 138 MB FP8) in the
+    256 MB last-level cache left by the calls before it."""
+    import numpy as np
+    import torch
+    wl = syn.WORKLOADS[name]
+    plan = syn.page_plan(wl)
+    c4, _ = build_cache(kvq, syn, wl, plan, kvq.FMT_FP4_E2M1, dev)
+    c8, _ = build_cache(kvq, syn, wl, plan, kvq.FMT_FP8_E4M3, dev)
+    r4 = int(math.ceil(min_bytes / c4.nbytes)) + 1
+    r8 = int(math.ceil(min_bytes / c8.nbytes)) + 1
+    c4s, c8s = replicate(kvq, c4, r4), replicate(kvq, c8, r8)
+    q = syn.queries(wl, dev)
+    bt = torch_from(plan.block_tables, dev)
+    cl = torch_from(plan.context_lens, dev)
+    maxL = int(plan.context_lens.max())
+    B, HQ, NQ, D, H = wl.batch, wl.num_q_heads, wl.n_q, wl.head_dim, wl.num_kv_heads
+    out = torch.empty((B, NQ, HQ, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(kvq.decode_workspace_bytes(c4, B, HQ, NQ, maxL),
+                         kvq.decode_workspace_bytes(c8, B, HQ, NQ, maxL)), dtype=torch.uint8, device=dev)
+
+    def d4(i):
+        kvq.decode_attn_fp4(c4s[i % r4], q, bt, cl, maxL, out=out, workspace=ws, stream=stream)
+
+    def d8(i):
+        kvq.decode_attn_fp8(c8s[i % r8], q, bt, cl, maxL, out=out, workspace=ws, stream=stream)
+
+    for i in range(2 * max(r4, r8)):
+        d4(i)
+        d8(i)
+    torch.cuda.synchronize()
+    t4, t8, ratio = abba(stream, d4, d8, steps)
+    tok = int(plan.context_lens.astype(np.int64).sum()) * H
+    kv4, kv8 = tok * (D // 2 + D // 32) * 2, tok * (D + D // 32) * 2
+    del c4s, c8s, c4, c8
+    return {
+        "workload": "%s: %s" % (wl.name, wl.description),
+        "replicas": {"fp4": r4, "fp8": r8},
+        "fp4_decode_ms": round(t4, 4),
+        "fp4_kv_gbs": round(kv4 / (t4 * 1e-3) / 1e9, 1),
+        "fp4_hbm_frac": round(kv4 / (t4 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "fp8_decode_ms": round(t8, 4),
+        "fp8_kv_gbs": round(kv8 / (t8 * 1e-3) / 1e9, 1),
+        "fp8_hbm_frac": round(kv8 / (t8 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "speedup_fp4_vs_fp8": round(ratio, 3),
+        "kv_bytes": {"fp4": kv4, "fp8": kv8},
+    }
+
+
+def bench_mix(kvq, syn, dev, stream, steps, R, name="mtp_mixed_b32", fp8=False):
     """Decode over a batch with shared prefixes and 3 MTP verify positions:
     the agentic mix (mtp_mixed_b32: contexts 4K-128K, 92% of each sequence's
     pages shared from 4 prefixes, so members share prefixes of different
@@ -438,15 +676,46 @@ def bench_mix(kvq, syn, dev, stream, steps, R, name="mtp_mixed_b32"):
     ws2 = torch.empty(kvq.decode_shared_workspace_bytes(c, B, HQ, NQ, groups), dtype=torch.uint8, device=dev)
     out2 = torch.empty_like(out)
     for i in range(5):
-        kvq.decode_attn_fp4_shared(cs[i % R], q, bt, cl, groups, out=out2, workspace=ws2, stream=stream)
+        kvq.decode_attn_fp4_shared(cs[i % R], q, bt, cl, groups, out=out2, workspace=ws2, stream=stream,
+                                   max_context_len=maxL)
     torch.cuda.synchronize()
     for i, (a, b) in enumerate(es):
         a.record(stream)
-        kvq.decode_attn_fp4_shared(cs[i % R], q, bt, cl, groups, out=out2, workspace=ws2, stream=stream)
+        kvq.decode_attn_fp4_shared(cs[i % R], q, bt, cl, groups, out=out2, workspace=ws2, stream=stream,
+                                   max_context_len=maxL)
         b.record(stream)
     torch.cuda.synchronize()
     t2 = statistics.fmean([a.elapsed_time(b) for a, b in es])
     max_diff = float((out2 - out).abs().max())
+
+    # the same plain decode over an FP8 cache of the same inputs, ABBA
+    fp8_res = None
+    if fp8:
+        c8, _ = build_cache(kvq, syn, wl, plan, kvq.FMT_FP8_E4M3, dev)
+        c8s = replicate(kvq, c8, R)
+        ws8 = torch.empty(kvq.decode_workspace_bytes(c8, B, HQ, NQ, maxL), dtype=torch.uint8, device=dev)
+        out8 = torch.empty_like(out)
+
+        def d4(i):
+            kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream)
+
+        def d8(i):
+            kvq.decode_attn_fp8(c8s[i % R], q, bt, cl, maxL, out=out8, workspace=ws8, stream=stream)
+
+        for i in range(5):
+            d8(i)
+        torch.cuda.synchronize()
+        t4a, t8a, ratio = abba(stream, d4, d8, steps)
+        logical8 = int(plan.context_lens.astype(np.int64).sum()) * (D + D // 32) * 2 * wl.num_kv_heads
+        fp8_res = {
+            "fp4_decode_ms": round(t4a, 4),
+            "fp8_decode_ms": round(t8a, 4),
+            "speedup_fp4_vs_fp8": round(ratio, 3),
+            "fp8_logical_gbs": round(logical8 / (t8a * 1e-3) / 1e9, 1),
+            "note": "plain decode, ABBA; the FP8 kernel runs the 24 rows per KV head as three 8-row tiles "
+                    "of one wave, the FP4 call the many-row kernel",
+        }
+        del c8s, c8
 
     per_tok = (D // 2 + D // 32) * 2 * wl.num_kv_heads
     logical = int(plan.context_lens.astype(np.int64).sum()) * per_tok
@@ -471,6 +740,7 @@ def bench_mix(kvq, syn, dev, stream, steps, R, name="mtp_mixed_b32"):
             "max_abs_diff_vs_plain": max_diff,
             "note": "kvq_decode_attn_fp4_shared, one group per prefix (%d)" % wl.n_prefixes,
         },
+        "fp8_comparator": fp8_res,
     }
 
 
@@ -510,10 +780,7 @@ def bench_extend(kvq, syn, dev, stream, steps, R, chunk=1024):
     visible = NQ * (L - NQ) + NQ * (NQ + 1) // 2          # (position, token) pairs per query head
     row_tokens = float(visible) * HQ * B
     alg_flops = 4.0 * D * row_tokens
-    qk_flops = 2.0 * D * row_tokens * 4
-    pv_flops = 2.0 * D * row_tokens * 2
-    t_peak = qk_flops / (PEAK_FP4_FP6 * 1e12) + pv_flops / (PEAK_BF16 * 1e12)
-    issued = qk_flops + pv_flops
+    roof = mfma_roofline(D, row_tokens, t)
     del cs, c
     return {
         "workload": "extend_b4_l32k: %s" % wl.description,
@@ -522,15 +789,7 @@ def bench_extend(kvq, syn, dev, stream, steps, R, chunk=1024):
         "decode_ms_events_mean": round(t, 4),
         "algorithmic_tflops": round(alg_flops / (t * 1e-3) / 1e12, 1),
         "tokens_per_s": round(B * NQ / (t * 1e-3), 1),
-        "roofline": {
-            "bound": "mfma", "unit": "TFLOP/s",
-            "achieved": round(issued / (t * 1e-3) / 1e12, 1),
-            "peak": round(issued / t_peak / 1e12, 1),
-            "frac": round(t_peak / (t * 1e-3), 4),
-            "traffic": None,
-            "note": "issued MFMA flops (QK^T 4 FP4xFP6 terms at 10.1 PF/s, PV bf16 hi+lo at 2.5 PF/s); "
-                    "peak = their time-weighted dense peak",
-        },
+        "roofline": roof,
     }
 
 
@@ -566,10 +825,7 @@ def bench_latent(kvq, syn, dev, stream, steps, R, name="mla_b16_l128k"):
     tokens = int(plan.context_lens.astype(np.int64).sum()) * wl.num_kv_heads
     rows = wl.group * NQ
     alg_flops = 4.0 * D * rows * tokens                 # QK^T + PV, single term
-    qk_flops = 2.0 * D * rows * tokens * 4              # four FP6 query terms
-    pv_flops = 2.0 * D * rows * tokens * 2              # P hi + lo
-    t_peak = qk_flops / (PEAK_FP4_FP6 * 1e12) + pv_flops / (PEAK_BF16 * 1e12)
-    issued = qk_flops + pv_flops
+    roof = mfma_roofline(D, float(rows) * tokens, t)
     kv_bytes = tokens * (D // 2 + D // 32)
 
     # selected-position decode over the same cache: per sequence 512 pooled
@@ -607,24 +863,18 @@ def bench_latent(kvq, syn, dev, stream, steps, R, name="mla_b16_l128k"):
         "kv_gbs": round(kv_bytes / (t * 1e-3) / 1e9, 1),
         "hbm_frac": round(kv_bytes / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "algorithmic_tflops": round(alg_flops / (t * 1e-3) / 1e12, 1),
-        "roofline": {
-            "bound": "mfma", "unit": "TFLOP/s",
-            "achieved": round(issued / (t * 1e-3) / 1e12, 1),
-            "peak": round(issued / t_peak / 1e12, 1),
-            "frac": round(t_peak / (t * 1e-3), 4),
-            "traffic": None,
-            "note": "issued MFMA flops (QK^T 4 FP4xFP6 terms at 10.1 PF/s, PV bf16 hi+lo at 2.5 PF/s); "
-                    "peak = their time-weighted dense peak",
-        },
+        "roofline": roof,
     }
 
 
 def cpu_baseline(wl, plan, target_s, threads):
-    """Time the oracle - dequantise the FP4 cache of one (sequence, KV head)
-    and run fp64 decode attention for its query heads - over (sequence, KV
-    head) items: first single-threaded until about target_s seconds, then on
-    `threads` host threads (the oracle's C code runs without the GIL) for
-    about target_s seconds of CPU time.  Reports KV GB/s."""
+    """Time the oracle on the host over the decode step of the workload: for
+    every (sequence, KV head), dequantise its FP4 K/V cache and run fp64
+    decode attention for its query heads.  The parallel leg runs every item
+    of the step (256 at b32_l32k: the whole 1.14 GB cache) on `threads` host
+    threads (the oracle's C code runs without the GIL); the single-threaded
+    leg runs items until about target_s seconds.  The oracle quantises the
+    FP4 inputs beforehand on the same threads, untimed.  Reports KV GB/s."""
     from concurrent.futures import ThreadPoolExecutor
 
     import numpy as np
@@ -637,19 +887,10 @@ def cpu_baseline(wl, plan, target_s, threads):
     g = wl.group
     sm = 1.0 / math.sqrt(wl.head_dim)
     if threads <= 0:
-        threads = min(16, os.cpu_count() or 1)
-    # sequence-major, so each sequence's K/V is drawn once per pass
+        threads = len(os.sched_getaffinity(0))
     order = [(b, h) for b in range(wl.batch) for h in range(wl.num_kv_heads)]
-    seq_cache = {}
 
-    def item(b, h):
-        """Quantised FP4 K/V of one (sequence, KV head) - not timed."""
-        if b not in seq_cache:
-            seq_cache.clear()
-            k = syn.bf16_bits(syn.sequence_kv(wl, plan, "k", b, dev))
-            v = None if wl.kv_shared else syn.bf16_bits(syn.sequence_kv(wl, plan, "v", b, dev))
-            seq_cache[b] = (k, v)
-        k, v = seq_cache[b]
+    def quant(k, v, h):
         kc, ks = oracle.quantize_fp4(np.ascontiguousarray(k[:, h:h + 1]), True)
         vc, vs = (None, None) if v is None else oracle.quantize_fp4(np.ascontiguousarray(v[:, h:h + 1]), True)
         return kc, ks, vc, vs
@@ -660,34 +901,44 @@ def cpu_baseline(wl, plan, target_s, threads):
         oracle.decode(q[b][:, h * g:(h + 1) * g], khat, vhat, True, sm)
         return kc.shape[0] * (kc.shape[-1] + ks.shape[-1]) * (1 if vc is None else 2)
 
-    # single thread
+    # inputs of every item, quantised by the oracle on the host threads (untimed)
+    t_prep = time.perf_counter()
+    items = {}
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        for b in range(wl.batch):
+            k = syn.bf16_bits(syn.sequence_kv(wl, plan, "k", b, dev))
+            v = None if wl.kv_shared else syn.bf16_bits(syn.sequence_kv(wl, plan, "v", b, dev))
+            futs = {h: ex.submit(quant, k, v, h) for h in range(wl.num_kv_heads)}
+            for h, fu in futs.items():
+                items[(b, h)] = fu.result()
+    t_prep = time.perf_counter() - t_prep
+
+    # single thread, a sample
     t1, b1, n1 = 0.0, 0, 0
     for b, h in order:
-        args = item(b, h)
         t0 = time.perf_counter()
-        b1 += work(b, h, *args)
+        b1 += work(b, h, *items[(b, h)])
         t1 += time.perf_counter() - t0
         n1 += 1
         if t1 >= target_s:
             break
-    per_item = t1 / n1
-    # parallel: enough items for about target_s of CPU time, inputs prepared first
-    n_par = max(threads, int(math.ceil(target_s / per_item / threads)) * threads)
-    items = [(b, h) + item(b, h) for b, h in (order * (n_par // len(order) + 1))[:n_par]]
+    # all items of the step on the host threads
     t0 = time.perf_counter()
     with ThreadPoolExecutor(max_workers=threads) as ex:
-        bpar = sum(ex.map(lambda a: work(*a), items))
+        bpar = sum(ex.map(lambda bh: work(bh[0], bh[1], *items[bh]), order))
     tpar = time.perf_counter() - t0
     return {
         "value": round(bpar / tpar / 1e9, 4),
         "unit": "GB/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": "%d (sequence, KV head) items of %s (%d tokens each): dequantise the "
-                  "FP4 K/V and run fp64 decode attention for %d query heads, on %d threads "
-                  "in %.2f s wall" % (n_par, wl.name, int(plan.context_lens[0]), g, threads, tpar),
+        "sample": "the whole decode step of %s: all %d (sequence, KV head) items (%d tokens each, "
+                  "%d B of FP4 KV): dequantise and run fp64 decode attention for %d query heads, on %d "
+                  "threads in %.2f s wall (inputs quantised by the oracle beforehand in %.1f s, untimed)"
+                  % (wl.name, len(order), int(plan.context_lens[0]), bpar, g, threads, tpar, t_prep),
         "single_thread": {"value": round(b1 / t1 / 1e9, 4), "unit": "GB/s", "items": n1,
                           "seconds": round(t1, 2)},
+        "host_cpus": os.cpu_count(),
         "cpu": cpu_model(),
     }
 

@@ -36,7 +36,9 @@ SPLITS_MASK = 0x0FFF0000
 ERRORS = {
     -1: "KVQ_ERR_NULL", -2: "KVQ_ERR_SHAPE", -3: "KVQ_ERR_FORMAT",
     -4: "KVQ_ERR_UNSUPPORTED", -5: "KVQ_ERR_WORKSPACE", -6: "KVQ_ERR_HIP",
+    -7: "KVQ_ERR_SCRATCH",
 }
+SCRATCH_BYTES = 32 << 20      # KVQ_SCRATCH_BYTES
 
 
 def splits_flag(n: int) -> int:
@@ -96,6 +98,8 @@ SIGNATURES = {
                                            ctypes.c_float, _U32, _P, _P, _SZ, _P]),
     "kvq_decode_attn_fp8": (ctypes.c_int, [_DESC, _P, _I32, _I32, _I32, _P, _I32, _P, _I32,
                                            ctypes.c_float, _U32, _P, _P, _SZ, _P]),
+    "kvq_decode_attn_fp4_scratch": (ctypes.c_int, [_DESC, _P, _I32, _I32, _I32, _P, _I32, _P, _I32,
+                                                   ctypes.c_float, _U32, _P, _P]),
     "kvq_append_decode_attn_fp4": (ctypes.c_int, [_DESC, _P, _P, _P, _I32, _P, _I32, _I32, _I32, _P, _I32, _P,
                                                   _I32, ctypes.c_float, _U32, _P, _P, _SZ, _P]),
     "kvq_decode_shared_workspace_bytes": (_SZ, [_DESC, _I32, _I32, _I32, _GROUPS, _U32]),
@@ -277,6 +281,30 @@ def decode_attn_fp4(cache: KVCache, q: torch.Tensor, block_tables: torch.Tensor,
     """q: bf16 [batch, n_q, num_q_heads, head_dim]; returns fp32 of that shape."""
     return _decode("kvq_decode_attn_fp4", cache, q, block_tables, context_lens, max_context_len,
                    sm_scale, flags, out, workspace, stream)
+
+
+def decode_attn_fp4_scratch(cache: KVCache, q: torch.Tensor, block_tables: torch.Tensor,
+                            context_lens: torch.Tensor, max_context_len: int, out: torch.Tensor,
+                            sm_scale: Optional[float] = None, flags: int = 0, stream=None) -> torch.Tensor:
+    """decode_attn_fp4 on the library's static scratch array (no workspace):
+    the caller passes `out`; nothing is allocated."""
+    B, n_q, hq, d = (int(x) for x in q.shape)
+    if d != cache.head_dim:
+        raise ValueError("q head_dim %d does not match the cache (%d)" % (d, cache.head_dim))
+    qp = _dev(q, torch.bfloat16, "q")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [batch, max_pages]")
+    bp = _dev(block_tables, torch.int32, "block_tables")
+    _shape(context_lens, (B,), "context_lens")
+    cp = _dev(context_lens, torch.int32, "context_lens")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(d)
+    _shape(out, (B, n_q, hq, d), "out")
+    op = _dev(out, torch.float32, "out")
+    _check(library().kvq_decode_attn_fp4_scratch(cache.ref(), qp, B, hq, n_q, bp, int(block_tables.shape[1]),
+                                                  cp, int(max_context_len), float(sm_scale), int(flags), op,
+                                                  _stream(stream)))
+    return out
 
 
 def append_decode_attn_fp4(cache: KVCache, k_new: torch.Tensor, v_new: Optional[torch.Tensor],

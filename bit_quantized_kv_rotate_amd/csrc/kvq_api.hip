@@ -1,10 +1,18 @@
 // C entry points of libkvq: argument checks on the host, then kernel
 // launches on the caller's stream.  Nothing here allocates device memory or
 // synchronises.
+#include <atomic>
 #include <cmath>
 #include <cstdio>
+#include <mutex>
 
 #include "kvq_internal.h"
+
+// Scratch of kvq_decode_attn_fp4_scratch: one copy per device, resident while
+// the code object is loaded.  Host code must not pass `scratch` itself to a
+// kernel (on the host the name is a stand-in, not a device address): it uses
+// the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[KVQ_SCRATCH_BYTES];
 
 namespace kvq {
 
@@ -68,11 +76,42 @@ int hip_status(hipError_t e) {
   return KVQ_ERR_HIP;
 }
 
+// Device address of the current device's `scratch` array, looked up once per
+// device (with that device current) and kept; nullptr if the lookup fails.
+constexpr int kScratchDevices = 64;
+
+void* scratch_address() {
+  static std::atomic<void*> addr[kScratchDevices];
+  static std::mutex mu;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kScratchDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(mu);
+  p = addr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    void* q = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !q) {
+      g_last_hip = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    p = q;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
 int decode_common(int want_fmt, const kvq_cache_desc* desc, const void* q, int32_t batch,
                   int32_t num_q_heads, int32_t n_q, const int32_t* block_tables,
                   int32_t max_pages_per_seq, const int32_t* context_lens, int32_t max_context_len,
                   float sm_scale, uint32_t flags, float* out, void* workspace,
-                  size_t workspace_bytes, kvq_stream_t stream, const AppendArgs* append = nullptr) {
+                  size_t workspace_bytes, kvq_stream_t stream, const AppendArgs* append = nullptr,
+                  bool use_scratch = false) {
   CacheGeom g;
   int st = check_desc(desc, &g);
   if (st != KVQ_OK) return st;
@@ -97,6 +136,13 @@ int decode_common(int want_fmt, const kvq_cache_desc* desc, const void* q, int32
   DecodePlan plan;
   st = plan_decode(g, batch, num_q_heads, n_q, max_context_len > 0 ? max_context_len : 1, flags, &plan);
   if (st != KVQ_OK) return st;
+  if (use_scratch) {
+    // the allocation-free entry point: the static array instead of a workspace
+    if (plan.workspace > KVQ_SCRATCH_BYTES) return KVQ_ERR_SCRATCH;
+    workspace = scratch_address();
+    if (!workspace) return KVQ_ERR_HIP;
+    workspace_bytes = KVQ_SCRATCH_BYTES;
+  }
   if (plan.workspace > 0 && (!workspace || workspace_bytes < plan.workspace)) return KVQ_ERR_WORKSPACE;
   if ((uintptr_t)workspace & 15u) return KVQ_ERR_WORKSPACE;
   DecodeArgs a;
@@ -329,6 +375,16 @@ int kvq_decode_attn_fp4(const kvq_cache_desc* desc, const void* q, int32_t batch
                        workspace, workspace_bytes, stream);
 }
 
+int kvq_decode_attn_fp4_scratch(const kvq_cache_desc* desc, const void* q, int32_t batch,
+                                int32_t num_q_heads, int32_t n_q, const int32_t* block_tables,
+                                int32_t max_pages_per_seq, const int32_t* context_lens,
+                                int32_t max_context_len, float sm_scale, uint32_t flags, float* out,
+                                kvq_stream_t stream) {
+  return decode_common(KVQ_FMT_FP4_E2M1, desc, q, batch, num_q_heads, n_q, block_tables,
+                       max_pages_per_seq, context_lens, max_context_len, sm_scale, flags, out,
+                       nullptr, 0, stream, nullptr, /*use_scratch=*/true);
+}
+
 int kvq_decode_attn_fp8(const kvq_cache_desc* desc, const void* q, int32_t batch,
                         int32_t num_q_heads, int32_t n_q, const int32_t* block_tables,
                         int32_t max_pages_per_seq, const int32_t* context_lens,
@@ -361,6 +417,7 @@ const char* kvq_strerror(int status) {
     case KVQ_ERR_FORMAT: return "cache format does not match the call";
     case KVQ_ERR_UNSUPPORTED: return "no kernel is built for this shape";
     case KVQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case KVQ_ERR_SCRATCH: return "the call needs more than the library's static scratch (KVQ_SCRATCH_BYTES)";
     case KVQ_ERR_HIP:
       snprintf(g_msg, sizeof g_msg, "HIP error: %s", hipGetErrorString(g_last_hip));
       return g_msg;

@@ -20,7 +20,9 @@
  *   - Every pointer argument that names tensor data is a DEVICE pointer owned
  *     by the caller.  The library allocates nothing, keeps no state between
  *     calls beyond a cache of device properties (compute units, kernel
- *     occupancy), never synchronises, and enqueues its kernels on `stream`.
+ *     occupancy) and the static scratch array of
+ *     kvq_decode_attn_fp4_scratch, never synchronises, and enqueues its
+ *     kernels on `stream`.
  *   - Arguments are checked on the host before any HIP call; on a failed
  *     check nothing is enqueued and the call returns a negative KVQ_ERR_*.
  *   - Contract violations that can only be seen on the device (a block-table
@@ -70,6 +72,7 @@ extern "C" {
 #define KVQ_ERR_UNSUPPORTED (-4) /* valid, but no kernel is built for it */
 #define KVQ_ERR_WORKSPACE (-5)   /* workspace missing or too small */
 #define KVQ_ERR_HIP (-6)         /* a HIP runtime call failed */
+#define KVQ_ERR_SCRATCH (-7)     /* needs more than KVQ_SCRATCH_BYTES of scratch */
 
 /* ---- cache formats ---------------------------------------------------- */
 #define KVQ_FMT_FP4_E2M1 1 /* 16 code bytes + 1 scale byte per 32 values */
@@ -196,6 +199,33 @@ int kvq_append_decode_attn_fp4(const kvq_cache_desc *desc, const void *k_new,
                                int32_t max_context_len, float sm_scale,
                                uint32_t flags, float *out, void *workspace,
                                size_t workspace_bytes, kvq_stream_t stream);
+/* Bytes of the library's static device scratch array (32 MiB), the most a
+ * kvq_decode_attn_fp4_scratch call may need (kvq_decode_workspace_bytes of
+ * its sizes). */
+#define KVQ_SCRATCH_BYTES ((size_t)32 << 20)
+
+/* kvq_decode_attn_fp4 without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  The query operands and split partials
+ * go to a file-scope static device array of KVQ_SCRATCH_BYTES bytes that the
+ * library holds on every device it runs on until the process ends; the call
+ * itself allocates nothing.  Arguments, results and flags are those of
+ * kvq_decode_attn_fp4 (the same kernels, the same plan, so the same output);
+ * the scratch needs no initialisation.  All calls on one device share that
+ * device's array: calls that overlap in time on one device (two streams, two
+ * threads) race and give undefined results; calls ordered on one stream do
+ * not.  Returns the errors of kvq_decode_attn_fp4, with KVQ_ERR_SCRATCH in
+ * place of KVQ_ERR_WORKSPACE when the sizes need more than
+ * KVQ_SCRATCH_BYTES. */
+int kvq_decode_attn_fp4_scratch(const kvq_cache_desc *desc, const void *q,
+                                int32_t batch, int32_t num_q_heads,
+                                int32_t n_q, const int32_t *block_tables,
+                                int32_t max_pages_per_seq,
+                                const int32_t *context_lens,
+                                int32_t max_context_len, float sm_scale,
+                                uint32_t flags, float *out,
+                                kvq_stream_t stream);
+
 /* The same decode over an FP8 (E4M3, per-32 UE8M0 scale) cache: the 8-bit
  * comparator of "UltraQuant vs 8-bit KV".  Identical arguments; returns
  * KVQ_ERR_FORMAT unless desc->format == KVQ_FMT_FP8_E4M3, and

@@ -55,7 +55,7 @@ def test_bad_geometry_sizes_zero(kw):
 
 
 def test_strerror_texts():
-    for st in (0, -1, -2, -3, -4, -5, -6):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7):
         assert kvq.strerror(st)
     assert "HIP" in kvq.strerror(-6)
 
@@ -297,6 +297,32 @@ def test_append_decode_argument_errors():
     assert call(ws=None, wsb=0) == -5
     assert call(n=0, k=None, v=None, s=None, B=0) == 0      # nothing to append or attend
     assert call(desc=_desc(d=96)) == -2
+
+
+def _scratch(desc=None, q=0x10, B=2, hq=16, n_q=1, bt=0x20, maxp=8, cl=0x30, maxl=128, sm=0.1, flags=0,
+             out=0x40):
+    desc = _desc() if desc is None else desc
+    return kvq.library().kvq_decode_attn_fp4_scratch(ctypes.byref(desc), q, B, hq, n_q, bt, maxp, cl, maxl,
+                                                     sm, flags, out, None)
+
+
+def test_scratch_decode_argument_errors():
+    """The allocation-free decode checks its arguments like the workspace
+    call, and refuses (before any HIP call) sizes that need more than the
+    static scratch array holds."""
+    assert _scratch(q=None) == -1
+    assert _scratch(out=None) == -1
+    assert _scratch(hq=12) == -2
+    assert _scratch(maxp=4, maxl=128) == -2
+    assert _scratch(desc=_desc(fmt=2)) == -3
+    assert _scratch(desc=_desc(d=64)) == -4
+    assert _scratch(B=0) == 0
+    L = kvq.library()
+    big = dict(B=64, hq=64, maxl=1 << 20, maxp=(1 << 20) // 16)
+    d64 = _desc(hkv=64)
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(d64), 64, 64, 1, 1 << 20, 0) > kvq.SCRATCH_BYTES
+    assert _scratch(desc=d64, **big) == -7
+    assert "scratch" in kvq.strerror(-7)
 
 
 def test_library_refuses_a_stale_build(monkeypatch):

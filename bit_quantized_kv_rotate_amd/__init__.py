@@ -23,7 +23,8 @@ from typing import Optional, Sequence, Tuple
 import torch  # loads torch's HIP runtime first; libkvq then shares it
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkvq.so")
+# KVQ_LIBRARY names another build of the library (the sanitizer run's)
+LIB_PATH = os.environ.get("KVQ_LIBRARY") or os.path.join(_HERE, "libkvq.so")
 
 KVQ_OK = 0
 FMT_FP4_E2M1 = 1
@@ -124,17 +125,17 @@ def library(path: str = LIB_PATH):
     if _lib is not None:
         return _lib
     from . import _build
-    if not os.path.exists(path):
+    if not os.path.exists(path) and os.path.abspath(path) == os.path.abspath(_build.LIB_PATH):
         _build.build()
-    if os.path.abspath(path) == os.path.abspath(LIB_PATH):
-        try:
-            with open(_build.HASH_PATH) as f:
-                built = f.read().strip()
-        except OSError:
-            built = None
-        if built != _build.source_hash():
-            raise RuntimeError("%s is stale: it was not built from the current csrc/ and include/ "
-                               "sources; rebuild it (python __graft_entry__.py)" % path)
+    # every build records the hash of its sources beside the library
+    try:
+        with open(path + ".srchash") as f:
+            built = f.read().strip()
+    except OSError:
+        built = None
+    if built != _build.source_hash():
+        raise RuntimeError("%s is stale: it was not built from the current csrc/ and include/ "
+                           "sources; rebuild it (python __graft_entry__.py)" % path)
     L = ctypes.CDLL(path)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(L, name)

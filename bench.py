@@ -35,6 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+QK_FLAGS = 0          # decode flags of the FP4 calls (KVQ_QK_CONVERT with --qk-convert)
 WORKLOAD = "b32_l32k"
 # HBM traffic of one append + decode call, measured with rocprofv3 counters and
 # scaled by a plain copy kernel; valid only for the kernel source it names.
@@ -63,6 +64,12 @@ def parse():
     ap.add_argument("--no-mla", action="store_true", help="skip the head_dim 512 latent decode")
     ap.add_argument("--no-mix", action="store_true", help="skip the shared-prefix MTP mix")
     ap.add_argument("--no-extend", action="store_true", help="skip the extend-chunk attention")
+    ap.add_argument("--sections", default="all",
+                    help="comma list of the sections run after the timed step: fp8 (also the 8K "
+                         "comparison), append, mix, fork, extend, latent, cpu; default all")
+    ap.add_argument("--qk-convert", action="store_true",
+                    help="FP4 decode calls compute scores by converting the K codes to bf16 "
+                         "(KVQ_QK_CONVERT), the route the native scaled-MFMA scores are compared with")
     ap.add_argument("--clock-trace", action="store_true",
                     help="sample the shader clock (one side-stream wave) during the warmup and "
                          "timed steps, and record clocks and socket power over 2.5 s of "
@@ -311,6 +318,8 @@ def sustained(fn, stream, seconds, sampler=None):
 
 def main():
     args = parse()
+    want = set(s.strip() for s in args.sections.split(",")) if args.sections != "all" else None
+    on = lambda s: want is None or s in want
     if args.gpus != 1:
         print("bench.py measures one GPU: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -323,6 +332,8 @@ def main():
     import kvq_synth as syn
 
     torch.cuda.set_device(0)
+    global QK_FLAGS
+    QK_FLAGS = kvq.QK_CONVERT if args.qk_convert else 0
     wl = syn.WORKLOADS[args.workload]
     plan = syn.page_plan(wl)
     P, H, D = wl.page_size, wl.num_kv_heads, wl.head_dim
@@ -334,7 +345,7 @@ def main():
     t0 = time.time()
     c4, last = build_cache(kvq, syn, wl, plan, kvq.FMT_FP4_E2M1, dev)
     c8 = None
-    if not args.no_fp8:
+    if not args.no_fp8 and on("fp8"):
         c8, _ = build_cache(kvq, syn, wl, plan, kvq.FMT_FP8_E4M3, dev)
     torch.cuda.synchronize()
     c4s = replicate(kvq, c4, R)
@@ -353,7 +364,7 @@ def main():
     maxL = int(plan.context_lens.max())
     out4 = torch.empty((B, NQ, HQ, D), dtype=torch.float32, device=dev)
     out8 = torch.empty_like(out4)
-    ws_bytes = max(kvq.decode_workspace_bytes(c4, B, HQ, NQ, maxL),
+    ws_bytes = max(kvq.decode_workspace_bytes(c4, B, HQ, NQ, maxL, QK_FLAGS),
                    0 if c8 is None else kvq.decode_workspace_bytes(c8, B, HQ, NQ, maxL))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
@@ -362,10 +373,10 @@ def main():
         # one decode step in one call: append the new token of every sequence,
         # then attend over the whole cache
         kvq.append_decode_attn_fp4(c4s[i % R], step_k, step_v, step_slots, q, bt, cl, maxL, out=out4,
-                                   workspace=ws, stream=stream)
+                                   workspace=ws, stream=stream, flags=QK_FLAGS)
 
     def dec4(i):
-        kvq.decode_attn_fp4(c4s[i % R], q, bt, cl, maxL, out=out4, workspace=ws, stream=stream)
+        kvq.decode_attn_fp4(c4s[i % R], q, bt, cl, maxL, out=out4, workspace=ws, stream=stream, flags=QK_FLAGS)
 
     def dec8(i):
         kvq.decode_attn_fp8(c8s[i % R], q, bt, cl, maxL, out=out8, workspace=ws, stream=stream)
@@ -426,36 +437,38 @@ def main():
     # ---------------- bulk append: the whole cache build in one call (every
     # sequence's tokens, 4.29 GB of bf16 K and V in, 1.14 GB of FP4 codes and
     # scales out), re-appended over a replica (rewrites identical codes)
-    parts = {t: [] for t in syn.tensor_names(wl)}
-    sl_parts = []
-    for b in range(B):
-        n_sh = plan.n_shared_pages[b] * P
-        Lb = int(plan.context_lens[b]) - n_sh
-        for t in parts:
-            parts[t].append(syn.private_tokens(wl, t, b, Lb, dev))
-        sl_parts.append(torch_from(syn.slots_for(plan.private_pages[b], Lb, P), dev))
-    kv0 = {t: torch.cat(x) for t, x in parts.items()}
-    sl0 = torch.cat(sl_parts)
-    del parts, sl_parts
-    L0 = int(sl0.numel())
-    torch.cuda.synchronize()
-    app_ms = []
-    for r in range(12):
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        kvq.rotate_quantize_append(c4s[r % R], kv0["k"], kv0.get("v"), sl0, stream=stream)
-        b.record(stream)
+    append_bulk = None
+    if on("append"):
+        parts = {t: [] for t in syn.tensor_names(wl)}
+        sl_parts = []
+        for b in range(B):
+            n_sh = plan.n_shared_pages[b] * P
+            Lb = int(plan.context_lens[b]) - n_sh
+            for t in parts:
+                parts[t].append(syn.private_tokens(wl, t, b, Lb, dev))
+            sl_parts.append(torch_from(syn.slots_for(plan.private_pages[b], Lb, P), dev))
+        kv0 = {t: torch.cat(x) for t, x in parts.items()}
+        sl0 = torch.cat(sl_parts)
+        del parts, sl_parts
+        L0 = int(sl0.numel())
         torch.cuda.synchronize()
-        app_ms.append(a.elapsed_time(b))
-    app_t = statistics.median(app_ms[2:])
-    app_bytes = L0 * H * n_t * (2 * D + D // 2 + D // 32) + L0 * 4
-    append_bulk = {
-        "tokens": L0, "ms": round(app_t, 4),
-        "bytes": app_bytes, "gbs": round(app_bytes / (app_t * 1e-3) / 1e9, 1),
-        "hbm_frac": round(app_bytes / (app_t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "note": "the whole cache build in one call: bf16 K and V read, FP4 codes + scales written, slot ids read",
-    }
-    del kv0, sl0
+        app_ms = []
+        for r in range(12):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            kvq.rotate_quantize_append(c4s[r % R], kv0["k"], kv0.get("v"), sl0, stream=stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            app_ms.append(a.elapsed_time(b))
+        app_t = statistics.median(app_ms[2:])
+        app_bytes = L0 * H * n_t * (2 * D + D // 2 + D // 32) + L0 * 4
+        append_bulk = {
+            "tokens": L0, "ms": round(app_t, 4),
+            "bytes": app_bytes, "gbs": round(app_bytes / (app_t * 1e-3) / 1e9, 1),
+            "hbm_frac": round(app_bytes / (app_t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "note": "the whole cache build in one call: bf16 K and V read, FP4 codes + scales written, slot ids read",
+        }
+        del kv0, sl0
 
     if args.copy_calibration:
         # torch's elementwise kernel: reads 512 MiB, writes 512 MiB
@@ -468,23 +481,24 @@ def main():
 
     # ---------------- 8K context: FP4 vs FP8 (ABBA), replicas past the last-level cache
     small = None
-    if not args.no_fp8:
+    if not args.no_fp8 and on("fp8"):
         small = bench_small(kvq, syn, dev, stream, max(args.steps // 2, 24))
 
     # ---------------- agentic mix: shared prefixes, MTP verify positions
     mix = fork = None
-    if not args.no_mix:
-        mix = bench_mix(kvq, syn, dev, stream, max(args.steps // 2, 20), R, fp8=not args.no_fp8)
+    if not args.no_mix and on("mix"):
+        mix = bench_mix(kvq, syn, dev, stream, max(args.steps // 2, 20), R, fp8=not args.no_fp8 and on("fp8"))
+    if not args.no_mix and on("fork"):
         fork = bench_mix(kvq, syn, dev, stream, max(args.steps // 2, 20), R, name="fork_b32_l32k")
 
     # ---------------- extend chunk (many query rows per KV head, MFMA-bound)
     ext = None
-    if not args.no_extend:
+    if not args.no_extend and on("extend"):
         ext = bench_extend(kvq, syn, dev, stream, max(args.steps // 10, 10), R)
 
     # ---------------- latent-width decode (head_dim 512, MFMA-bound)
     mla = None
-    if not args.no_mla:
+    if not args.no_mla and on("latent"):
         mla = bench_latent(kvq, syn, dev, stream, max(args.steps // 2, 20), R)
 
     # ---------------- shader clock of a cold start, clocks and socket power
@@ -503,7 +517,7 @@ def main():
 
     # ---------------- CPU oracle baseline on a bounded sample
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and on("cpu"):
         cpu = cpu_baseline(wl, plan, args.cpu_seconds, args.cpu_threads)
 
     res = {
@@ -517,7 +531,10 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp4 e2m1 cache; scaled fp4 x fp6 MFMA scores, bf16 hi/lo MFMA PV, fp32 accumulate",
+        "dtype": ("fp4 e2m1 cache; scaled fp4 x fp6 MFMA scores, bf16 hi/lo MFMA PV, fp32 accumulate"
+                  if not args.qk_convert else
+                  "fp4 e2m1 cache; codes converted to bf16 for bf16 hi/lo MFMA scores, bf16 hi/lo MFMA PV, "
+                  "fp32 accumulate"),
         "data": "synthetic (seeded bf16 N(0,1) + outlier channels; no trace or dataset)",
         "config": {
             "workload": "%s: %s" % (wl.name, wl.description),
@@ -654,14 +671,14 @@ def bench_mix(kvq, syn, dev, stream, steps, R, name="mtp_mixed_b32", fp8=False):
     maxL = int(plan.context_lens.max())
     B, HQ, NQ, D = wl.batch, wl.num_q_heads, wl.n_q, wl.head_dim
     out = torch.empty((B, NQ, HQ, D), dtype=torch.float32, device=dev)
-    ws = torch.empty(kvq.decode_workspace_bytes(c, B, HQ, NQ, maxL), dtype=torch.uint8, device=dev)
+    ws = torch.empty(kvq.decode_workspace_bytes(c, B, HQ, NQ, maxL, QK_FLAGS), dtype=torch.uint8, device=dev)
     for i in range(5):
-        kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream)
+        kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream, flags=QK_FLAGS)
     torch.cuda.synchronize()
     es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for i, (a, b) in enumerate(es):
         a.record(stream)
-        kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream)
+        kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream, flags=QK_FLAGS)
         b.record(stream)
     torch.cuda.synchronize()
     t = statistics.fmean([a.elapsed_time(b) for a, b in es])
@@ -697,7 +714,7 @@ def bench_mix(kvq, syn, dev, stream, steps, R, name="mtp_mixed_b32", fp8=False):
         out8 = torch.empty_like(out)
 
         def d4(i):
-            kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream)
+            kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream, flags=QK_FLAGS)
 
         def d8(i):
             kvq.decode_attn_fp8(c8s[i % R], q, bt, cl, maxL, out=out8, workspace=ws8, stream=stream)
@@ -765,14 +782,14 @@ def bench_extend(kvq, syn, dev, stream, steps, R, chunk=1024):
     maxL = int(plan.context_lens.max())
     B, HQ, NQ, D = wl.batch, wl.num_q_heads, wl.n_q, wl.head_dim
     out = torch.empty((B, NQ, HQ, D), dtype=torch.float32, device=dev)
-    ws = torch.empty(kvq.decode_workspace_bytes(c, B, HQ, NQ, maxL), dtype=torch.uint8, device=dev)
+    ws = torch.empty(kvq.decode_workspace_bytes(c, B, HQ, NQ, maxL, QK_FLAGS), dtype=torch.uint8, device=dev)
     for i in range(3):
-        kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream)
+        kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream, flags=QK_FLAGS)
     torch.cuda.synchronize()
     es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for i, (a, b) in enumerate(es):
         a.record(stream)
-        kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream)
+        kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream, flags=QK_FLAGS)
         b.record(stream)
     torch.cuda.synchronize()
     t = statistics.fmean([a.elapsed_time(b) for a, b in es])
@@ -811,14 +828,14 @@ def bench_latent(kvq, syn, dev, stream, steps, R, name="mla_b16_l128k"):
     maxL = int(plan.context_lens.max())
     B, HQ, NQ, D = wl.batch, wl.num_q_heads, wl.n_q, wl.head_dim
     out = torch.empty((B, NQ, HQ, D), dtype=torch.float32, device=dev)
-    ws = torch.empty(kvq.decode_workspace_bytes(c, B, HQ, NQ, maxL), dtype=torch.uint8, device=dev)
+    ws = torch.empty(kvq.decode_workspace_bytes(c, B, HQ, NQ, maxL, QK_FLAGS), dtype=torch.uint8, device=dev)
     for i in range(10):
-        kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream)
+        kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream, flags=QK_FLAGS)
     torch.cuda.synchronize()
     es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for i, (a, b) in enumerate(es):
         a.record(stream)
-        kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream)
+        kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream, flags=QK_FLAGS)
         b.record(stream)
     torch.cuda.synchronize()
     t = statistics.fmean([a.elapsed_time(b) for a, b in es])

@@ -31,6 +31,7 @@ FMT_FP4_E2M1 = 1
 FMT_FP8_E4M3 = 2
 Q_PREROTATED = 0x1
 OUT_ROTATED = 0x2
+QK_CONVERT = 0x4
 SPLITS_SHIFT = 16
 SPLITS_MASK = 0x0FFF0000
 

@@ -125,7 +125,7 @@ int decode_common(int want_fmt, const kvq_cache_desc* desc, const void* q, int32
   if (num_q_heads % g.hkv != 0) return KVQ_ERR_SHAPE;
   if ((int64_t)max_pages_per_seq * g.p < (int64_t)max_context_len) return KVQ_ERR_SHAPE;
   if (!std::isfinite(sm_scale)) return KVQ_ERR_SHAPE;
-  if (flags & ~(KVQ_Q_PREROTATED | KVQ_OUT_ROTATED | KVQ_SPLITS_MASK)) return KVQ_ERR_SHAPE;
+  if (flags & ~(KVQ_Q_PREROTATED | KVQ_OUT_ROTATED | KVQ_QK_CONVERT | KVQ_SPLITS_MASK)) return KVQ_ERR_SHAPE;
   if (batch == 0) {
     // nothing to attend to; an append still runs
     if (append && append->n_tokens > 0)

@@ -62,27 +62,26 @@ struct Ring {
 };
 
 // Query operands of the score product.
-//  FP4 cache: kQTerms FP6 terms for the scaled MFMA (6 packed dwords + scale).
-//  FP8 cache: bf16 hi + lo parts for the bf16 MFMA (4 k-steps of 32 channels).
+//  Native FP4 scores: kQTerms FP6 terms for the scaled MFMA (6 packed dwords
+//  + scale).  FP8 cache, and FP4 through the conversion route: bf16 hi + lo
+//  parts for the bf16 MFMA (4 k-steps of 32 channels).
 template <int FMT, int NT>
-struct QOps;
+struct QOps {
+  bf16x8_t b[NT][4];
+};
 template <int NT>
 struct QOps<KVQ_FMT_FP4_E2M1, NT> {
   i32x8_t b[NT][kQMfma];
   int sc[NT][kQMfma];
 };
-template <int NT>
-struct QOps<KVQ_FMT_FP8_E4M3, NT> {
-  bf16x8_t b[NT][4];
-};
 
 // Workspace image of the query operands: per (sequence, KV head, row tile)
-// kSlots operands of kDwords per lane (FP4: 6 packed FP6 dwords + scale +
-// pad; FP8: one bf16x8 = 4 dwords).
+// kSlots operands of kDwords per lane (FP6 terms: 6 packed dwords + scale +
+// pad; bf16 hi / lo: one bf16x8 = 4 dwords).
 template <int FMT>
 struct QOpsLayout {
-  static constexpr int kSlots = (FMT == KVQ_FMT_FP4_E2M1) ? kQMfma : 4;
-  static constexpr int kDwords = (FMT == KVQ_FMT_FP4_E2M1) ? 8 : 4;
+  static constexpr int kSlots = Fmt<FMT>::kNativeQK ? kQMfma : 4;
+  static constexpr int kDwords = Fmt<FMT>::kNativeQK ? 8 : 4;
 };
 
 template <int FMT>
@@ -172,7 +171,7 @@ __device__ __forceinline__ void compute_pair(const DecodeParams& p, const int32_
   constexpr bool kLate = NT >= 2;
   auto scores_t = [&](int s, int t) -> f32x4_t {
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    if constexpr (Fmt<FMT>::kFP4) {
+    if constexpr (Fmt<FMT>::kNativeQK) {
       // FP4 codes and UE8M0 scales straight into the scaled MFMA (A operand)
       const i32x8_t A = {(int)r[s].k[0], (int)r[s].k[1], (int)r[s].k[2], (int)r[s].k[3], 0, 0, 0, 0};
 #pragma unroll
@@ -180,7 +179,8 @@ __device__ __forceinline__ void compute_pair(const DecodeParams& p, const int32_
         acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, q.b[t][m], acc, 4, 2, 0, (int)r[s].ksc, 0,
                                                                q.sc[t][m]);
     } else {
-      // E4M3 codes dequantised to bf16 (exact) as the A operand of bf16 MFMAs
+      // E4M3 (or, on the conversion route, E2M1) codes dequantised with their
+      // scale to bf16 (exact) as the A operand of bf16 MFMAs
       uint32_t kb[16];
       dequant_group<FMT>(r[s].k, scale_operand(r[s].ksc), kb);
 #pragma unroll
@@ -358,7 +358,7 @@ __device__ __forceinline__ void qprep_row(const DecodeParams& p, int gr, int lan
   const int t = r >> 3;
   const int c7 = r & 7;
   uint32_t* base = p.qops + (size_t)bh * NT * kS * 64 * kW;
-  if constexpr (Fmt<FMT>::kFP4) {
+  if constexpr (Fmt<FMT>::kNativeQK) {
     // kQTerms FP6 (E2M3) terms per 32-channel block (16 lanes), each with its
     // own UE8M0 scale and carrying the previous residual.  The block's 32
     // six-bit codes form a 192-bit little-endian stream: lane i of the block
@@ -495,7 +495,7 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
       for (int m = 0; m < kS; ++m) {
         const uint32_t* w = src + (size_t)(t * kS + m) * 64 * kW;
         const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(w);
-        if constexpr (Fmt<FMT>::kFP4) {
+        if constexpr (Fmt<FMT>::kNativeQK) {
           const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(w + 4);
           q.b[t][m] = i32x8_t{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], 0, 0};
           q.sc[t][m] = (int)a1[2];
@@ -658,19 +658,26 @@ int resident_waves_nt(int dev) {
   return v;
 }
 
-int resident_waves(int fmt, int row_tiles) {
+template <int FMT>
+int resident_waves_fmt(int dev, int row_tiles) {
+  switch (row_tiles) {
+    case 1: return resident_waves_nt<FMT, 1>(dev);
+    case 2: return resident_waves_nt<FMT, 2>(dev);
+    case 3: return resident_waves_nt<FMT, 3>(dev);
+    default: return 0;
+  }
+}
+
+// kernel format: the cache's, or the FP4 conversion route
+int resident_waves(int kfmt, int row_tiles) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
-  const bool fp4 = fmt == KVQ_FMT_FP4_E2M1;
-  switch (row_tiles) {
-    case 1: return fp4 ? resident_waves_nt<KVQ_FMT_FP4_E2M1, 1>(dev) : resident_waves_nt<KVQ_FMT_FP8_E4M3, 1>(dev);
-    case 2: return fp4 ? resident_waves_nt<KVQ_FMT_FP4_E2M1, 2>(dev) : resident_waves_nt<KVQ_FMT_FP8_E4M3, 2>(dev);
-    case 3: return fp4 ? resident_waves_nt<KVQ_FMT_FP4_E2M1, 3>(dev) : resident_waves_nt<KVQ_FMT_FP8_E4M3, 3>(dev);
-    default: return 0;
-  }
+  if (kfmt == KVQ_FMT_FP4_E2M1) return resident_waves_fmt<KVQ_FMT_FP4_E2M1>(dev, row_tiles);
+  if (kfmt == kFmtFP4Conv) return resident_waves_fmt<kFmtFP4Conv>(dev, row_tiles);
+  return resident_waves_fmt<KVQ_FMT_FP8_E4M3>(dev, row_tiles);
 }
 
 }  // namespace
@@ -692,6 +699,9 @@ int plan_decode(const CacheGeom& c, int batch, int hq, int n_q, int max_context_
     return plan_extend(c, batch, hq, n_q, max_context_len, flags, plan);
   }
   plan->kind = kDecodeFew;
+  const bool convert = c.fmt == KVQ_FMT_FP4_E2M1 && (flags & KVQ_QK_CONVERT);
+  plan->qk_convert = convert ? 1 : 0;
+  const int kfmt = convert ? kFmtFP4Conv : c.fmt;
   const int rows = (int)rows_ll;
   const int row_tiles = (rows + 7) / 8;
   const int n_tiles = (int)(((long long)max_context_len + 15) / 16);
@@ -703,7 +713,7 @@ int plan_decode(const CacheGeom& c, int batch, int hq, int n_q, int max_context_
     // most kMaxTilesPerSplit: with ragged context lengths only the maximum
     // is known here, and long splits of the longest sequences would then
     // set the time of the whole call.
-    int slots = resident_waves(c.fmt, row_tiles);
+    int slots = resident_waves(kfmt, row_tiles);
     if (slots <= 0) slots = kDefaultWaveSlots;
     const long long units = (long long)batch * c.hkv;
     long long want = units >= slots ? 1 : slots / units;
@@ -724,10 +734,10 @@ int plan_decode(const CacheGeom& c, int batch, int hq, int n_q, int max_context_
   plan->splits = splits;
   plan->tiles_per_split = per;
   const size_t qops = (size_t)batch * c.hkv * row_tiles * 64 * sizeof(uint32_t) *
-                      ((c.fmt == KVQ_FMT_FP4_E2M1) ? QOpsLayout<KVQ_FMT_FP4_E2M1>::kSlots *
-                                                         QOpsLayout<KVQ_FMT_FP4_E2M1>::kDwords
-                                                   : QOpsLayout<KVQ_FMT_FP8_E4M3>::kSlots *
-                                                         QOpsLayout<KVQ_FMT_FP8_E4M3>::kDwords);
+                      ((kfmt == KVQ_FMT_FP4_E2M1) ? QOpsLayout<KVQ_FMT_FP4_E2M1>::kSlots *
+                                                        QOpsLayout<KVQ_FMT_FP4_E2M1>::kDwords
+                                                  : QOpsLayout<KVQ_FMT_FP8_E4M3>::kSlots *
+                                                        QOpsLayout<KVQ_FMT_FP8_E4M3>::kDwords);
   plan->qops_bytes = qops;
   plan->workspace =
       qops + ((splits > 1) ? (size_t)batch * c.hkv * splits * (8 * row_tiles) * (kD + 2) * sizeof(float) : 0);
@@ -784,7 +794,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     ap = make_append_params(a.c, *a.append);
     app = &ap;
   }
-  if (a.c.fmt == KVQ_FMT_FP4_E2M1) return launch_fmt<KVQ_FMT_FP4_E2M1>(p, a.plan.row_tiles, a.batch, app, stream);
+  if (a.c.fmt == KVQ_FMT_FP4_E2M1) {
+    if (a.plan.qk_convert) return launch_fmt<kFmtFP4Conv>(p, a.plan.row_tiles, a.batch, app, stream);
+    return launch_fmt<KVQ_FMT_FP4_E2M1>(p, a.plan.row_tiles, a.batch, app, stream);
+  }
   return launch_fmt<KVQ_FMT_FP8_E4M3>(p, a.plan.row_tiles, a.batch, app, stream);
 }
 

@@ -110,7 +110,7 @@ __device__ __forceinline__ void load_chunk5(const DecodeParams& p, const int32_t
 // [B][hkv][2 RG owners][4 blocks][kM5][64 lanes][8 dwords].  Lane l holds
 // channels 8l .. 8l + 7; a 32-channel block is 4 lanes whose 8 six-bit codes
 // (48 bits each) make the block's 192-bit stream.
-template <int RG>
+template <int RG, bool CONV>
 __global__ __launch_bounds__(256) void qprep512_kernel(const DecodeParams p) {
   constexpr int ROWS = 16 * RG;
   constexpr int NO = 2 * RG;  // score owners
@@ -136,6 +136,27 @@ __global__ __launch_bounds__(256) void qprep512_kernel(const DecodeParams p) {
   for (int i = 0; i < 8; ++i) x[i] = x[i] * p.qscale;
 
   const int owner = r >> 3;
+  if constexpr (CONV) {
+    // bf16 hi + lo operands of the conversion route, [B][hkv][owners][4
+    // chunks][4 k-steps][64 lanes][4 dwords]: k-step j of chunk c holds, in
+    // operand lane 16 quad + col, channels 128 c + 32 quad + 8 j .. + 7 of the
+    // owner's row col & 7 (hi for col < 8, lo for col >= 8) - exactly the
+    // eight channels this lane holds (lane = 16 c + 4 quad + j)
+    uint32_t hi[4], lo[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t h0 = f32_to_bf16_rne(x[2 * i]), h1 = f32_to_bf16_rne(x[2 * i + 1]);
+      const uint32_t l0 = f32_to_bf16_rne(x[2 * i] - bf16_to_f32((uint16_t)h0));
+      const uint32_t l1 = f32_to_bf16_rne(x[2 * i + 1] - bf16_to_f32((uint16_t)h1));
+      hi[i] = h0 | (h1 << 16);
+      lo[i] = l0 | (l1 << 16);
+    }
+    const int c = lane >> 4, quad = (lane >> 2) & 3, j = lane & 3;
+    uint32_t* dst = p.qops + (((((size_t)bh * NO + owner) * 4 + c) * 4 + j) * 64 + 16 * quad + (r & 7)) * 4;
+    *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{hi[0], hi[1], hi[2], hi[3]};
+    *reinterpret_cast<u32x4_t*>(dst + 8 * 4) = u32x4_t{lo[0], lo[1], lo[2], lo[3]};
+    return;
+  }
   const int gi = lane >> 2;  // 32-channel group of the lane
   const int blk = gi >> 2;
   const int q = gi & 3;
@@ -199,6 +220,36 @@ __device__ __forceinline__ f32x4_t qk_chunk5(f32x4_t acc, const u32x4_t kc, int 
   return acc;
 }
 
+// The conversion route's form of qk_chunk5: the chunk's K codes are
+// converted with their scale to bf16 (kb, 16 dwords: channels 32 g .. 32 g
+// + 31 of the lane's group g), and k-step j multiplies dwords 4 j .. 4 j + 3
+// against the bf16 hi / lo query operand qv[j] (columns c < 8 hold hi of row
+// c, c >= 8 lo of row c - 8, so x + its ror-8 partner is the row's score, as
+// on the native route).
+template <int J>
+__device__ __forceinline__ f32x4_t qk_chunk5_conv(f32x4_t acc, const uint32_t (&kb)[16], const bf16x8_t (&qv)[J]) {
+  static_assert(J == 4, "four k-steps per chunk");
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const u32x4_t a = {kb[4 * j], kb[4 * j + 1], kb[4 * j + 2], kb[4 * j + 3]};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), qv[j], acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// Query operands of one score owner on the conversion route.
+template <int J>
+__device__ __forceinline__ void load_qconv5(const DecodeParams& p, int bh, int NO, int owner, int lane,
+                                            bf16x8_t (&qv)[4][J]) {
+  static_assert(J == 4, "four k-steps per chunk");
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      qv[c][j] = __builtin_bit_cast(
+          bf16x8_t, *reinterpret_cast<const u32x4_t*>(p.qops + (((((size_t)bh * NO + owner) * 4 + c) * 4 + j) * 64 + lane) * 4));
+}
+
 // Online softmax of one 8-row score owner over a tile pair, from its scores
 // S (tile t, token 4 quad + i; column c of the MFMA output holds query-term
 // half c / 8 of row c & 7, so x + its ror-8 partner is the row's score):
@@ -260,7 +311,7 @@ __device__ __forceinline__ void owner_softmax(const f32x4_t (&S)[2], int tile, i
 // SEL: the scan runs over the list of selected positions of each sequence
 // (p.sel; context_lens are the list lengths), one query position per
 // sequence.
-template <int RG, bool SHARED, bool SEL>
+template <int RG, bool SHARED, bool SEL, bool CONV = false>
 __global__ __launch_bounds__(512) void decode512_kernel(const DecodeParams p) {
   constexpr int ROWS = 16 * RG;
   constexpr int NO = 2 * RG;
@@ -330,7 +381,11 @@ __global__ __launch_bounds__(512) void decode512_kernel(const DecodeParams p) {
   // bytes packed four to a register (the MFMA's scale op_sel picks the byte)
   i32x8_t qb[4][kM5];
   int qs[2] = {0, 0};
-  if (owner) {
+  bf16x8_t qv[4][CONV ? 4 : 1];
+  if constexpr (CONV) {
+    if (owner) load_qconv5(p, bh, NO, w, lane, qv);
+  }
+  if (owner && !CONV) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
 #pragma unroll
@@ -357,10 +412,21 @@ __global__ __launch_bounds__(512) void decode512_kernel(const DecodeParams p) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-      acc = qk_chunk5<0>(acc, s_k[par][s][0][lane], (int)s_ks[par][s][0][lane], qb, qs);
-      acc = qk_chunk5<1>(acc, s_k[par][s][1][lane], (int)s_ks[par][s][1][lane], qb, qs);
-      acc = qk_chunk5<2>(acc, s_k[par][s][2][lane], (int)s_ks[par][s][2][lane], qb, qs);
-      acc = qk_chunk5<3>(acc, s_k[par][s][3][lane], (int)s_ks[par][s][3][lane], qb, qs);
+      if constexpr (CONV) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const u32x4_t kc = s_k[par][s][c][lane];
+          const uint32_t kw[4] = {kc[0], kc[1], kc[2], kc[3]};
+          uint32_t kb[16];
+          dequant_group<KVQ_FMT_FP4_E2M1>(kw, scale_operand(s_ks[par][s][c][lane]), kb);
+          acc = qk_chunk5_conv(acc, kb, qv[c]);
+        }
+      } else {
+        acc = qk_chunk5<0>(acc, s_k[par][s][0][lane], (int)s_ks[par][s][0][lane], qb, qs);
+        acc = qk_chunk5<1>(acc, s_k[par][s][1][lane], (int)s_ks[par][s][1][lane], qb, qs);
+        acc = qk_chunk5<2>(acc, s_k[par][s][2][lane], (int)s_ks[par][s][2][lane], qb, qs);
+        acc = qk_chunk5<3>(acc, s_k[par][s][3][lane], (int)s_ks[par][s][3][lane], qb, qs);
+      }
       S[s] = acc;
     }
     owner_softmax(S, tile, row_lim, lane, w & 1, m_run, l_run, s_p[par][w >> 1], &s_alpha[par][8 * w], &s_flag[par][w]);
@@ -475,7 +541,7 @@ __global__ __launch_bounds__(512) void decode512_kernel(const DecodeParams p) {
 // by four owners' waves instead of eight, P by four output waves).  With
 // fewer rows the score waves' two softmax chains are the longer path and
 // the plain kernel is faster.
-template <int RG, bool SHARED, bool SEL>
+template <int RG, bool SHARED, bool SEL, bool CONV = false>
 __global__ __launch_bounds__(512) void decode512r_kernel(const DecodeParams p) {
   constexpr int ROWS = 16 * RG;
   constexpr int NO = 2 * RG;
@@ -512,7 +578,14 @@ __global__ __launch_bounds__(512) void decode512r_kernel(const DecodeParams p) {
     const bool active = 2 * s < NO;
     i32x8_t qb[2][4][kM5];
     int qs[2][2] = {{0, 0}, {0, 0}};
-    if (active) {
+    bf16x8_t qv[2][4][CONV ? 4 : 1];
+    if constexpr (CONV) {
+      if (active) {
+        load_qconv5(p, bh, NO, 2 * s, lane, qv[0]);
+        load_qconv5(p, bh, NO, 2 * s + 1, lane, qv[1]);
+      }
+    }
+    if (active && !CONV) {
 #pragma unroll
       for (int o = 0; o < 2; ++o)
 #pragma unroll
@@ -539,6 +612,24 @@ __global__ __launch_bounds__(512) void decode512r_kernel(const DecodeParams p) {
       const int par = pi & 1;
       const int tile = t_begin + 2 * pi;
       f32x4_t S[2][2];
+      if constexpr (CONV) {
+        // each chunk's K codes converted once, for both owners
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const u32x4_t kc = s_k[par][t][c][lane];
+            const uint32_t kw[4] = {kc[0], kc[1], kc[2], kc[3]};
+            uint32_t kb[16];
+            dequant_group<KVQ_FMT_FP4_E2M1>(kw, scale_operand(s_ks[par][t][c][lane]), kb);
+            a0 = qk_chunk5_conv(a0, kb, qv[0][c]);
+            a1 = qk_chunk5_conv(a1, kb, qv[1][c]);
+          }
+          S[0][t] = a0;
+          S[1][t] = a1;
+        }
+      } else {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
@@ -560,6 +651,7 @@ __global__ __launch_bounds__(512) void decode512r_kernel(const DecodeParams p) {
         a1 = qk_chunk5<3>(a1, kc, ksc, qb[1], qs[1]);
         S[0][t] = a0;
         S[1][t] = a1;
+      }
       }
 #pragma unroll
       for (int o = 0; o < 2; ++o)
@@ -706,7 +798,7 @@ constexpr int kMinTilesPerSplit5 = 8;
 constexpr int kDefaultSlots5 = 256;  // MI355X: 256 CUs x 1 block
 constexpr int kMaxDevices5 = 64;
 
-template <int RG, bool SHARED>
+template <int RG, bool SHARED, bool CONV>
 int resident_blocks5(int dev) {
   static std::atomic<int> cache[kMaxDevices5];
   if (dev < kMaxDevices5) {
@@ -717,9 +809,9 @@ int resident_blocks5(int dev) {
   hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e == hipSuccess) {
     if constexpr (RG >= kRoleSplitRG5)
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode512r_kernel<RG, SHARED, false>, 512, 0);
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode512r_kernel<RG, SHARED, false, CONV>, 512, 0);
     else
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode512_kernel<RG, SHARED, false>, 512, 0);
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, decode512_kernel<RG, SHARED, false, CONV>, 512, 0);
   }
   if (e != hipSuccess) {
     (void)hipGetLastError();
@@ -730,45 +822,50 @@ int resident_blocks5(int dev) {
   return v;
 }
 
-int resident_slots5(int rg, bool shared) {
+template <bool CONV>
+int resident_slots5_c(int dev, int rg, bool shared) {
+  switch (rg) {
+    case 1: return shared ? resident_blocks5<1, true, CONV>(dev) : resident_blocks5<1, false, CONV>(dev);
+    case 2: return shared ? resident_blocks5<2, true, CONV>(dev) : resident_blocks5<2, false, CONV>(dev);
+    case 3: return shared ? resident_blocks5<3, true, CONV>(dev) : resident_blocks5<3, false, CONV>(dev);
+    case 4: return shared ? resident_blocks5<4, true, CONV>(dev) : resident_blocks5<4, false, CONV>(dev);
+    default: return 0;
+  }
+}
+
+int resident_slots5(int rg, bool shared, bool conv) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
-  switch (rg) {
-    case 1: return shared ? resident_blocks5<1, true>(dev) : resident_blocks5<1, false>(dev);
-    case 2: return shared ? resident_blocks5<2, true>(dev) : resident_blocks5<2, false>(dev);
-    case 3: return shared ? resident_blocks5<3, true>(dev) : resident_blocks5<3, false>(dev);
-    case 4: return shared ? resident_blocks5<4, true>(dev) : resident_blocks5<4, false>(dev);
-    default: return 0;
-  }
+  return conv ? resident_slots5_c<true>(dev, rg, shared) : resident_slots5_c<false>(dev, rg, shared);
 }
 
-template <int RG, bool SHARED, bool SEL>
+template <int RG, bool SHARED, bool SEL, bool CONV = false>
 hipError_t launch5(const DecodeParams& p, int batch, hipStream_t stream) {
   const unsigned qblocks = (unsigned)((size_t)batch * p.hkv * 16 * RG / 4);
-  hipLaunchKernelGGL((qprep512_kernel<RG>), dim3(qblocks), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((qprep512_kernel<RG, CONV>), dim3(qblocks), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid((unsigned)p.splits, (unsigned)p.hkv, (unsigned)batch);
   if constexpr (RG >= kRoleSplitRG5)
-    hipLaunchKernelGGL((decode512r_kernel<RG, SHARED, SEL>), grid, dim3(64 * kW5), 0, stream, p);
+    hipLaunchKernelGGL((decode512r_kernel<RG, SHARED, SEL, CONV>), grid, dim3(64 * kW5), 0, stream, p);
   else
-    hipLaunchKernelGGL((decode512_kernel<RG, SHARED, SEL>), grid, dim3(64 * kW5), 0, stream, p);
+    hipLaunchKernelGGL((decode512_kernel<RG, SHARED, SEL, CONV>), grid, dim3(64 * kW5), 0, stream, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((merge_kernel<16 * RG, 8>), dim3(qblocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
-template <bool SHARED, bool SEL>
+template <bool SHARED, bool SEL, bool CONV = false>
 hipError_t launch5_rg(const DecodeParams& p, int rg, int batch, hipStream_t stream) {
   switch (rg) {
-    case 1: return launch5<1, SHARED, SEL>(p, batch, stream);
-    case 2: return launch5<2, SHARED, SEL>(p, batch, stream);
-    case 3: return launch5<3, SHARED, SEL>(p, batch, stream);
-    case 4: return launch5<4, SHARED, SEL>(p, batch, stream);
+    case 1: return launch5<1, SHARED, SEL, CONV>(p, batch, stream);
+    case 2: return launch5<2, SHARED, SEL, CONV>(p, batch, stream);
+    case 3: return launch5<3, SHARED, SEL, CONV>(p, batch, stream);
+    case 4: return launch5<4, SHARED, SEL, CONV>(p, batch, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -789,7 +886,7 @@ int plan_decode512(const CacheGeom& c, int batch, int hq, int n_q, int max_conte
   int splits = (int)((flags & KVQ_SPLITS_MASK) >> KVQ_SPLITS_SHIFT);
   if (splits <= 0) {
     // one round of blocks over the device (one block per compute unit)
-    int slots = resident_slots5(rg, c.kv_shared != 0);
+    int slots = resident_slots5(rg, c.kv_shared != 0, (flags & KVQ_QK_CONVERT) != 0);
     if (slots <= 0) slots = kDefaultSlots5;
     const long long units = (long long)batch * c.hkv;
     long long want = units >= slots ? 1 : slots / units;
@@ -807,6 +904,10 @@ int plan_decode512(const CacheGeom& c, int batch, int hq, int n_q, int max_conte
   plan->row_tiles = rg;
   plan->splits = splits;
   plan->tiles_per_split = per;
+  plan->qk_convert = (flags & KVQ_QK_CONVERT) ? 1 : 0;
+  // query operands: FP6 terms (4 chunks x kM5 x 8 dwords per lane) or, on
+  // the conversion route, bf16 hi / lo (4 chunks x 4 k-steps x 4 dwords):
+  // the same size
   plan->qops_bytes = (size_t)batch * c.hkv * (2 * rg) * 4 * kM5 * 64 * 8 * sizeof(uint32_t);
   plan->workspace = plan->qops_bytes + (size_t)batch * c.hkv * splits * (16 * rg) * (kD5 + 2) * sizeof(float);
   return KVQ_OK;
@@ -850,6 +951,10 @@ hipError_t launch_decode512(const DecodeArgs& a, hipStream_t stream) {
   if (a.sel) {
     if (a.c.kv_shared) return launch5_rg<true, true>(p, a.plan.row_tiles, a.batch, stream);
     return launch5_rg<false, true>(p, a.plan.row_tiles, a.batch, stream);
+  }
+  if (a.plan.qk_convert) {
+    if (a.c.kv_shared) return launch5_rg<true, false, true>(p, a.plan.row_tiles, a.batch, stream);
+    return launch5_rg<false, false, true>(p, a.plan.row_tiles, a.batch, stream);
   }
   if (a.c.kv_shared) return launch5_rg<true, false>(p, a.plan.row_tiles, a.batch, stream);
   return launch5_rg<false, false>(p, a.plan.row_tiles, a.batch, stream);

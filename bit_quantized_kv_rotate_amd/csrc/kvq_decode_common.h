@@ -56,9 +56,16 @@ struct DecodeParams {
   int sel_stride;
 };
 
+// Kernel format: the cache format, or kFmtFP4Conv, an FP4 cache whose score
+// product converts the K codes with their scales to bf16 for bf16 MFMAs
+// against a bf16 hi + lo query (the alternative to the native scaled MFMA,
+// kept for comparison: KVQ_QK_CONVERT).
+constexpr int kFmtFP4Conv = 3;
+
 template <int FMT>
 struct Fmt {
-  static constexpr bool kFP4 = FMT == KVQ_FMT_FP4_E2M1;
+  static constexpr bool kFP4 = FMT == KVQ_FMT_FP4_E2M1 || FMT == kFmtFP4Conv;  // FP4 codes in the cache
+  static constexpr bool kNativeQK = FMT == KVQ_FMT_FP4_E2M1;  // codes straight into the scaled MFMA
   static constexpr int kWords = kFP4 ? 4 : 8;      // uint32 of codes per (token, group)
 };
 

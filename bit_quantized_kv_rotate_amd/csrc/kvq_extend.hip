@@ -40,6 +40,7 @@ constexpr int kRingX = 2;             // tile pairs in flight per staging wave
 // 32-channel block and store the B operands [B][hkv][rows_pad / 16]
 // [kTX][64 lanes][8 dwords]: lane (k-group j, column n) holds term t of row
 // 16 g + n, channels 32 j .. 32 j + 31 (6 packed dwords), its scale, a pad.
+template <bool CONV>
 __global__ __launch_bounds__(256) void qprep_ext_kernel(const DecodeParams p) {
   const int lane = threadIdx.x & 63;
   const long long gr = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);  // grid covers B * hkv * rows_pad
@@ -72,6 +73,24 @@ __global__ __launch_bounds__(256) void qprep_ext_kernel(const DecodeParams p) {
   if (p.rotate_q) wave_fwht<2>(x, lane, p.norm);
   x[0] = x[0] * p.qscale;
   x[1] = x[1] * p.qscale;
+
+  if constexpr (CONV) {
+    // conversion route: bf16 hi and lo operands [B][hkv][rows_pad / 16][hi,
+    // lo][4 k-steps][64 lanes][4 dwords]; operand lane (quad, n) of k-step j
+    // holds channels 32 quad + 8 j .. + 7 of row 16 g + n, the order in which
+    // a K lane of group quad offers its converted channels.  This lane's two
+    // channels 2 lane, 2 lane + 1 are dword lane & 3 of k-step (lane >> 2) & 3,
+    // operand lane 16 (lane >> 4) + n.
+    const uint32_t h0 = f32_to_bf16_rne(x[0]), h1 = f32_to_bf16_rne(x[1]);
+    const uint32_t l0 = f32_to_bf16_rne(x[0] - bf16_to_f32((uint16_t)h0));
+    const uint32_t l1 = f32_to_bf16_rne(x[1] - bf16_to_f32((uint16_t)h1));
+    const int g = r >> 4, n = r & 15;
+    uint32_t* dst = p.qops + ((((size_t)bh * (p.rows_pad / 16) + g) * 2 * 4 + ((lane >> 2) & 3)) * 64 +
+                              16 * (lane >> 4) + n) * 4 + (lane & 3);
+    dst[0] = h0 | (h1 << 16);
+    dst[4 * 64 * 4] = l0 | (l1 << 16);
+    return;
+  }
 
   // 16 lanes per 32-channel block; lane i of the block holds bits 12i ..
   // 12i + 11 of the block's 192-bit stream; lanes 0..5 assemble its dwords,
@@ -134,7 +153,7 @@ __device__ __forceinline__ void load_stage(const DecodeParams& p, const int32_t*
 // GRP: prefix level of a shared-prefix decode (units are prefix groups; see
 // DecodeParams); otherwise units are sequences, optionally scanned from
 // p.tok_start[b] on.
-template <bool GRP, int WAVES>
+template <bool GRP, int WAVES, bool CONV = false>
 __global__ __launch_bounds__(64 * WAVES) void extend_kernel(const DecodeParams p) {
   constexpr int kRowsX = 16 * WAVES;                // rows per block
   constexpr int kJobs = WAVES >= 4 ? 1 : 4 / WAVES;  // staging jobs per staging wave
@@ -246,7 +265,15 @@ __global__ __launch_bounds__(64 * WAVES) void extend_kernel(const DecodeParams p
   const int g = r0 >> 4;
   i32x8_t qb[kTX];
   int qs[kTX];
-  {
+  bf16x8_t qv[CONV ? 2 : 1][4];   // conversion route: hi, lo per k-step
+  if constexpr (CONV) {
+    const uint32_t* src = p.qops + (((size_t)u * (p.rows_pad / 16) + g) * 2 * 4 * 64 + lane) * 4;
+#pragma unroll
+    for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        qv[hl][j] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const u32x4_t*>(src + (size_t)(4 * hl + j) * 64 * 4));
+  } else {
     const uint32_t* src = p.qops + (((size_t)u * (p.rows_pad / 16) + g) * kTX * 64 + lane) * 8;
 #pragma unroll
     for (int t = 0; t < kTX; ++t) {
@@ -317,11 +344,26 @@ __global__ __launch_bounds__(64 * WAVES) void extend_kernel(const DecodeParams p
         for (int s = 0; s < 2; ++s) {
           const u32x4_t kc = s_k[par][s][lane];
           const int ksc = (int)s_ks[par][s][lane];
-          const i32x8_t A = {(int)kc[0], (int)kc[1], (int)kc[2], (int)kc[3], 0, 0, 0, 0};
           f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+          if constexpr (CONV) {
+            // K codes with their scale to bf16 (exact); k-step j takes this
+            // lane's converted channels 8 j .. 8 j + 7; q hi and lo accumulate
+            // into the same scores
+            const uint32_t kw[4] = {kc[0], kc[1], kc[2], kc[3]};
+            uint32_t kb[16];
+            dequant_group<KVQ_FMT_FP4_E2M1>(kw, scale_operand((uint32_t)ksc), kb);
 #pragma unroll
-          for (int t = 0; t < kTX; ++t)
-            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, qb[t], acc, 4, 2, 0, ksc, 0, qs[t]);
+            for (int j = 0; j < 4; ++j) {
+              const bf16x8_t A = __builtin_bit_cast(bf16x8_t, u32x4_t{kb[4 * j], kb[4 * j + 1], kb[4 * j + 2], kb[4 * j + 3]});
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qv[0][j], acc, 0, 0, 0);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qv[1][j], acc, 0, 0, 0);
+            }
+          } else {
+            const i32x8_t A = {(int)kc[0], (int)kc[1], (int)kc[2], (int)kc[3], 0, 0, 0, 0};
+#pragma unroll
+            for (int t = 0; t < kTX; ++t)
+              acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, qb[t], acc, 4, 2, 0, ksc, 0, qs[t]);
+          }
           S[s] = acc;
         }
         // score (s, i) is token tile * 16 + 16 s + 4 quad + i: visible while
@@ -453,7 +495,7 @@ constexpr int kDefaultSlotsX = 256;  // wide blocks: one per CU (MI355X); narrow
 constexpr int kMaxDevicesX = 64;
 constexpr int kMaxRowsX = 1 << 16;
 
-template <int WAVES>
+template <int WAVES, bool CONV = false>
 int resident_blocks_x() {
   static std::atomic<int> cache[kMaxDevicesX];
   int dev = 0;
@@ -467,7 +509,8 @@ int resident_blocks_x() {
   }
   int cus = 0, blocks = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, extend_kernel<false, WAVES>, 64 * WAVES, 0) != hipSuccess) {
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, extend_kernel<false, WAVES, CONV>, 64 * WAVES, 0) !=
+          hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
@@ -487,6 +530,7 @@ int plan_extend_rows(const CacheGeom& c, int batch, long long rows, int max_cont
                      DecodePlan* plan, int block_rows) {
   if (c.d != kDX || c.fmt != KVQ_FMT_FP4_E2M1) return KVQ_ERR_UNSUPPORTED;
   if (rows < 1 || rows > kMaxRowsX) return KVQ_ERR_UNSUPPORTED;
+  const bool conv = (flags & KVQ_QK_CONVERT) != 0;
   if (block_rows == 0) block_rows = rows <= kNarrowMaxRows ? 16 * kNarrowX : 16 * kWideX;
   if (block_rows != 16 * kNarrowX && block_rows != 16 * kWideX) return KVQ_ERR_UNSUPPORTED;
   const int kRowsX = block_rows;
@@ -496,7 +540,8 @@ int plan_extend_rows(const CacheGeom& c, int batch, long long rows, int max_cont
   if (splits <= 0) {
     // one round of blocks over the device, at least kMinTilesPerSplitX tiles
     // and at most a cap per split (below)
-    int slots = block_rows == 16 * kNarrowX ? resident_blocks_x<kNarrowX>() : resident_blocks_x<kWideX>();
+    int slots = block_rows == 16 * kNarrowX ? (conv ? resident_blocks_x<kNarrowX, true>() : resident_blocks_x<kNarrowX>())
+                                             : (conv ? resident_blocks_x<kWideX, true>() : resident_blocks_x<kWideX>());
     if (slots <= 0) slots = block_rows == 16 * kNarrowX ? 6 * kDefaultSlotsX : kDefaultSlotsX;
     const long long work = (long long)batch * c.hkv * row_blocks;
     long long want = work >= slots ? 1 : slots / work;
@@ -530,6 +575,9 @@ int plan_extend_rows(const CacheGeom& c, int batch, long long rows, int max_cont
   plan->block_rows = block_rows;
   plan->splits = splits;
   plan->tiles_per_split = per;
+  plan->qk_convert = conv ? 1 : 0;
+  // query operands per 16-row group: kTX FP6 terms of 8 dwords per lane, or
+  // (conversion route) bf16 hi and lo of 4 k-steps of 4 dwords: the same size
   plan->qops_bytes = (size_t)batch * c.hkv * (rows_pad / 16) * kTX * 64 * 8 * sizeof(uint32_t);
   plan->workspace = plan->qops_bytes + (size_t)batch * c.hkv * splits * rows_pad * (kDX + 2) * sizeof(float);
   return KVQ_OK;
@@ -581,12 +629,20 @@ hipError_t launch_extend(const DecodeArgs& a, hipStream_t stream) {
   p.ws_o = reinterpret_cast<float*>(ws + a.plan.qops_bytes);
   p.ws_ml = p.ws_o + n_o;
   const unsigned qblocks = (unsigned)(units * p.rows_pad / 4);
-  hipLaunchKernelGGL(qprep_ext_kernel, dim3(qblocks), dim3(256), 0, stream, p);
+  const bool conv = a.plan.qk_convert != 0 && !grp;  // the prefix level keeps the native route
+  if (conv)
+    hipLaunchKernelGGL(qprep_ext_kernel<true>, dim3(qblocks), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(qprep_ext_kernel<false>, dim3(qblocks), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((size_t)p.splits * units * a.plan.row_tiles));
   const bool narrow = a.plan.block_rows == 16 * kNarrowX;
-  if (grp && narrow)
+  if (conv && narrow)
+    hipLaunchKernelGGL((extend_kernel<false, kNarrowX, true>), grid, dim3(64 * kNarrowX), 0, stream, p);
+  else if (conv)
+    hipLaunchKernelGGL((extend_kernel<false, kWideX, true>), grid, dim3(64 * kWideX), 0, stream, p);
+  else if (grp && narrow)
     hipLaunchKernelGGL((extend_kernel<true, kNarrowX>), grid, dim3(64 * kNarrowX), 0, stream, p);
   else if (grp)
     hipLaunchKernelGGL((extend_kernel<true, kWideX>), grid, dim3(64 * kWideX), 0, stream, p);

@@ -65,6 +65,7 @@ struct DecodePlan {
   size_t qops_bytes;     // query operands (first part of the workspace)
   size_t workspace;      // bytes
   int block_rows = 0;    // many-row kernel: rows per block (16 per wave)
+  int qk_convert = 0;    // FP4 scores through bf16 conversion of the codes (KVQ_QK_CONVERT)
 };
 
 // Decide split count and workspace size; returns KVQ_OK or an error code.

@@ -83,6 +83,13 @@ extern "C" {
 #define KVQ_Q_PREROTATED 0x1u
 /* leave `out` in the rotated basis (the caller folds H into what follows) */
 #define KVQ_OUT_ROTATED 0x2u
+/* FP4 cache: compute the scores by converting the K codes with their scales
+ * to bf16 and multiplying against a bf16 hi + lo query on bf16 MFMAs,
+ * instead of feeding the codes to the scaled FP4 MFMA against FP6 query
+ * terms.  The two routes give the same attention within the acceptance
+ * bound; the flag exists to compare them (the native route is the faster,
+ * and the default).  Decode calls only; ignored for an FP8 cache. */
+#define KVQ_QK_CONVERT 0x4u
 /* bits 16..27 force the number of context splits (0: chosen by the library);
  * the result does not depend on it beyond fp32 rounding. */
 #define KVQ_SPLITS_SHIFT 16

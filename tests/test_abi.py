@@ -97,7 +97,8 @@ def test_decode_argument_errors():
     assert _decode(n_q=0) == -2
     assert _decode(maxp=4, maxl=128) == -2       # 4 pages of 16 cannot hold 128 tokens
     assert _decode(sm=float("inf")) == -2
-    assert _decode(flags=0x4) == -2
+    assert _decode(flags=0x8) == -2
+    assert _shared(flags=kvq.QK_CONVERT) == -2          # decode calls only
     assert _decode(desc=_desc(fmt=2)) == -3      # FP4 entry point, FP8 cache
     assert _decode(fn="kvq_decode_attn_fp8", desc=_desc(fmt=1)) == -3
     assert _decode(desc=_desc(d=64)) == -4       # no kernel for head_dim 64 yet

@@ -306,3 +306,49 @@ def test_decode_ragged_splits_stale_workspace(gpu, kind):
                                       workspace=ws).cpu().numpy()
         for b in range(wl.batch):
             assert_close(got[b], want[b], "%s, %d splits, seq %d, stale workspace" % (kind, s, b))
+
+
+@pytest.mark.parametrize("wl_name,group,n_q", [("tiny_b1_l256", 0, 0), ("b8_l8k", 0, 0), ("ragged", 16, 1),
+                                               ("ragged", 4, 3), ("ragged", 2, 5)])
+def test_decode_fp4_convert_route(gpu, wl_name, group, n_q):
+    """KVQ_QK_CONVERT: the FP4 scores through bf16 conversion of the codes
+    (the route the native scaled MFMA is compared with) match the oracle,
+    at one, two and three 8-row tiles of the one-wave kernel."""
+    if wl_name == "ragged":
+        wl = syn.Workload("conv_g%d_nq%d" % (group, n_q), batch=3, num_kv_heads=2, num_q_heads=2 * group,
+                          head_dim=128, page_size=16, context=0, n_q=n_q, ctx_range=(40, 3000))
+    else:
+        wl = syn.WORKLOADS[wl_name]
+    f = Filled(wl, "fp4")
+    q = syn.queries(wl).cuda()
+    got = f.decode(q, flags=kvq.QK_CONVERT).cpu().numpy()
+    want = oracle_decode_batch(f, syn.bf16_bits(q.cpu()))
+    for b in range(wl.batch):
+        assert_close(got[b], want[b], "%s convert route seq %d" % (wl.name, b))
+
+
+@pytest.mark.parametrize("kind", ["latent64", "latent16", "mix24", "rows48", "chunk64"])
+def test_decode_convert_route_other_kernels(gpu, kind):
+    """KVQ_QK_CONVERT in the latent-width kernels (role-split at 64 rows, the
+    8-wave kernel at 16) and the many-row kernel (narrow blocks at 24 and 48
+    rows, a 64-token chunk in wide blocks) matches the oracle."""
+    if kind.startswith("latent"):
+        hq = 64 if kind == "latent64" else 16
+        wl = syn.Workload("conv_" + kind, batch=3, num_kv_heads=1, num_q_heads=hq, head_dim=512, page_size=64,
+                          context=0, ctx_range=(100, 4000), kv_shared=True, std=math.sqrt(0.5), n_outliers=4,
+                          outlier_mult=16.0)
+    elif kind == "mix24":
+        wl = syn.Workload("conv_mix24", batch=4, num_kv_heads=2, num_q_heads=16, head_dim=128, page_size=16,
+                          context=0, n_q=3, ctx_range=(200, 5000))
+    elif kind == "rows48":
+        wl = syn.Workload("conv_rows48", batch=2, num_kv_heads=2, num_q_heads=32, head_dim=128, page_size=16,
+                          context=0, n_q=3, ctx_range=(200, 3000))
+    else:
+        wl = syn.Workload("conv_chunk64", batch=2, num_kv_heads=2, num_q_heads=16, head_dim=128, page_size=16,
+                          context=0, n_q=64, ctx_range=(300, 2000))
+    f = Filled(wl, "fp4")
+    q = syn.queries(wl).cuda()
+    got = f.decode(q, flags=kvq.QK_CONVERT).cpu().numpy()
+    want = oracle_decode_batch(f, syn.bf16_bits(q.cpu()))
+    for b in range(wl.batch):
+        assert_close(got[b], want[b], "%s convert route seq %d" % (kind, b))

@@ -20,11 +20,8 @@ MAX_ABS = 2e-3
 REL_L2 = 1e-3
 
 # Two GPU results of one cache that differ only in how the context is cut
-# (split count, shared-prefix levels) round each softmax weight to bf16
-# hi + lo against a different reference maximum: 2^-17 relative per weight,
-# so an output may move by up to 2 * 2^-17 * max|V|, besides the order of the
-# fp32 sums.  The absolute part covers |V| up to 16 (2.4e-4); where outputs
-# (and so values) are larger, the relative part covers them.
+# (split count, shared-prefix levels): each cut rounds its softmax weights to
+# bf16 hi + lo (2^-17 relative) against its own running maximum.
 SPLIT_RTOL = 5e-5
 SPLIT_ATOL = 3e-4
 

@@ -53,12 +53,14 @@ constexpr int kD = 128;              // head_dim handled by this kernel
 constexpr int kQTerms = 4;           // FP6 (E2M3) terms of the pre-scaled query (FP4 cache)
 constexpr int kQMfma = kQTerms / 2;  // scaled MFMAs per tile and row tile
 constexpr int kVRow = 2 * kD + 32;   // LDS bytes per token row of V (bf16, padded)
-// tile pairs held in registers per wave: two, except one at 16 rows, where
-// that keeps two waves per SIMD (at 24 rows, which only the FP8 cache runs
-// here, one wave fits either way, and the deeper ring wins)
+// tile pairs held in registers per wave: one at 8 and 16 rows, with two
+// waves per SIMD (on b32_l32k a second pair in flight per wave made the
+// scan 2% slower and a third 4%: more outstanding random blocks cost HBM
+// row conflicts); two at 24 rows (FP8 cache only), where one wave per SIMD
+// fits either way and the deeper ring wins
 template <int NT>
 struct Ring {
-  static constexpr int kN = NT == 2 ? 1 : 2;
+  static constexpr int kN = NT == 3 ? 2 : 1;
 };
 
 // Query operands of the score product.
@@ -278,7 +280,7 @@ __device__ __forceinline__ void compute_pair(const DecodeParams& p, const int32_
       const uint32_t l = pack_bf16x2(p0 - as_f32(u0 & 0xFFFF0000u), p1 - as_f32(u1 & 0xFFFF0000u));
       pw[e] = hi_col ? h : l;
     }
-    if (__builtin_amdgcn_ballot_w64(grow)) {
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(grow) != 0, 0)) {
       // a row reference moved in some lane: rescale (rare once the scan settles)
       const float alpha = __builtin_amdgcn_exp2f(m_old - m_use);
       st.l_run[t] *= alpha;
@@ -522,19 +524,28 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
   const int interior_limit = min(tok_limit, L - p.n_q + 1);
 
   // ---- page scan: ring of kRing tile pairs; the pair count is padded to a
-  // multiple of kRing with fully masked pairs so every refill is unconditional
+  // multiple of kRing with fully masked pairs so every refill is unconditional.
+  // Iterations whose pairs all lie below interior_limit run without masks;
+  // the rest (the split's last pairs) run masked.  Two loops rather than a
+  // per-pair branch keep the loop-carried registers in place.
+  const int n_int_pairs = (interior_limit >= 16 * t_begin + 32) ? (interior_limit - 16 * t_begin - 32) / 32 + 1 : 0;
+  const int n_int_iter = min(n_int_pairs, n_pairs) / kRing;
 #pragma unroll 1
-  for (int it = 0; it < n_iter; ++it) {
+  for (int it = 0; it < n_int_iter; ++it) {
 #pragma unroll
     for (int u = 0; u < kRing; ++u) {
-      const int pi = it * kRing + u;
-      const int tile = t_begin + 2 * pi;
-      if (tile * 16 + 32 <= interior_limit)
-        compute_pair<FMT, NT, false>(p, bt_row, kvh, tile, t_end, tile + 2 * kRing, tok_limit,
-                                     interior_limit, row_last, q, ring[u], s_v, lane, lo, st);
-      else
-        compute_pair<FMT, NT, true>(p, bt_row, kvh, tile, t_end, tile + 2 * kRing, tok_limit,
-                                    interior_limit, row_last, q, ring[u], s_v, lane, lo, st);
+      const int tile = t_begin + 2 * (it * kRing + u);
+      compute_pair<FMT, NT, false>(p, bt_row, kvh, tile, t_end, tile + 2 * kRing, tok_limit,
+                                   interior_limit, row_last, q, ring[u], s_v, lane, lo, st);
+    }
+  }
+#pragma unroll 1
+  for (int it = n_int_iter; it < n_iter; ++it) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) {
+      const int tile = t_begin + 2 * (it * kRing + u);
+      compute_pair<FMT, NT, true>(p, bt_row, kvh, tile, t_end, tile + 2 * kRing, tok_limit,
+                                  interior_limit, row_last, q, ring[u], s_v, lane, lo, st);
     }
   }
 
@@ -602,7 +613,8 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
 
 constexpr int kMinTilesPerSplit = 8;     // 128 tokens
 constexpr int kMaxTilesPerSplit = 256;   // 4096 tokens
-constexpr int kDefaultWaveSlots = 2048;  // MI355X: 256 CUs x 8 resident waves
+constexpr int kMaxWavesPerCU = 8;        // two page-scan waves per SIMD
+constexpr int kDefaultWaveSlots = 2048;  // MI355X: 256 CUs x kMaxWavesPerCU
 constexpr int kMaxDevices = 64;
 
 template <int FMT, int NT>
@@ -653,7 +665,11 @@ int resident_waves_nt(int dev) {
     (void)hipGetLastError();
     return 0;
   }
-  const int v = cus * blocks;
+  // at most kMaxWavesPerCU page streams per CU: the scan's random 1 KB
+  // blocks lose HBM bandwidth to row conflicts as concurrent streams grow
+  // (three waves per SIMD were a third slower than two on b32_l32k, with
+  // the same bytes in flight per wave)
+  const int v = cus * (blocks < kMaxWavesPerCU ? blocks : kMaxWavesPerCU);
   if (dev < kMaxDevices) cache[dev].store(v, std::memory_order_relaxed);
   return v;
 }

@@ -15,9 +15,9 @@
 //    MFMA, online softmax, P split into bf16 hi + lo);
 //  * wave w converts one 128-channel quarter of one tile of each tile pair
 //    to bf16 into the shared LDS tile;
-//  * wave w accumulates O for all rows over channels 64w .. 64w + 63.  The
-//    PV product puts hi and lo of P in the contraction (k = 16 tokens x
-//    {hi, lo}), so one accumulator holds 16 full rows.
+//  * wave w accumulates O for all rows over channels 64w .. 64w + 63: hi
+//    and lo of P are two A operands of 16 full rows x 32 tokens against the
+//    same V operand, accumulated into one accumulator.
 // P (as ready MFMA A operands), the rescale factors and V pass through LDS,
 // double-buffered by tile-pair parity: one barrier per pair.  Above 32 rows
 // (three or four 16-row groups) decode512r_kernel splits the same work by
@@ -106,11 +106,14 @@ __device__ __forceinline__ void load_chunk5(const DecodeParams& p, const int32_t
 
 // Query prologue for the 512-wide kernel, one wave per query row (rows of a
 // KV head padded to 16 RG): load, rotate, pre-scale, split into kT5 FP6
-// terms per 32-channel block and store the score owner's B operands
-// [B][hkv][2 RG owners][4 blocks][kM5][64 lanes][8 dwords].  Lane l holds
-// channels 8l .. 8l + 7; a 32-channel block is 4 lanes whose 8 six-bit codes
-// (48 bits each) make the block's 192-bit stream.
-template <int RG, bool CONV>
+// terms per 32-channel block and store the score B operands.  8-row owners
+// (R16 false): [B][hkv][2 RG owners][4 blocks][kM5][64 lanes][8 dwords],
+// two terms per MFMA in columns c and c + 8.  16-row groups (R16, the
+// role-split kernel): [B][hkv][RG groups][4 blocks][kT5 terms][64 lanes][8
+// dwords], one term of 16 rows per MFMA.  Lane l holds channels 8l .. 8l +
+// 7; a 32-channel block is 4 lanes whose 8 six-bit codes (48 bits each) make
+// the block's 192-bit stream.
+template <int RG, bool CONV, bool R16 = false>
 __global__ __launch_bounds__(256) void qprep512_kernel(const DecodeParams p) {
   constexpr int ROWS = 16 * RG;
   constexpr int NO = 2 * RG;  // score owners
@@ -200,9 +203,14 @@ __global__ __launch_bounds__(256) void qprep512_kernel(const DecodeParams p) {
       d0 = (uint32_t)byte;
       d1 = 0u;
     }
-    const int m = t >> 1;
-    const int col = (r & 7) + 8 * (t & 1);
-    uint32_t* dst = p.qops + (((((size_t)bh * NO + owner) * 4 + blk) * kM5 + m) * 64 + 16 * q + col) * 8 + 2 * j4;
+    uint32_t* dst;
+    if constexpr (R16) {
+      dst = p.qops + (((((size_t)bh * RG + (r >> 4)) * 4 + blk) * kT5 + t) * 64 + 16 * q + (r & 15)) * 8 + 2 * j4;
+    } else {
+      const int m = t >> 1;
+      const int col = (r & 7) + 8 * (t & 1);
+      dst = p.qops + (((((size_t)bh * NO + owner) * 4 + blk) * kM5 + m) * 64 + 16 * q + col) * 8 + 2 * j4;
+    }
     *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{d0, d1};
   }
 }
@@ -297,15 +305,66 @@ __device__ __forceinline__ void owner_softmax(const f32x4_t (&S)[2], int tile, i
     const uint32_t l = pack_bf16x2(p0 - as_f32(u0 & 0xFFFF0000u), p1 - as_f32(u1 & 0xFFFF0000u));
     pw[e] = hi_col ? h : l;
   }
-  // A operand slot: k-half quad / 2 (token quads {0,1} or {2,3}); lane
-  // k-group (quad & 1) + 2 * lo, row 8 half + (col & 7)
-  const int kg = (quad & 1) + (hi_col ? 0 : 2);
-  sp[quad >> 1][16 * kg + 8 * half + (col & 7)] = u32x4_t{pw[0], pw[1], pw[2], pw[3]};
+  // A operand of the hi part (slot 0) or the lo part (slot 1) of the
+  // 16-row group: lane k-group quad (tokens 4 quad .. 4 quad + 3 of both
+  // tiles), row 8 half + (col & 7)
+  sp[hi_col ? 0 : 1][16 * quad + 8 * half + (col & 7)] = u32x4_t{pw[0], pw[1], pw[2], pw[3]};
   const float a = __builtin_amdgcn_exp2f(m_old - m_use);
   l_run = l_run * a + psum;
   if (lane < 8) alpha[lane] = a;
   const bool moved = __builtin_amdgcn_ballot_w64(grow) != 0;
   if (lane == 0) *flag = moved ? 1 : 0;
+}
+
+// Online softmax of one 16-row score group over a tile pair (role-split
+// kernel, native scores): S (tile t, token 4 quad + i) holds row `col` of
+// the group in column col.  Masked past row_lim when `masked`; lazy
+// reference maximum; P split into bf16 hi and lo, stored as the group's two
+// PV A operands (slot 0: hi, slot 1: lo; lane 16 quad + col); the rows'
+// rescale factors go to alpha[0..15] and whether any reference moved to
+// flag[0] and flag[1] (the group's two 8-row halves).
+__device__ __forceinline__ void group_softmax(const f32x4_t (&S)[2], int tile, int row_lim, bool masked, int lane,
+                                              float& m_run, float& l_run, u32x4_t (*sp)[64], float* alpha,
+                                              int* flag) {
+  const int quad = lane >> 4;
+  float sc[8];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sc[4 * t + i] = S[t][i];
+  if (masked) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[4 * t + i] = ((tile + t) * 16 + 4 * quad + i <= row_lim) ? sc[4 * t + i] : -INFINITY;
+  }
+  float mloc = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                     fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+  mloc = quad_max(mloc);
+  const float m_old = m_run;
+  const float m_tgt = fmaxf(m_old, mloc);
+  const bool grow = m_tgt > m_old + kLazyLog2;
+  const float m_new = grow ? m_tgt : m_old;
+  const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+  m_run = m_new;
+  float psum = 0.0f;
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float p0 = __builtin_amdgcn_exp2f(sc[2 * e] - m_use);
+    const float p1 = __builtin_amdgcn_exp2f(sc[2 * e + 1] - m_use);
+    psum += p0 + p1;
+    const uint32_t u0 = as_u32(p0), u1 = as_u32(p1);
+    h[e] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+    l[e] = pack_bf16x2(p0 - as_f32(u0 & 0xFFFF0000u), p1 - as_f32(u1 & 0xFFFF0000u));
+  }
+  sp[0][lane] = u32x4_t{h[0], h[1], h[2], h[3]};
+  sp[1][lane] = u32x4_t{l[0], l[1], l[2], l[3]};
+  const float a = __builtin_amdgcn_exp2f(m_old - m_use);
+  l_run = l_run * a + psum;
+  if (lane < 16) alpha[lane] = a;
+  const bool moved = __builtin_amdgcn_ballot_w64(grow) != 0;
+  if (lane < 2) flag[lane] = moved ? 1 : 0;
 }
 
 // SEL: the scan runs over the list of selected positions of each sequence
@@ -485,22 +544,29 @@ __global__ __launch_bounds__(512) void decode512_kernel(const DecodeParams p) {
       const int rr = col >> 2;
       const int c4 = (col & 3) * 4;
       typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
-      auto read_b = [&](int Q, int n) {
-        const int cb = 2 * (64 * w + 16 * n + c4);
-        lds_bf16x4* a0 = (lds_bf16x4*)((__attribute__((address_space(3))) uint8_t*)&s_v[vb][0][4 * Q + rr][cb]);
-        lds_bf16x4* a1 = (lds_bf16x4*)((__attribute__((address_space(3))) uint8_t*)&s_v[vb][1][4 * Q + rr][cb]);
+      // one B operand (the pair's 32 tokens x 16 channels) serves the hi
+      // and the lo MFMA of every row group
+      // one LDS base per pair; the reads of tile 1 and of channel tile n
+      // are constant offsets from it
+      // (the buffer offset is made uniform so that the compiler keeps one
+      // lane address instead of one per read)
+      const int vbuf = __builtin_amdgcn_readfirstlane(vb * (int)sizeof(s_v[0]));
+      __attribute__((address_space(3))) uint8_t* const vrow =
+          (__attribute__((address_space(3))) uint8_t*)&s_v[0][0][4 * quad + rr][2 * (64 * w + c4)] + vbuf;
+      auto read_b = [&](int n) {
+        lds_bf16x4* a0 = (lds_bf16x4*)(vrow + 32 * n);
+        lds_bf16x4* a1 = (lds_bf16x4*)(vrow + 16 * kVRow5 + 32 * n);
         const u32x2_t w0 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(a0));
         const u32x2_t w1 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(a1));
         return __builtin_bit_cast(bf16x8_t, u32x4_t{w0[0], w0[1], w1[0], w1[1]});
       };
 #pragma unroll
       for (int n = 0; n < 4; ++n) {
-        const bf16x8_t B0 = read_b(quad & 1, n);
-        const bf16x8_t B1 = read_b(2 + (quad & 1), n);
+        const bf16x8_t B = read_b(n);
 #pragma unroll
         for (int g = 0; g < RG; ++g) {
-          O[g][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][0], B0, O[g][n], 0, 0, 0);
-          O[g][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][1], B1, O[g][n], 0, 0, 0);
+          O[g][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][0], B, O[g][n], 0, 0, 0);
+          O[g][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][1], B, O[g][n], 0, 0, 0);
         }
       }
       // stage pair pi + 2 from the ring, refill the slot
@@ -573,31 +639,86 @@ __global__ __launch_bounds__(512) void decode512r_kernel(const DecodeParams p) {
   const size_t base = ((size_t)bh * p.splits + split) * ROWS;
 
   if (w < 4) {
-    // ---------------- score wave: owners 2w and 2w + 1
+    // ---------------- score wave: rows 16w .. 16w + 15 (owners 2w, 2w + 1)
     const int s = w;
     const bool active = 2 * s < NO;
-    i32x8_t qb[2][4][kM5];
-    int qs[2][2] = {{0, 0}, {0, 0}};
-    bf16x8_t qv[2][4][CONV ? 4 : 1];
-    if constexpr (CONV) {
+    if constexpr (!CONV) {
+      // native scores: one FP6 query term of the 16 rows per scaled MFMA
+      // (column = row), four terms and four 128-channel chunks per tile
+      i32x8_t qb[4][kT5];
+      int qs[4] = {0, 0, 0, 0};
       if (active) {
-        load_qconv5(p, bh, NO, 2 * s, lane, qv[0]);
-        load_qconv5(p, bh, NO, 2 * s + 1, lane, qv[1]);
-      }
-    }
-    if (active && !CONV) {
-#pragma unroll
-      for (int o = 0; o < 2; ++o)
 #pragma unroll
         for (int c = 0; c < 4; ++c)
 #pragma unroll
-          for (int m = 0; m < kM5; ++m) {
-            const uint32_t* src = p.qops + (((((size_t)bh * NO + 2 * s + o) * 4 + c) * kM5 + m) * 64 + lane) * 8;
+          for (int tm = 0; tm < kT5; ++tm) {
+            const uint32_t* src = p.qops + (((((size_t)bh * RG + s) * 4 + c) * kT5 + tm) * 64 + lane) * 8;
             const u32x4_t a0 = *reinterpret_cast<const u32x4_t*>(src);
             const u32x4_t a1 = *reinterpret_cast<const u32x4_t*>(src + 4);
-            qb[o][c][m] = i32x8_t{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], 0, 0};
-            qs[o][c >> 1] |= (int)((a1[2] & 0xFFu) << (8 * (2 * (c & 1) + m)));
+            qb[c][tm] = i32x8_t{(int)a0[0], (int)a0[1], (int)a0[2], (int)a0[3], (int)a1[0], (int)a1[1], 0, 0};
+            qs[c] |= (int)((a1[2] & 0xFFu) << (8 * tm));
           }
+      }
+      const int row = 16 * s + col;
+      const int row_lim = (active && row < p.rows) ? min(tok_limit - 1, L - p.n_q + row / p.group) : -1;
+      // pairs ending at or below every real row's last visible token need
+      // no mask (padding rows have zero queries and are never read back)
+      int vis = row_lim >= 0 ? row_lim : 0x7FFFFFFF;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) vis = min(vis, __shfl_xor(vis, o, 64));
+      vis = __builtin_amdgcn_readfirstlane(vis);
+      float m_run = -INFINITY, l_run = 0.0f;
+      auto scores = [&](int pi) {
+        const int par = pi & 1;
+        const int tile = t_begin + 2 * pi;
+        f32x4_t S[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          // two accumulators (even and odd chunks) halve the MFMA chain
+          f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const u32x4_t kc = s_k[par][tt][c][lane];
+            const int ksc = (int)s_ks[par][tt][c][lane];
+            const i32x8_t A = {(int)kc[0], (int)kc[1], (int)kc[2], (int)kc[3], 0, 0, 0, 0};
+            f32x4_t& acc = (c & 1) ? a1 : a0;
+            // the query scale of term tm is byte tm of qs[c]
+            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, qb[c][0], acc, 4, 2, 0, ksc, 0, qs[c]);
+            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, qb[c][1], acc, 4, 2, 0, ksc, 1, qs[c]);
+            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, qb[c][2], acc, 4, 2, 0, ksc, 2, qs[c]);
+            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, qb[c][3], acc, 4, 2, 0, ksc, 3, qs[c]);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) S[tt][i] = a0[i] + a1[i];
+        }
+        group_softmax(S, tile, row_lim, tile * 16 + 31 > vis, lane, m_run, l_run, s_p[par][s],
+                      &s_alpha[par][16 * s], &s_flag[par][2 * s]);
+      };
+      __syncthreads();
+      if (n_pairs > 0 && active) scores(0);
+      __syncthreads();
+#pragma unroll 1
+      for (int pi = 0; pi < n_iter * kRing; ++pi) {
+        // past the last pair the staged tiles lie beyond the context and
+        // every score is masked: the softmax state stays unchanged
+        if (active) scores(pi + 1);
+        __syncthreads();
+      }
+      if (active) {
+        const float lrow = quad_sum(l_run);
+        if (lane < 16) {
+          p.ws_ml[(base + 16 * s + lane) * 2 + 0] = m_run;
+          p.ws_ml[(base + 16 * s + lane) * 2 + 1] = lrow;
+        }
+      }
+      return;
+    } else {
+    // conversion route: 8-row owners 2w and 2w + 1, query hi / lo in
+    // columns c and c + 8
+    bf16x8_t qv[2][4][4];
+    if (active) {
+      load_qconv5(p, bh, NO, 2 * s, lane, qv[0]);
+      load_qconv5(p, bh, NO, 2 * s + 1, lane, qv[1]);
     }
     int row_lim[2];
     float m_run[2], l_run[2];
@@ -612,46 +733,21 @@ __global__ __launch_bounds__(512) void decode512r_kernel(const DecodeParams p) {
       const int par = pi & 1;
       const int tile = t_begin + 2 * pi;
       f32x4_t S[2][2];
-      if constexpr (CONV) {
-        // each chunk's K codes converted once, for both owners
+      // each chunk's K codes converted once, for both owners
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const u32x4_t kc = s_k[par][t][c][lane];
-            const uint32_t kw[4] = {kc[0], kc[1], kc[2], kc[3]};
-            uint32_t kb[16];
-            dequant_group<KVQ_FMT_FP4_E2M1>(kw, scale_operand(s_ks[par][t][c][lane]), kb);
-            a0 = qk_chunk5_conv(a0, kb, qv[0][c]);
-            a1 = qk_chunk5_conv(a1, kb, qv[1][c]);
-          }
-          S[0][t] = a0;
-          S[1][t] = a1;
-        }
-      } else {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
+      for (int tt = 0; tt < 2; ++tt) {
         f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-        u32x4_t kc = s_k[par][t][0][lane];
-        int ksc = (int)s_ks[par][t][0][lane];
-        a0 = qk_chunk5<0>(a0, kc, ksc, qb[0], qs[0]);
-        a1 = qk_chunk5<0>(a1, kc, ksc, qb[1], qs[1]);
-        kc = s_k[par][t][1][lane];
-        ksc = (int)s_ks[par][t][1][lane];
-        a0 = qk_chunk5<1>(a0, kc, ksc, qb[0], qs[0]);
-        a1 = qk_chunk5<1>(a1, kc, ksc, qb[1], qs[1]);
-        kc = s_k[par][t][2][lane];
-        ksc = (int)s_ks[par][t][2][lane];
-        a0 = qk_chunk5<2>(a0, kc, ksc, qb[0], qs[0]);
-        a1 = qk_chunk5<2>(a1, kc, ksc, qb[1], qs[1]);
-        kc = s_k[par][t][3][lane];
-        ksc = (int)s_ks[par][t][3][lane];
-        a0 = qk_chunk5<3>(a0, kc, ksc, qb[0], qs[0]);
-        a1 = qk_chunk5<3>(a1, kc, ksc, qb[1], qs[1]);
-        S[0][t] = a0;
-        S[1][t] = a1;
-      }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const u32x4_t kc = s_k[par][tt][c][lane];
+          const uint32_t kw[4] = {kc[0], kc[1], kc[2], kc[3]};
+          uint32_t kb[16];
+          dequant_group<KVQ_FMT_FP4_E2M1>(kw, scale_operand(s_ks[par][tt][c][lane]), kb);
+          a0 = qk_chunk5_conv(a0, kb, qv[0][c]);
+          a1 = qk_chunk5_conv(a1, kb, qv[1][c]);
+        }
+        S[0][tt] = a0;
+        S[1][tt] = a1;
       }
 #pragma unroll
       for (int o = 0; o < 2; ++o)
@@ -665,8 +761,6 @@ __global__ __launch_bounds__(512) void decode512r_kernel(const DecodeParams p) {
     __syncthreads();
 #pragma unroll 1
     for (int pi = 0; pi < n_iter * kRing; ++pi) {
-      // past the last pair the staged tiles lie beyond the context and
-      // every score is masked: the softmax state stays unchanged
       if (active) scores(pi + 1);
       __syncthreads();
     }
@@ -681,6 +775,7 @@ __global__ __launch_bounds__(512) void decode512r_kernel(const DecodeParams p) {
       }
     }
     return;
+    }
   }
 
   // ---------------- output wave: channels 128v .. 128v + 127, staging of chunk v
@@ -757,22 +852,27 @@ __global__ __launch_bounds__(512) void decode512r_kernel(const DecodeParams p) {
         A[g][1] = __builtin_bit_cast(bf16x8_t, s_p[par][g][1][lane]);
       }
       const int vb = pi % 3;
-      auto read_b = [&](int Q, int n) {
-        const int cb = 2 * (128 * v + 16 * n + c4);
-        lds_bf16x4* a0 = (lds_bf16x4*)((__attribute__((address_space(3))) uint8_t*)&s_v[vb][0][4 * Q + rr][cb]);
-        lds_bf16x4* a1 = (lds_bf16x4*)((__attribute__((address_space(3))) uint8_t*)&s_v[vb][1][4 * Q + rr][cb]);
+      // one LDS base per pair; the reads of tile 1 and of channel tile n
+      // are constant offsets from it
+      // (the buffer offset is made uniform so that the compiler keeps one
+      // lane address instead of one per read)
+      const int vbuf = __builtin_amdgcn_readfirstlane(vb * (int)sizeof(s_v[0]));
+      __attribute__((address_space(3))) uint8_t* const vrow =
+          (__attribute__((address_space(3))) uint8_t*)&s_v[0][0][4 * quad + rr][2 * (128 * v + c4)] + vbuf;
+      auto read_b = [&](int n) {
+        lds_bf16x4* a0 = (lds_bf16x4*)(vrow + 32 * n);
+        lds_bf16x4* a1 = (lds_bf16x4*)(vrow + 16 * kVRow5 + 32 * n);
         const u32x2_t w0 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(a0));
         const u32x2_t w1 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(a1));
         return __builtin_bit_cast(bf16x8_t, u32x4_t{w0[0], w0[1], w1[0], w1[1]});
       };
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
-        const bf16x8_t B0 = read_b(quad & 1, n);
-        const bf16x8_t B1 = read_b(2 + (quad & 1), n);
+        const bf16x8_t B = read_b(n);
 #pragma unroll
         for (int g = 0; g < RG; ++g) {
-          O[g][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][0], B0, O[g][n], 0, 0, 0);
-          O[g][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][1], B1, O[g][n], 0, 0, 0);
+          O[g][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][0], B, O[g][n], 0, 0, 0);
+          O[g][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][1], B, O[g][n], 0, 0, 0);
         }
       }
       {
@@ -845,7 +945,7 @@ int resident_slots5(int rg, bool shared, bool conv) {
 template <int RG, bool SHARED, bool SEL, bool CONV = false>
 hipError_t launch5(const DecodeParams& p, int batch, hipStream_t stream) {
   const unsigned qblocks = (unsigned)((size_t)batch * p.hkv * 16 * RG / 4);
-  hipLaunchKernelGGL((qprep512_kernel<RG, CONV>), dim3(qblocks), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((qprep512_kernel<RG, CONV, (RG >= kRoleSplitRG5) && !CONV>), dim3(qblocks), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid((unsigned)p.splits, (unsigned)p.hkv, (unsigned)batch);

@@ -14,8 +14,8 @@
 //  * scores S^T = K q^T with the FP4 K codes and scale bytes as A and four
 //    FP6 query terms accumulated in the same 16 x 16 tile (16 full rows);
 //  * online softmax per row, P split into bf16 hi + lo;
-//  * PV with hi and lo in the MFMA rows (rows 0-7 and 8-15 of the wave in two
-//    accumulator sets), so each V operand read serves 32 rows x 32 tokens.
+//  * PV against hi and lo in two accumulator sets (the wave's 16 rows in the
+//    MFMA rows of each), so each V operand read serves 32 rows x 32 tokens.
 // One barrier per tile pair; LDS is double-buffered by pair parity.
 #include <atomic>
 
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(64 * WAVES) void extend_kernel(const DecodeParams p
   for (int o = 1; o < 16; o <<= 1) wave_lim = max(wave_lim, __shfl_xor(wave_lim, o, 64));
   wave_lim = __builtin_amdgcn_readfirstlane(wave_lim);
   float m_run = -INFINITY, l_run = 0.0f;
-  f32x4_t O1[8], O2[8];  // rows 0-7 and 8-15 of the wave: hi in MFMA rows 0-7, lo in 8-15
+  f32x4_t O1[8], O2[8];  // the wave's 16 rows: PV of the hi part of P, of the lo part
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
     O1[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -319,164 +319,159 @@ __global__ __launch_bounds__(64 * WAVES) void extend_kernel(const DecodeParams p
   }
   __syncthreads();
 
-#pragma unroll 1
-  for (int it = 0; it < n_iter; ++it) {
+  // Pairs whose 32 tokens every real row of the wave sees run without
+  // score masks (the iterations before n_int_iter); padding rows have zero
+  // queries (exact zero scores) and are never read back, so they need none
+  // either.
+  int vis_all = row_lim >= 0 ? row_lim : 0x7FFFFFFF;
 #pragma unroll
-    for (int k = 0; k < kRingX; ++k) {
-      const int pi = it * kRingX + k;
-      const int par = pi & 1;
-      const int tile = t_begin + 2 * pi;
-      // ---- stage the next pair (its buffer was last read before the
-      // previous barrier), refill the ring slot
-      if (stager) {
-        const int nk = (k + 1) % kRingX;
+  for (int o = 1; o < 16; o <<= 1) vis_all = min(vis_all, __shfl_xor(vis_all, o, 64));
+  vis_all = __builtin_amdgcn_readfirstlane(vis_all);
+  const int int_tok = wave_lim < 0 ? 0 : vis_all + 1;
+  const int n_int_pairs = (int_tok >= 16 * t_begin + 32) ? (int_tok - 16 * t_begin - 32) / 32 + 1 : 0;
+  const int n_int_iter = min(n_int_pairs, n_pairs) / kRingX;
+
+  auto pair_step = [&](int it, int k, bool masked) {
+    const int pi = it * kRingX + k;
+    const int par = pi & 1;
+    const int tile = t_begin + 2 * pi;
+    // ---- stage the next pair (its buffer was last read before the
+    // previous barrier), refill the ring slot
+    if (stager) {
+      const int nk = (k + 1) % kRingX;
 #pragma unroll
-        for (int jj = 0; jj < kJobs; ++jj) {
-          stage(pi + 1, w + WAVES * jj, ring[jj][nk]);
-          fetch(pi + 1 + kRingX, w + WAVES * jj, ring[jj][nk]);
-        }
+      for (int jj = 0; jj < kJobs; ++jj) {
+        stage(pi + 1, w + WAVES * jj, ring[jj][nk]);
+        fetch(pi + 1 + kRingX, w + WAVES * jj, ring[jj][nk]);
       }
-      if (tile * 16 <= wave_lim) {
-        // ---- scores of the wave's 16 rows (past the last pair every score is
-        // masked: the softmax state does not change)
-        f32x4_t S[2];
+    }
+    if (!masked || tile * 16 <= wave_lim) {
+      // ---- scores of the wave's 16 rows (past the last pair every score is
+      // masked: the softmax state does not change)
+      f32x4_t S[2];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const u32x4_t kc = s_k[par][s][lane];
-          const int ksc = (int)s_ks[par][s][lane];
-          f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-          if constexpr (CONV) {
-            // K codes with their scale to bf16 (exact); k-step j takes this
-            // lane's converted channels 8 j .. 8 j + 7; q hi and lo accumulate
-            // into the same scores
-            const uint32_t kw[4] = {kc[0], kc[1], kc[2], kc[3]};
-            uint32_t kb[16];
-            dequant_group<KVQ_FMT_FP4_E2M1>(kw, scale_operand((uint32_t)ksc), kb);
+      for (int s = 0; s < 2; ++s) {
+        const u32x4_t kc = s_k[par][s][lane];
+        const int ksc = (int)s_ks[par][s][lane];
+        f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (CONV) {
+          // K codes with their scale to bf16 (exact); k-step j takes this
+          // lane's converted channels 8 j .. 8 j + 7; q hi and lo accumulate
+          // into the same scores
+          const uint32_t kw[4] = {kc[0], kc[1], kc[2], kc[3]};
+          uint32_t kb[16];
+          dequant_group<KVQ_FMT_FP4_E2M1>(kw, scale_operand((uint32_t)ksc), kb);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const bf16x8_t A = __builtin_bit_cast(bf16x8_t, u32x4_t{kb[4 * j], kb[4 * j + 1], kb[4 * j + 2], kb[4 * j + 3]});
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qv[0][j], acc, 0, 0, 0);
-              acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qv[1][j], acc, 0, 0, 0);
-            }
-          } else {
-            const i32x8_t A = {(int)kc[0], (int)kc[1], (int)kc[2], (int)kc[3], 0, 0, 0, 0};
-#pragma unroll
-            for (int t = 0; t < kTX; ++t)
-              acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, qb[t], acc, 4, 2, 0, ksc, 0, qs[t]);
+          for (int j = 0; j < 4; ++j) {
+            const bf16x8_t A = __builtin_bit_cast(bf16x8_t, u32x4_t{kb[4 * j], kb[4 * j + 1], kb[4 * j + 2], kb[4 * j + 3]});
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qv[0][j], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, qv[1][j], acc, 0, 0, 0);
           }
-          S[s] = acc;
+        } else {
+          const i32x8_t A = {(int)kc[0], (int)kc[1], (int)kc[2], (int)kc[3], 0, 0, 0, 0};
+#pragma unroll
+          for (int t = 0; t < kTX; ++t)
+            acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, qb[t], acc, 4, 2, 0, ksc, 0, qs[t]);
         }
+        S[s] = acc;
+      }
+      float sc[8];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[4 * s + i] = S[s][i];
+      if (masked) {
         // score (s, i) is token tile * 16 + 16 s + 4 quad + i: visible while
         // 16 s + i <= rel
         const int rel = row_lim - tile * 16 - 4 * quad;
-        float sc[8];
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) sc[4 * s + i] = (16 * s + i <= rel) ? S[s][i] : -INFINITY;
-        float mloc = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                           fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-        mloc = quad_max(mloc);
-        // lazy reference maximum: a row's reference moves only when its
-        // running maximum passes it by more than kLazyLog2, so most pairs
-        // skip the rescale; weights stay below 2^kLazyLog2
-        const float m_old = m_run;
-        const float m_tgt = fmaxf(m_old, mloc);
-        const bool grow = m_tgt > m_old + kLazyLog2;
-        const float m_new = grow ? m_tgt : m_old;
-        const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
-        m_run = m_new;
-        float psum = 0.0f;
-        uint32_t h[4], l[4];
+          for (int i = 0; i < 4; ++i) sc[4 * s + i] = (16 * s + i <= rel) ? sc[4 * s + i] : -INFINITY;
+      }
+      float mloc = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                         fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+      mloc = quad_max(mloc);
+      // lazy reference maximum: a row's reference moves only when its
+      // running maximum passes it by more than kLazyLog2, so most pairs
+      // skip the rescale; weights stay below 2^kLazyLog2
+      const float m_old = m_run;
+      const float m_tgt = fmaxf(m_old, mloc);
+      const bool grow = m_tgt > m_old + kLazyLog2;
+      const float m_new = grow ? m_tgt : m_old;
+      const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
+      m_run = m_new;
+      float psum = 0.0f;
+      // P of this lane's row as bf16 hi (A1) and lo (A2): the wave's 16 rows
+      // are the MFMA rows of both, so O1 collects hi and O2 lo
+      uint32_t a1[4], a2[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(sc[2 * e] - m_use);
-          const float p1 = __builtin_amdgcn_exp2f(sc[2 * e + 1] - m_use);
-          psum += p0 + p1;
-          const uint32_t u0 = as_u32(p0), u1 = as_u32(p1);
-          h[e] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
-          l[e] = pack_bf16x2(p0 - as_f32(u0 & 0xFFFF0000u), p1 - as_f32(u1 & 0xFFFF0000u));
-        }
-        // A operands with hi / lo in the MFMA rows: rows 0-7 of the wave
-        // (lanes c < 8 own hi, lanes c >= 8 take lo of row c - 8 from lane
-        // c - 8) and rows 8-15 (lanes c < 8 take hi of row c + 8)
-        uint32_t a1[4], a2[4];
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(sc[2 * e] - m_use);
+        const float p1 = __builtin_amdgcn_exp2f(sc[2 * e + 1] - m_use);
+        psum += p0 + p1;
+        const uint32_t u0 = as_u32(p0), u1 = as_u32(p1);
+        a1[e] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+        a2[e] = pack_bf16x2(p0 - as_f32(u0 & 0xFFFF0000u), p1 - as_f32(u1 & 0xFFFF0000u));
+      }
+      if (__builtin_expect(__builtin_amdgcn_ballot_w64(grow) != 0, 0)) {
+        // a row max moved: rescale.  Lane (quad, c) of O1 and O2 holds rows
+        // 4 quad + i; lane c holds the factor of row c (in every quad)
+        const float alpha = __builtin_amdgcn_exp2f(m_old - m_use);
+        l_run *= alpha;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t lr = (uint32_t)__builtin_amdgcn_mov_dpp((int)l[e], 0x128, 0xF, 0xF, false);
-          const uint32_t hr = (uint32_t)__builtin_amdgcn_mov_dpp((int)h[e], 0x128, 0xF, 0xF, false);
-          a1[e] = hi_col ? h[e] : lr;
-          a2[e] = hi_col ? hr : l[e];
-        }
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-          // a row max moved: rescale.  Lane (q, c) of O1 holds rows
-          // (4q + i) & 7, of O2 rows 8 + ((4q + i) & 7): row i or 4 + i by the
-          // parity of q; lane c holds the factor of row c (in every quad)
-          const float alpha = __builtin_amdgcn_exp2f(m_old - m_use);
-          l_run *= alpha;
+        for (int i = 0; i < 4; ++i) {
+          const float al = __shfl(alpha, 4 * quad + i, 64);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float x0 = as_f32((uint32_t)__builtin_amdgcn_readlane((int)as_u32(alpha), i));
-            const float x1 = as_f32((uint32_t)__builtin_amdgcn_readlane((int)as_u32(alpha), 4 + i));
-            const float y0 = as_f32((uint32_t)__builtin_amdgcn_readlane((int)as_u32(alpha), 8 + i));
-            const float y1 = as_f32((uint32_t)__builtin_amdgcn_readlane((int)as_u32(alpha), 12 + i));
-            const float al1 = (quad & 1) ? x1 : x0;
-            const float al2 = (quad & 1) ? y1 : y0;
-#pragma unroll
-            for (int n = 0; n < 8; ++n) {
-              O1[n][i] *= al1;
-              O2[n][i] *= al2;
-            }
+          for (int n = 0; n < 8; ++n) {
+            O1[n][i] *= al;
+            O2[n][i] *= al;
           }
         }
-        l_run += psum;
-        const bf16x8_t A1 = __builtin_bit_cast(bf16x8_t, u32x4_t{a1[0], a1[1], a1[2], a1[3]});
-        const bf16x8_t A2 = __builtin_bit_cast(bf16x8_t, u32x4_t{a2[0], a2[1], a2[2], a2[3]});
-
-        // ---- PV: B operands read transposed from the LDS V tiles
-        const int rr = col >> 2;
-        const int c4 = (col & 3) * 4;
-        typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
-        auto read_b = [&](int n) {
-          lds_bf16x4* p0 = (lds_bf16x4*)((__attribute__((address_space(3))) uint8_t*)&s_v[par][0][4 * quad + rr][2 * (16 * n + c4)]);
-          lds_bf16x4* p1 = (lds_bf16x4*)((__attribute__((address_space(3))) uint8_t*)&s_v[par][1][4 * quad + rr][2 * (16 * n + c4)]);
-          const u32x2_t w0 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p0));
-          const u32x2_t w1 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p1));
-          return __builtin_bit_cast(bf16x8_t, u32x4_t{w0[0], w0[1], w1[0], w1[1]});
-        };
-        bf16x8_t B0 = read_b(0);
-#pragma unroll
-        for (int n = 0; n < 8; ++n) {
-          const bf16x8_t C0 = (n + 1 < 8) ? read_b(n + 1) : B0;
-          O1[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B0, O1[n], 0, 0, 0);
-          O2[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, B0, O2[n], 0, 0, 0);
-          B0 = C0;
-        }
       }
-      __syncthreads();
-    }
-  }
+      l_run += psum;
+      const bf16x8_t A1 = __builtin_bit_cast(bf16x8_t, u32x4_t{a1[0], a1[1], a1[2], a1[3]});
+      const bf16x8_t A2 = __builtin_bit_cast(bf16x8_t, u32x4_t{a2[0], a2[1], a2[2], a2[3]});
 
-  // ---- partials: hi + lo halves of O (lanes 0..31 then hold rows 4q + i of
-  // O1 / O2 for q = 0, 1), row sums; rows past p.rows are padding
-  const float lrow = quad_sum(l_run);
-#pragma unroll
-  for (int n = 0; n < 8; ++n)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      O1[n][i] = add_half_swap(O1[n][i]);
-      O2[n][i] = add_half_swap(O2[n][i]);
-    }
-  if (lane < 32) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const long long d1 = part_row(r0 + 4 * quad + i);
-      const long long d2 = part_row(r0 + 8 + 4 * quad + i);
+      // ---- PV: B operands read transposed from the LDS V tiles
+      const int rr = col >> 2;
+      const int c4 = (col & 3) * 4;
+      typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+      auto read_b = [&](int n) {
+        lds_bf16x4* p0 = (lds_bf16x4*)((__attribute__((address_space(3))) uint8_t*)&s_v[par][0][4 * quad + rr][2 * (16 * n + c4)]);
+        lds_bf16x4* p1 = (lds_bf16x4*)((__attribute__((address_space(3))) uint8_t*)&s_v[par][1][4 * quad + rr][2 * (16 * n + c4)]);
+        const u32x2_t w0 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p0));
+        const u32x2_t w1 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(p1));
+        return __builtin_bit_cast(bf16x8_t, u32x4_t{w0[0], w0[1], w1[0], w1[1]});
+      };
+      bf16x8_t B0 = read_b(0);
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
-        if (d1 >= 0) p.ws_o[d1 * kDX + 16 * n + col] = O1[n][i];
-        if (d2 >= 0) p.ws_o[d2 * kDX + 16 * n + col] = O2[n][i];
+        const bf16x8_t C0 = (n + 1 < 8) ? read_b(n + 1) : B0;
+        O1[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B0, O1[n], 0, 0, 0);
+        O2[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, B0, O2[n], 0, 0, 0);
+        B0 = C0;
       }
+    }
+    __syncthreads();
+  };
+
+  // one loop with a uniform mask flag: two loops (masked, unmasked) made
+  // the compiler rotate the accumulators through copies
+#pragma unroll 1
+  for (int it = 0; it < n_iter; ++it) {
+#pragma unroll
+    for (int k = 0; k < kRingX; ++k) pair_step(it, k, it >= n_int_iter);
+  }
+  // ---- partials: O = hi part + lo part (lane (quad, c) holds rows 4 quad + i
+  // of the wave, channel 16 n + c), row sums; rows past p.rows are padding
+  const float lrow = quad_sum(l_run);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const long long d = part_row(r0 + 4 * quad + i);
+    if (d >= 0) {
+#pragma unroll
+      for (int n = 0; n < 8; ++n) p.ws_o[d * kDX + 16 * n + col] = O1[n][i] + O2[n][i];
     }
   }
   if (lane < 16) {

@@ -234,28 +234,27 @@ __device__ __forceinline__ void compute_pair(const DecodeParams& p, const int32_
 #pragma unroll
     for (int s = 0; s < 2; ++s) St[s] = kLate ? scores_t(s, t) : S[s][kLate ? 0 : t];
     if (kLate && t == NT - 1) issue_pair<FMT>(p, bt_row, kvh, refill, t_end, lo, r);
-    float sc[8];
+    // Row col & 7's scores: the two query-term halves (columns c and c + 8)
+    // summed.  Lanes c < 8 then keep tile 0's four tokens 4 quad + i, lanes
+    // c >= 8 tile 1's, so each score's softmax runs once.
+    const int ts = hi_col ? 0 : 1;  // this lane's tile of the pair
+    float sc[4];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = St[s][i];
-        sc[4 * s + i] = x + dpp_ror8(x);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const float x0 = St[0][i] + dpp_ror8(St[0][i]);
+      const float x1 = St[1][i] + dpp_ror8(St[1][i]);
+      sc[i] = hi_col ? x0 : x1;
     }
     if constexpr (Boundary) {
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int tok = (tile + s) * 16 + 4 * quad + i;
-          const bool ok = (tok < tok_limit) && (tok <= row_last[t]);
-          sc[4 * s + i] = ok ? sc[4 * s + i] : -INFINITY;
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int tok = (tile + ts) * 16 + 4 * quad + i;
+        const bool ok = (tok < tok_limit) && (tok <= row_last[t]);
+        sc[i] = ok ? sc[i] : -INFINITY;
       }
     }
-    float mloc = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                       fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+    float mloc = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mloc = fmaxf(mloc, dpp_ror8(mloc));
     mloc = quad_max(mloc);
     // lazy reference maximum: a row's reference moves only when its running
     // maximum passes it by more than kLazyLog2, so most tiles skip the
@@ -267,18 +266,28 @@ __device__ __forceinline__ void compute_pair(const DecodeParams& p, const int32_
     const float m_use = (m_new == -INFINITY) ? 0.0f : m_new;
     st.m_run[t] = m_new;
     float psum = 0.0f;
-    uint32_t pw[4];
+    uint32_t h[2], l[2];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < 2; ++e) {
       const float p0 = __builtin_amdgcn_exp2f(sc[2 * e] - m_use);
       const float p1 = __builtin_amdgcn_exp2f(sc[2 * e + 1] - m_use);
       psum += p0 + p1;
       // hi: the upper halves of p0, p1 (bf16 by truncation, one byte permute);
       // lo: the exact remainders rounded to bf16.  |p - hi - lo| <= 2^-16 |p|.
       const uint32_t u0 = as_u32(p0), u1 = as_u32(p1);
-      const uint32_t h = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
-      const uint32_t l = pack_bf16x2(p0 - as_f32(u0 & 0xFFFF0000u), p1 - as_f32(u1 & 0xFFFF0000u));
-      pw[e] = hi_col ? h : l;
+      h[e] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+      l[e] = pack_bf16x2(p0 - as_f32(u0 & 0xFFFF0000u), p1 - as_f32(u1 & 0xFFFF0000u));
+    }
+    // PV A operand: lane c < 8 holds hi of row c for tile 0 then tile 1,
+    // lane c >= 8 lo of row c - 8; each lane passes its partner (lane c ^ 8)
+    // the half it lacks
+    uint32_t pw[4];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const uint32_t give = hi_col ? l[e] : h[e];
+      const uint32_t got = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)give, 0x128, 0xF, 0xF, false);
+      pw[e] = hi_col ? h[e] : got;
+      pw[2 + e] = hi_col ? got : l[e];
     }
     if (__builtin_expect(__builtin_amdgcn_ballot_w64(grow) != 0, 0)) {
       // a row reference moved in some lane: rescale (rare once the scan settles)
@@ -554,6 +563,7 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     lrow[t] = quad_sum(st.l_run[t]);
+    lrow[t] += dpp_ror8(lrow[t]);  // lanes c and c + 8 summed different tiles
 #pragma unroll
     for (int n = 0; n < 8; ++n) {
 #pragma unroll

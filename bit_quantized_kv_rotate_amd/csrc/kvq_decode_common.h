@@ -19,6 +19,7 @@ struct DecodeParams {
   const uint8_t* vc;
   const uint8_t* vs;
   int64_t c_head, c_page, s_head, s_page;
+  int64_t c_total, s_total;  // bytes of one code / scale array (the page scan's flat addressing)
   int P;
   int p_shift;  // log2(P)
   int hkv;

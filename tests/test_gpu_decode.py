@@ -352,3 +352,28 @@ def test_decode_convert_route_other_kernels(gpu, kind):
     want = oracle_decode_batch(f, syn.bf16_bits(q.cpu()))
     for b in range(wl.batch):
         assert_close(got[b], want[b], "%s convert route seq %d" % (kind, b))
+
+
+@pytest.mark.parametrize("fmt", ["fp4", "fp8"])
+def test_decode_cache_arrays_above_4gib(gpu, fmt):
+    """Cache arrays above 4 GiB: the page scan addresses each (page, head)
+    block through its own buffer resource instead of 32-bit page offsets
+    into one resource per array.  The sequences' pages sit past the first
+    4 GiB of the code arrays."""
+    wl = syn.Workload("big_cache", batch=3, num_kv_heads=2, num_q_heads=16, head_dim=128,
+                      page_size=16, context=0, ctx_range=(40, 700))
+    plan = syn.page_plan(wl)
+    code_page = wl.num_kv_heads * (wl.head_dim // 32) * wl.page_size * (16 if fmt == "fp4" else 32)
+    off = (1 << 32) // code_page + 1000  # every used page starts past 4 GiB
+    plan = dataclasses.replace(
+        plan, num_pages=plan.num_pages + off, block_tables=plan.block_tables + off,
+        private_pages=[p + off for p in plan.private_pages], prefix_pages=[p + off for p in plan.prefix_pages])
+    assert plan.num_pages * code_page > (1 << 32)
+    f = Filled(wl, fmt, plan=plan)
+    q = syn.queries(wl)
+    out = f.decode(q.cuda()).cpu().numpy()
+    want = oracle_decode_batch(f, syn.bf16_bits(q))
+    for b in range(wl.batch):
+        assert_close(out[b], want[b], "%s cache above 4 GiB, seq %d" % (fmt, b))
+    del f
+    torch.cuda.empty_cache()

@@ -668,9 +668,6 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
 constexpr int kMinTilesPerSplit = 8;     // 128 tokens
 constexpr int kMaxTilesPerSplit = 256;   // 4096 tokens
 constexpr int kMaxWavesPerCU = 8;        // two page-scan waves per SIMD
-// largest cache array (bytes) the flat addressing serves: page offsets are
-// 32-bit scalar offsets
-constexpr int64_t kFlatMaxBytes = 0xFFFFF000LL;
 constexpr int kDefaultWaveSlots = 2048;  // MI355X: 256 CUs x kMaxWavesPerCU
 constexpr int kMaxDevices = 64;
 
@@ -689,7 +686,7 @@ hipError_t launch_nt(const DecodeParams& p, int batch, const AppendParams* ap, h
   hipError_t e0 = hipGetLastError();
   if (e0 != hipSuccess) return e0;
   const dim3 grid((unsigned)((size_t)p.splits * p.hkv * batch));
-  if (p.c_total <= kFlatMaxBytes && p.s_total <= kFlatMaxBytes)
+  if (p.flat)
     hipLaunchKernelGGL((decode_kernel<FMT, NT, true>), grid, dim3(64), 0, stream, p);
   else
     hipLaunchKernelGGL((decode_kernel<FMT, NT, false>), grid, dim3(64), 0, stream, p);
@@ -841,6 +838,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   p.s_page = a.c.s_page;
   p.c_total = (int64_t)a.c.num_pages * a.c.c_page;
   p.s_total = (int64_t)a.c.num_pages * a.c.s_page;
+  p.flat = flat_ok(p.c_total, p.s_total);
   p.P = a.c.p;
   p.p_shift = __builtin_ctz((unsigned)a.c.p);
   p.hkv = a.c.hkv;

@@ -19,7 +19,11 @@ struct DecodeParams {
   const uint8_t* vc;
   const uint8_t* vs;
   int64_t c_head, c_page, s_head, s_page;
-  int64_t c_total, s_total;  // bytes of one code / scale array (the page scan's flat addressing)
+  int64_t c_total, s_total;  // bytes of one code / scale array
+  // 1: both arrays below 4 GiB, so a page's offset fits the 32-bit scalar
+  // offset of one buffer resource per array (flat addressing); 0: one
+  // resource per (page, head) block
+  int flat;
   int P;
   int p_shift;  // log2(P)
   int hkv;
@@ -154,6 +158,13 @@ __device__ __forceinline__ uint32_t e2m3_split(float y, int e, float& val) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t* base, int64_t off,
                                                              int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)(base + off), 0, (int)bytes, 0x00020000);
+}
+
+// Largest cache array (bytes) the flat addressing serves: page offsets are
+// 32-bit scalar offsets.
+constexpr int64_t kFlatMaxBytes = 0xFFFFF000LL;
+inline int flat_ok(int64_t c_total, int64_t s_total) {
+  return c_total <= kFlatMaxBytes && s_total <= kFlatMaxBytes;
 }
 
 // Walsh-Hadamard transform of one row of D = 64 C channels held by a wave,

@@ -134,26 +134,42 @@ struct Stage {
   uint32_t sc;
 };
 
+// FLAT (cache arrays below 4 GiB): one buffer resource per array from this
+// head on (loop-invariant, built once), the page as the 32-bit scalar
+// offset; else one resource per (page, head) block.
+template <bool FLAT>
 __device__ __forceinline__ void load_stage(const DecodeParams& p, const int32_t* bt_row, int kvh, int tile,
                                            bool v, int lane, Stage& t) {
   const int tok = tile * 16;
   const int page = __builtin_amdgcn_readfirstlane(bt_row[tok >> p.p_shift]);
   const int in_page = tok & (p.P - 1);
-  const int64_t cb = (int64_t)page * p.c_page + (int64_t)kvh * p.c_head;
-  const int64_t sb = (int64_t)page * p.s_page + (int64_t)kvh * p.s_head;
   const int idx = (lane >> 4) * p.P + (lane & 15);
-  const __amdgpu_buffer_rsrc_t rc = block_rsrc(v ? p.vc : p.kc, cb, p.c_head);
-  const __amdgpu_buffer_rsrc_t rs = block_rsrc(v ? p.vs : p.ks, sb, p.s_head);
-  const u32x4_t a = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, idx * 16, in_page * 16, 2));
+  __amdgpu_buffer_rsrc_t rc, rs;
+  int coff, soff;
+  if constexpr (FLAT) {
+    const int64_t ch = (int64_t)kvh * p.c_head, sh = (int64_t)kvh * p.s_head;
+    rc = block_rsrc(v ? p.vc : p.kc, ch, p.c_total - ch);
+    rs = block_rsrc(v ? p.vs : p.ks, sh, p.s_total - sh);
+    coff = (int)((uint32_t)page * (uint32_t)p.c_page + (uint32_t)in_page * 16u);
+    soff = (int)((uint32_t)page * (uint32_t)p.s_page + (uint32_t)in_page);
+  } else {
+    const int64_t cb = (int64_t)page * p.c_page + (int64_t)kvh * p.c_head;
+    const int64_t sb = (int64_t)page * p.s_page + (int64_t)kvh * p.s_head;
+    rc = block_rsrc(v ? p.vc : p.kc, cb, p.c_head);
+    rs = block_rsrc(v ? p.vs : p.ks, sb, p.s_head);
+    coff = in_page * 16;
+    soff = in_page;
+  }
+  const u32x4_t a = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rc, idx * 16, coff, 2));
 #pragma unroll
   for (int w = 0; w < 4; ++w) t.c[w] = a[w];
-  t.sc = __builtin_amdgcn_raw_buffer_load_b8(rs, idx, in_page, 0);
+  t.sc = __builtin_amdgcn_raw_buffer_load_b8(rs, idx, soff, 0);
 }
 
 // GRP: prefix level of a shared-prefix decode (units are prefix groups; see
 // DecodeParams); otherwise units are sequences, optionally scanned from
 // p.tok_start[b] on.
-template <bool GRP, int WAVES, bool CONV = false>
+template <bool GRP, int WAVES, bool CONV = false, bool FLAT = true>
 __global__ __launch_bounds__(64 * WAVES) void extend_kernel(const DecodeParams p) {
   constexpr int kRowsX = 16 * WAVES;                // rows per block
   constexpr int kJobs = WAVES >= 4 ? 1 : 4 / WAVES;  // staging jobs per staging wave
@@ -228,7 +244,7 @@ __global__ __launch_bounds__(64 * WAVES) void extend_kernel(const DecodeParams p
   // one each and both waves of a narrow block take two
   const bool stager = w < 4;
   auto fetch = [&](int pi, int j, Stage& c) {
-    load_stage(p, bt_row, kvh, min(t_begin + 2 * pi + (j & 1), t_end - 1), j >= 2, lane, c);
+    load_stage<FLAT>(p, bt_row, kvh, min(t_begin + 2 * pi + (j & 1), t_end - 1), j >= 2, lane, c);
   };
   auto stage = [&](int pi, int j, const Stage& c) {
     const int st_tile = j & 1;
@@ -578,6 +594,14 @@ int plan_extend_rows(const CacheGeom& c, int batch, long long rows, int max_cont
   return KVQ_OK;
 }
 
+template <bool GRP, int WAVES, bool CONV>
+void launch_x(const DecodeParams& p, dim3 grid, hipStream_t stream) {
+  if (p.flat)
+    hipLaunchKernelGGL((extend_kernel<GRP, WAVES, CONV, true>), grid, dim3(64 * WAVES), 0, stream, p);
+  else
+    hipLaunchKernelGGL((extend_kernel<GRP, WAVES, CONV, false>), grid, dim3(64 * WAVES), 0, stream, p);
+}
+
 hipError_t launch_extend(const DecodeArgs& a, hipStream_t stream) {
   DecodeParams p{};
   p.kc = a.c.kc;
@@ -588,6 +612,9 @@ hipError_t launch_extend(const DecodeArgs& a, hipStream_t stream) {
   p.c_page = a.c.c_page;
   p.s_head = a.c.s_head;
   p.s_page = a.c.s_page;
+  p.c_total = (int64_t)a.c.num_pages * a.c.c_page;
+  p.s_total = (int64_t)a.c.num_pages * a.c.s_page;
+  p.flat = flat_ok(p.c_total, p.s_total);
   p.P = a.c.p;
   p.p_shift = __builtin_ctz((unsigned)a.c.p);
   p.hkv = a.c.hkv;
@@ -634,17 +661,17 @@ hipError_t launch_extend(const DecodeArgs& a, hipStream_t stream) {
   const dim3 grid((unsigned)((size_t)p.splits * units * a.plan.row_tiles));
   const bool narrow = a.plan.block_rows == 16 * kNarrowX;
   if (conv && narrow)
-    hipLaunchKernelGGL((extend_kernel<false, kNarrowX, true>), grid, dim3(64 * kNarrowX), 0, stream, p);
+    launch_x<false, kNarrowX, true>(p, grid, stream);
   else if (conv)
-    hipLaunchKernelGGL((extend_kernel<false, kWideX, true>), grid, dim3(64 * kWideX), 0, stream, p);
+    launch_x<false, kWideX, true>(p, grid, stream);
   else if (grp && narrow)
-    hipLaunchKernelGGL((extend_kernel<true, kNarrowX>), grid, dim3(64 * kNarrowX), 0, stream, p);
+    launch_x<true, kNarrowX, false>(p, grid, stream);
   else if (grp)
-    hipLaunchKernelGGL((extend_kernel<true, kWideX>), grid, dim3(64 * kWideX), 0, stream, p);
+    launch_x<true, kWideX, false>(p, grid, stream);
   else if (narrow)
-    hipLaunchKernelGGL((extend_kernel<false, kNarrowX>), grid, dim3(64 * kNarrowX), 0, stream, p);
+    launch_x<false, kNarrowX, false>(p, grid, stream);
   else
-    hipLaunchKernelGGL((extend_kernel<false, kWideX>), grid, dim3(64 * kWideX), 0, stream, p);
+    launch_x<false, kWideX, false>(p, grid, stream);
   e = hipGetLastError();
   if (e != hipSuccess || a.keep_partials) return e;
   hipLaunchKernelGGL((merge_kernel<0, 2>), dim3(qblocks), dim3(256), 0, stream, p);

@@ -354,14 +354,15 @@ def test_decode_convert_route_other_kernels(gpu, kind):
         assert_close(got[b], want[b], "%s convert route seq %d" % (kind, b))
 
 
-@pytest.mark.parametrize("fmt", ["fp4", "fp8"])
-def test_decode_cache_arrays_above_4gib(gpu, fmt):
-    """Cache arrays above 4 GiB: the page scan addresses each (page, head)
-    block through its own buffer resource instead of 32-bit page offsets
-    into one resource per array.  The sequences' pages sit past the first
-    4 GiB of the code arrays."""
+@pytest.mark.parametrize("fmt,n_q", [("fp4", 1), ("fp8", 1), ("fp4", 3)])
+def test_decode_cache_arrays_above_4gib(gpu, fmt, n_q):
+    """Cache arrays above 4 GiB: the page scan (8 rows) and the many-row
+    kernel (24 rows, FP4) address each (page, head) block through its own
+    buffer resource instead of 32-bit page offsets into one resource per
+    array.  The sequences' pages sit past the first 4 GiB of the code
+    arrays."""
     wl = syn.Workload("big_cache", batch=3, num_kv_heads=2, num_q_heads=16, head_dim=128,
-                      page_size=16, context=0, ctx_range=(40, 700))
+                      page_size=16, context=0, n_q=n_q, ctx_range=(40, 700))
     plan = syn.page_plan(wl)
     code_page = wl.num_kv_heads * (wl.head_dim // 32) * wl.page_size * (16 if fmt == "fp4" else 32)
     off = (1 << 32) // code_page + 1000  # every used page starts past 4 GiB
@@ -374,6 +375,6 @@ def test_decode_cache_arrays_above_4gib(gpu, fmt):
     out = f.decode(q.cuda()).cpu().numpy()
     want = oracle_decode_batch(f, syn.bf16_bits(q))
     for b in range(wl.batch):
-        assert_close(out[b], want[b], "%s cache above 4 GiB, seq %d" % (fmt, b))
+        assert_close(out[b], want[b], "%s n_q %d cache above 4 GiB, seq %d" % (fmt, n_q, b))
     del f
     torch.cuda.empty_cache()

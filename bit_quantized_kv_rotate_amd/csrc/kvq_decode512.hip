@@ -55,7 +55,10 @@ struct Chunk5 {
   uint32_t vsc;
 };
 
-template <bool SHARED, bool SEL>
+// FLAT (cache arrays below 4 GiB): one buffer resource per array from this
+// head on (loop-invariant), the page as the 32-bit scalar offset; else one
+// resource per (page, head) block.
+template <bool SHARED, bool SEL, bool FLAT>
 __device__ __forceinline__ void load_chunk5(const DecodeParams& p, const int32_t* bt_row, const int32_t* sel_row,
                                             int L, int kvh, int tile, int chunk, int lane, Chunk5& t) {
   if constexpr (SEL) {
@@ -84,23 +87,38 @@ __device__ __forceinline__ void load_chunk5(const DecodeParams& p, const int32_t
   const int tok = tile * 16;
   const int page = __builtin_amdgcn_readfirstlane(bt_row[tok >> p.p_shift]);
   const int in_page = tok & (p.P - 1);
-  const int64_t cb = (int64_t)page * p.c_page + (int64_t)kvh * p.c_head;
-  const int64_t sb = (int64_t)page * p.s_page + (int64_t)kvh * p.s_head;
   const int idx = (4 * chunk + (lane >> 4)) * p.P + (lane & 15);
-  const int coff = in_page * 16;
-  const __amdgpu_buffer_rsrc_t rk = block_rsrc(p.kc, cb, p.c_head);
-  const __amdgpu_buffer_rsrc_t rks = block_rsrc(p.ks, sb, p.s_head);
+  const int64_t ch = (int64_t)kvh * p.c_head, sh = (int64_t)kvh * p.s_head;
+  int64_t cb, sb, cn, sn;
+  int coff, soff;
+  if constexpr (FLAT) {
+    cb = ch;
+    sb = sh;
+    cn = p.c_total - ch;
+    sn = p.s_total - sh;
+    coff = (int)((uint32_t)page * (uint32_t)p.c_page + (uint32_t)in_page * 16u);
+    soff = (int)((uint32_t)page * (uint32_t)p.s_page + (uint32_t)in_page);
+  } else {
+    cb = (int64_t)page * p.c_page + ch;
+    sb = (int64_t)page * p.s_page + sh;
+    cn = p.c_head;
+    sn = p.s_head;
+    coff = in_page * 16;
+    soff = in_page;
+  }
+  const __amdgpu_buffer_rsrc_t rk = block_rsrc(p.kc, cb, cn);
+  const __amdgpu_buffer_rsrc_t rks = block_rsrc(p.ks, sb, sn);
   const u32x4_t a = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, idx * 16, coff, 2));
 #pragma unroll
   for (int w = 0; w < 4; ++w) t.k[w] = a[w];
-  t.ksc = __builtin_amdgcn_raw_buffer_load_b8(rks, idx, in_page, 0);
+  t.ksc = __builtin_amdgcn_raw_buffer_load_b8(rks, idx, soff, 0);
   if constexpr (!SHARED) {
-    const __amdgpu_buffer_rsrc_t rv = block_rsrc(p.vc, cb, p.c_head);
-    const __amdgpu_buffer_rsrc_t rvs = block_rsrc(p.vs, sb, p.s_head);
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc(p.vc, cb, cn);
+    const __amdgpu_buffer_rsrc_t rvs = block_rsrc(p.vs, sb, sn);
     const u32x4_t c = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, idx * 16, coff, 2));
 #pragma unroll
     for (int w = 0; w < 4; ++w) t.v[w] = c[w];
-    t.vsc = __builtin_amdgcn_raw_buffer_load_b8(rvs, idx, in_page, 0);
+    t.vsc = __builtin_amdgcn_raw_buffer_load_b8(rvs, idx, soff, 0);
   }
 }
 
@@ -370,7 +388,7 @@ __device__ __forceinline__ void group_softmax(const f32x4_t (&S)[2], int tile, i
 // SEL: the scan runs over the list of selected positions of each sequence
 // (p.sel; context_lens are the list lengths), one query position per
 // sequence.
-template <int RG, bool SHARED, bool SEL, bool CONV = false>
+template <int RG, bool SHARED, bool SEL, bool CONV = false, bool FLAT = true>
 __global__ __launch_bounds__(512) void decode512_kernel(const DecodeParams p) {
   constexpr int ROWS = 16 * RG;
   constexpr int NO = 2 * RG;
@@ -427,7 +445,7 @@ __global__ __launch_bounds__(512) void decode512_kernel(const DecodeParams p) {
   };
   // refill a ring slot with pair pi (clamped to the split's last tile)
   auto fetch = [&](int pi, Chunk5& c) {
-    load_chunk5<SHARED, SEL>(p, bt_row, sel_row, L, kvh, min(t_begin + 2 * pi + mtile, t_end - 1), mchunk, lane, c);
+    load_chunk5<SHARED, SEL, FLAT>(p, bt_row, sel_row, L, kvh, min(t_begin + 2 * pi + mtile, t_end - 1), mchunk, lane, c);
   };
 
   Chunk5 ring[kRing5];
@@ -607,7 +625,7 @@ __global__ __launch_bounds__(512) void decode512_kernel(const DecodeParams p) {
 // by four owners' waves instead of eight, P by four output waves).  With
 // fewer rows the score waves' two softmax chains are the longer path and
 // the plain kernel is faster.
-template <int RG, bool SHARED, bool SEL, bool CONV = false>
+template <int RG, bool SHARED, bool SEL, bool CONV = false, bool FLAT = true>
 __global__ __launch_bounds__(512) void decode512r_kernel(const DecodeParams p) {
   constexpr int ROWS = 16 * RG;
   constexpr int NO = 2 * RG;
@@ -796,7 +814,7 @@ __global__ __launch_bounds__(512) void decode512r_kernel(const DecodeParams p) {
     for (int i = 0; i < 4; ++i) dst[i] = u32x4_t{vb[4 * i], vb[4 * i + 1], vb[4 * i + 2], vb[4 * i + 3]};
   };
   auto fetch = [&](int pi, int t, Chunk5& c) {
-    load_chunk5<SHARED, SEL>(p, bt_row, sel_row, L, kvh, min(t_begin + 2 * pi + t, t_end - 1), v, lane, c);
+    load_chunk5<SHARED, SEL, FLAT>(p, bt_row, sel_row, L, kvh, min(t_begin + 2 * pi + t, t_end - 1), v, lane, c);
   };
   Chunk5 ring[kRing][2];
   if (n_pairs > 0) {
@@ -949,10 +967,19 @@ hipError_t launch5(const DecodeParams& p, int batch, hipStream_t stream) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 grid((unsigned)p.splits, (unsigned)p.hkv, (unsigned)batch);
-  if constexpr (RG >= kRoleSplitRG5)
-    hipLaunchKernelGGL((decode512r_kernel<RG, SHARED, SEL, CONV>), grid, dim3(64 * kW5), 0, stream, p);
-  else
-    hipLaunchKernelGGL((decode512_kernel<RG, SHARED, SEL, CONV>), grid, dim3(64 * kW5), 0, stream, p);
+  // the gathered selection (SEL) addresses every lane's page on its own
+  const bool flat = p.flat && !SEL;
+  if constexpr (RG >= kRoleSplitRG5) {
+    if (flat)
+      hipLaunchKernelGGL((decode512r_kernel<RG, SHARED, SEL, CONV, true>), grid, dim3(64 * kW5), 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode512r_kernel<RG, SHARED, SEL, CONV, false>), grid, dim3(64 * kW5), 0, stream, p);
+  } else {
+    if (flat)
+      hipLaunchKernelGGL((decode512_kernel<RG, SHARED, SEL, CONV, true>), grid, dim3(64 * kW5), 0, stream, p);
+    else
+      hipLaunchKernelGGL((decode512_kernel<RG, SHARED, SEL, CONV, false>), grid, dim3(64 * kW5), 0, stream, p);
+  }
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((merge_kernel<16 * RG, 8>), dim3(qblocks), dim3(256), 0, stream, p);
@@ -1023,6 +1050,9 @@ hipError_t launch_decode512(const DecodeArgs& a, hipStream_t stream) {
   p.c_page = a.c.c_page;
   p.s_head = a.c.s_head;
   p.s_page = a.c.s_page;
+  p.c_total = (int64_t)a.c.num_pages * a.c.c_page;
+  p.s_total = (int64_t)a.c.num_pages * a.c.s_page;
+  p.flat = flat_ok(p.c_total, p.s_total);
   p.P = a.c.p;
   p.p_shift = __builtin_ctz((unsigned)a.c.p);
   p.hkv = a.c.hkv;

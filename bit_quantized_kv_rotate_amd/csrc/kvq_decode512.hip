@@ -276,6 +276,27 @@ __device__ __forceinline__ void load_qconv5(const DecodeParams& p, int bh, int N
           bf16x8_t, *reinterpret_cast<const u32x4_t*>(p.qops + (((((size_t)bh * NO + owner) * 4 + c) * 4 + j) * 64 + lane) * 4));
 }
 
+// Byte J of a transposed code read (the channel pair of one token) to two
+// bf16, with that token's scale: byte J of `sb`.
+// (the scale operand byte << 23 in one SDWA shift)
+template <int J>
+__device__ __forceinline__ uint32_t cvt_token(int codes, uint32_t sb, uint32_t k23) {
+  uint32_t s;
+  if constexpr (J == 0)
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0"
+        : "=v"(s) : "v"(k23), "v"(sb));
+  else if constexpr (J == 1)
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1"
+        : "=v"(s) : "v"(k23), "v"(sb));
+  else if constexpr (J == 2)
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2"
+        : "=v"(s) : "v"(k23), "v"(sb));
+  else
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
+        : "=v"(s) : "v"(k23), "v"(sb));
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)codes, as_f32(s), J));
+}
+
 // Online softmax of one 8-row score owner over a tile pair, from its scores
 // S (tile t, token 4 quad + i; column c of the MFMA output holds query-term
 // half c / 8 of row c & 7, so x + its ror-8 partner is the row's score):
@@ -630,9 +651,16 @@ __global__ __launch_bounds__(512) void decode512r_kernel(const DecodeParams p) {
   constexpr int ROWS = 16 * RG;
   constexpr int NO = 2 * RG;
   constexpr int kRing = 1;  // tile pairs in flight per staging wave (a deeper ring spills)
-  __shared__ __attribute__((aligned(16))) u32x4_t s_k[2][2][4][64];
-  __shared__ uint32_t s_ks[2][2][4][64];
-  __shared__ __attribute__((aligned(16))) uint8_t s_v[3][2][16][kVRow5];
+  // staged FP4 codes, three buffers (pair i + 2 is staged while the scores
+  // read pair i + 1 and PV reads pair i): K as the score MFMA's A operand,
+  // with its scale bytes; V (the K codes themselves when K = V) is read by
+  // the PV waves straight from these codes, with its scale bytes in
+  // s_vsb[buf][tile][chunk][token / 4][group][token % 4] (zero past the
+  // context)
+  __shared__ __attribute__((aligned(16))) u32x4_t s_k[3][2][4][64];
+  __shared__ uint32_t s_ks[3][2][4][64];
+  __shared__ __attribute__((aligned(16))) u32x4_t s_vc[SHARED ? 1 : 3][2][4][64];
+  __shared__ __attribute__((aligned(16))) uint8_t s_vsb[3][2][4][64];
   __shared__ __attribute__((aligned(16))) u32x4_t s_p[2][RG][2][64];
   __shared__ float s_alpha[2][ROWS];
   __shared__ int s_flag[2][NO];
@@ -688,6 +716,7 @@ __global__ __launch_bounds__(512) void decode512r_kernel(const DecodeParams p) {
       float m_run = -INFINITY, l_run = 0.0f;
       auto scores = [&](int pi) {
         const int par = pi & 1;
+        const int kbuf = pi % 3;
         const int tile = t_begin + 2 * pi;
         f32x4_t S[2];
 #pragma unroll
@@ -696,8 +725,8 @@ __global__ __launch_bounds__(512) void decode512r_kernel(const DecodeParams p) {
           f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            const u32x4_t kc = s_k[par][tt][c][lane];
-            const int ksc = (int)s_ks[par][tt][c][lane];
+            const u32x4_t kc = s_k[kbuf][tt][c][lane];
+            const int ksc = (int)s_ks[kbuf][tt][c][lane];
             const i32x8_t A = {(int)kc[0], (int)kc[1], (int)kc[2], (int)kc[3], 0, 0, 0, 0};
             f32x4_t& acc = (c & 1) ? a1 : a0;
             // the query scale of term tm is byte tm of qs[c]
@@ -749,6 +778,7 @@ __global__ __launch_bounds__(512) void decode512r_kernel(const DecodeParams p) {
     }
     auto scores = [&](int pi) {
       const int par = pi & 1;
+      const int kbuf = pi % 3;
       const int tile = t_begin + 2 * pi;
       f32x4_t S[2][2];
       // each chunk's K codes converted once, for both owners
@@ -757,10 +787,10 @@ __global__ __launch_bounds__(512) void decode512r_kernel(const DecodeParams p) {
         f32x4_t a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const u32x4_t kc = s_k[par][tt][c][lane];
+          const u32x4_t kc = s_k[kbuf][tt][c][lane];
           const uint32_t kw[4] = {kc[0], kc[1], kc[2], kc[3]};
           uint32_t kb[16];
-          dequant_group<KVQ_FMT_FP4_E2M1>(kw, scale_operand(s_ks[par][tt][c][lane]), kb);
+          dequant_group<KVQ_FMT_FP4_E2M1>(kw, scale_operand(s_ks[kbuf][tt][c][lane]), kb);
           a0 = qk_chunk5_conv(a0, kb, qv[0][c]);
           a1 = qk_chunk5_conv(a1, kb, qv[1][c]);
         }
@@ -798,20 +828,17 @@ __global__ __launch_bounds__(512) void decode512r_kernel(const DecodeParams p) {
 
   // ---------------- output wave: channels 128v .. 128v + 127, staging of chunk v
   const int v = w - 4;
+  // stage pair pi: codes and scale bytes as they came (lane = token col,
+  // group quad of chunk v); V's scale byte is zero past the context, so
+  // whatever codes the cache holds there convert to zero
   auto stage = [&](int pi, int t, const Chunk5& c) {
     const int tile = t_begin + 2 * pi + t;
-    s_k[pi & 1][t][v][lane] = u32x4_t{c.k[0], c.k[1], c.k[2], c.k[3]};
-    s_ks[pi & 1][t][v][lane] = c.ksc;
+    const int buf = pi % 3;
+    s_k[buf][t][v][lane] = u32x4_t{c.k[0], c.k[1], c.k[2], c.k[3]};
+    s_ks[buf][t][v][lane] = c.ksc;
+    if constexpr (!SHARED) s_vc[buf][t][v][lane] = u32x4_t{c.v[0], c.v[1], c.v[2], c.v[3]};
     const bool dead = tile * 16 + col >= tok_limit;
-    uint32_t vw[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) vw[i] = dead ? 0u : (SHARED ? c.k[i] : c.v[i]);
-    const uint32_t vsc = dead ? 0u : (SHARED ? c.ksc : c.vsc);
-    uint32_t vb[16];
-    dequant_group<KVQ_FMT_FP4_E2M1>(vw, scale_operand(vsc), vb);
-    u32x4_t* dst = reinterpret_cast<u32x4_t*>(&s_v[pi % 3][t][col][2 * (128 * v + 32 * quad)]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = u32x4_t{vb[4 * i], vb[4 * i + 1], vb[4 * i + 2], vb[4 * i + 3]};
+    s_vsb[buf][t][v][16 * (col >> 2) + 4 * quad + (col & 3)] = (uint8_t)(dead ? 0u : (SHARED ? c.ksc : c.vsc));
   };
   auto fetch = [&](int pi, int t, Chunk5& c) {
     load_chunk5<SHARED, SEL, FLAT>(p, bt_row, sel_row, L, kvh, min(t_begin + 2 * pi + t, t_end - 1), v, lane, c);
@@ -845,9 +872,17 @@ __global__ __launch_bounds__(512) void decode512r_kernel(const DecodeParams p) {
   }
   __syncthreads();
 
-  const int rr = col >> 2;
-  const int c4 = (col & 3) * 4;
-  typedef __attribute__((address_space(3))) bf16x4_t lds_bf16x4;
+  // PV B operands from the staged FP4 codes: one transposing byte read per
+  // 32-channel group gives lane (quad, col) byte col of the eight token
+  // records 4 quad .. 4 quad + 3 of tile 0 and of tile 1 (the k order of the
+  // P operands), i.e. channels 2 col and 2 col + 1 of eight tokens; row j of
+  // the read (lanes 2j, 2j + 1 of the quad: the record's two halves) is
+  // token 4 quad + j % 4 of tile j / 4.  Each byte is converted with its
+  // token's scale; even and odd channels make two n-tiles.
+  typedef int v2i_t __attribute__((ext_vector_type(2)));
+  typedef __attribute__((address_space(3))) v2i_t lds_v2i;
+  const int vlane = (col >> 3) * (int)sizeof(s_k[0][0]) + (4 * quad + ((col >> 1) & 3)) * 16 + 8 * (col & 1);
+  const uint32_t k23 = 23;
 #pragma unroll 1
   for (int it = 0; it < n_iter; ++it) {
 #pragma unroll
@@ -869,28 +904,38 @@ __global__ __launch_bounds__(512) void decode512r_kernel(const DecodeParams p) {
         A[g][0] = __builtin_bit_cast(bf16x8_t, s_p[par][g][0][lane]);
         A[g][1] = __builtin_bit_cast(bf16x8_t, s_p[par][g][1][lane]);
       }
-      const int vb = pi % 3;
-      // one LDS base per pair; the reads of tile 1 and of channel tile n
-      // are constant offsets from it
-      // (the buffer offset is made uniform so that the compiler keeps one
-      // lane address instead of one per read)
-      const int vbuf = __builtin_amdgcn_readfirstlane(vb * (int)sizeof(s_v[0]));
+      const int kbuf = pi % 3;
+      // (buffer offsets uniform, so that one lane address serves every read)
+      const int cbuf = __builtin_amdgcn_readfirstlane(kbuf * (int)sizeof(s_k[0]) + v * (int)sizeof(s_k[0][0][0]));
       __attribute__((address_space(3))) uint8_t* const vrow =
-          (__attribute__((address_space(3))) uint8_t*)&s_v[0][0][4 * quad + rr][2 * (128 * v + c4)] + vbuf;
-      auto read_b = [&](int n) {
-        lds_bf16x4* a0 = (lds_bf16x4*)(vrow + 32 * n);
-        lds_bf16x4* a1 = (lds_bf16x4*)(vrow + 16 * kVRow5 + 32 * n);
-        const u32x2_t w0 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(a0));
-        const u32x2_t w1 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4bf16(a1));
-        return __builtin_bit_cast(bf16x8_t, u32x4_t{w0[0], w0[1], w1[0], w1[1]});
-      };
+          (__attribute__((address_space(3))) uint8_t*)(SHARED ? &s_k[0][0][0][0] : &s_vc[0][0][0][0]) + vlane + cbuf;
+      v2i_t raw[4];
 #pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const bf16x8_t B = read_b(n);
+      for (int gg = 0; gg < 4; ++gg)
+        raw[gg] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vrow + 256 * gg));
+      // scale bytes of tokens 4 quad .. 4 quad + 3, groups 0..3, per tile
+      const u32x4_t sb0 = *reinterpret_cast<const u32x4_t*>(&s_vsb[kbuf][0][v][16 * quad]);
+      const u32x4_t sb1 = *reinterpret_cast<const u32x4_t*>(&s_vsb[kbuf][1][v][16 * quad]);
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg) {
+        const uint32_t d[8] = {cvt_token<0>(raw[gg][0], sb0[gg], k23), cvt_token<1>(raw[gg][0], sb0[gg], k23),
+                               cvt_token<2>(raw[gg][0], sb0[gg], k23), cvt_token<3>(raw[gg][0], sb0[gg], k23),
+                               cvt_token<0>(raw[gg][1], sb1[gg], k23), cvt_token<1>(raw[gg][1], sb1[gg], k23),
+                               cvt_token<2>(raw[gg][1], sb1[gg], k23), cvt_token<3>(raw[gg][1], sb1[gg], k23)};
+        uint32_t be[4], bo[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          be[m] = __builtin_amdgcn_perm(d[2 * m + 1], d[2 * m], 0x05040100u);
+          bo[m] = __builtin_amdgcn_perm(d[2 * m + 1], d[2 * m], 0x07060302u);
+        }
+        const bf16x8_t Be = __builtin_bit_cast(bf16x8_t, u32x4_t{be[0], be[1], be[2], be[3]});
+        const bf16x8_t Bo = __builtin_bit_cast(bf16x8_t, u32x4_t{bo[0], bo[1], bo[2], bo[3]});
 #pragma unroll
         for (int g = 0; g < RG; ++g) {
-          O[g][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][0], B, O[g][n], 0, 0, 0);
-          O[g][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][1], B, O[g][n], 0, 0, 0);
+          O[g][2 * gg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][0], Be, O[g][2 * gg], 0, 0, 0);
+          O[g][2 * gg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][1], Be, O[g][2 * gg], 0, 0, 0);
+          O[g][2 * gg + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][0], Bo, O[g][2 * gg + 1], 0, 0, 0);
+          O[g][2 * gg + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[g][1], Bo, O[g][2 * gg + 1], 0, 0, 0);
         }
       }
       {
@@ -903,13 +948,14 @@ __global__ __launch_bounds__(512) void decode512r_kernel(const DecodeParams p) {
       __syncthreads();
     }
   }
+  // n-tile n holds channels 128 v + 32 (n / 2) + 2 col + n % 2
 #pragma unroll
   for (int g = 0; g < RG; ++g)
 #pragma unroll
     for (int n = 0; n < 8; ++n)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        p.ws_o[(base + 16 * g + 4 * quad + i) * kD5 + 128 * v + 16 * n + col] = O[g][n][i];
+        p.ws_o[(base + 16 * g + 4 * quad + i) * kD5 + 128 * v + 32 * (n >> 1) + 2 * col + (n & 1)] = O[g][n][i];
 }
 
 constexpr int kMinTilesPerSplit5 = 8;

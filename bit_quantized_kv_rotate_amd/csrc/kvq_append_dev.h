@@ -66,10 +66,12 @@ __device__ __forceinline__ void encode_fp8_group(float (&x)[32], int e_s, float 
 }
 
 // The value x holds in lane l ^ s (s a power of two below 64): a DPP quad
-// permutation for s = 1 and 2, the LDS permute network above.
+// permutation for s = 1 and 2 (every source lane is in range, so the zero
+// fill of bound_ctrl never applies; it lets the move fold into the add that
+// uses it), the LDS permute network above.
 __device__ __forceinline__ float xor_lane(float x, int s) {
-  if (s == 1) return as_f32((uint32_t)__builtin_amdgcn_mov_dpp((int)as_u32(x), 0xB1, 0xF, 0xF, false));  // [1,0,3,2]
-  if (s == 2) return as_f32((uint32_t)__builtin_amdgcn_mov_dpp((int)as_u32(x), 0x4E, 0xF, 0xF, false));  // [2,3,0,1]
+  if (s == 1) return as_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u32(x), 0xB1, 0xF, 0xF, true));  // [1,0,3,2]
+  if (s == 2) return as_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u32(x), 0x4E, 0xF, 0xF, true));  // [2,3,0,1]
   return __shfl_xor(x, s, 64);
 }
 
@@ -146,13 +148,15 @@ __device__ __forceinline__ void append_wave(const AppendParams& p, int wave, int
         }
       }
     }
+    // y - x is y + (-x) and x + y is y + x, exactly: one add with the
+    // lane's sign on x
 #pragma unroll
     for (int s = 1; s < G; s <<= 1) {
+      float sx[32];
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        const float y = xor_lane(x[i], s);
-        x[i] = (g & s) ? (y - x[i]) : (x[i] + y);
-      }
+      for (int i = 0; i < 32; ++i) sx[i] = (g & s) ? -x[i] : x[i];
+#pragma unroll
+      for (int i = 0; i < 32; ++i) x[i] = xor_lane(x[i], s) + sx[i];
     }
 #pragma unroll
     for (int i = 0; i < 32; ++i) x[i] = x[i] * p.norm;
@@ -169,8 +173,9 @@ __device__ __forceinline__ void append_wave(const AppendParams& p, int wave, int
   const int byte = max(field - (fp4 ? 2 : 8), 0);
   const int e_s = byte - 127;
 
-  const int page = slot / c.p;
-  const int off = slot - page * c.p;
+  // (the page size is 16, 32 or 64 and the slot is not negative here)
+  const int page = slot >> __builtin_ctz((unsigned)c.p);
+  const int off = slot & (c.p - 1);
   const int64_t unit = (int64_t)g * c.p + off;  // (group, offset) inside the (page, head) block
   uint8_t* codes = (tensor == 0 ? p.kc : p.vc) + (int64_t)page * c.c_page + (int64_t)h * c.c_head + unit * c.cb;
   uint8_t* scales = (tensor == 0 ? p.ks : p.vs) + (int64_t)page * c.s_page + (int64_t)h * c.s_head;

@@ -185,12 +185,22 @@ __device__ __forceinline__ void wave_fwht(float (&x)[C], int lane, float c) {
       }
     }
   }
+  // (y - x is y + (-x) and x + y is y + x, exactly; lanes 1 and 2 apart
+  // exchange by DPP quad permutations, the rest through the LDS permute
+  // network)
 #pragma unroll
   for (int hs = 1; hs < 64; hs <<= 1) {
 #pragma unroll
     for (int i = 0; i < C; ++i) {
-      const float y = __shfl_xor(x[i], hs, 64);
-      x[i] = (lane & hs) ? (y - x[i]) : (x[i] + y);
+      const float sx = (lane & hs) ? -x[i] : x[i];
+      float y;
+      if (hs == 1)
+        y = as_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u32(x[i]), 0xB1, 0xF, 0xF, true));
+      else if (hs == 2)
+        y = as_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u32(x[i]), 0x4E, 0xF, 0xF, true));
+      else
+        y = __shfl_xor(x[i], hs, 64);
+      x[i] = y + sx;
     }
   }
 #pragma unroll

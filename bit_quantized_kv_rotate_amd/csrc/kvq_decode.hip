@@ -423,10 +423,7 @@ __device__ __forceinline__ void qprep_row(const DecodeParams& p, int gr, int lan
 #pragma unroll
     for (int tm = 0; tm < kQTerms; ++tm) {
       float am = fmaxf(fabsf(x0), fabsf(x1));
-      am = fmaxf(am, __shfl_xor(am, 1, 64));
-      am = fmaxf(am, __shfl_xor(am, 2, 64));
-      am = fmaxf(am, __shfl_xor(am, 4, 64));
-      am = fmaxf(am, __shfl_xor(am, 8, 64));
+      am = row16_max(am);
       const int byte = max((int)((as_u32(am) >> 23) & 0xFFu) - 2, 0);
       const int e = byte - 127;
       float v0, v1;
@@ -435,7 +432,7 @@ __device__ __forceinline__ void qprep_row(const DecodeParams& p, int gr, int lan
       x0 -= v0;
       x1 -= v1;
       const uint32_t v12 = c0 | (c1 << 6);
-      const uint32_t u24 = v12 | ((uint32_t)__shfl_xor((int)v12, 1, 64) << 12);  // valid on even li
+      const uint32_t u24 = v12 | ((uint32_t)__builtin_amdgcn_update_dpp(0, (int)v12, kDppXor1, 0xF, 0xF, true) << 12);  // valid on even li
       const uint32_t ua = (uint32_t)__shfl((int)u24, src_a, 64);
       const uint32_t ub = (uint32_t)__shfl((int)u24, src_a + 2, 64);
       const uint32_t d = (ua >> sh) | (ub << (24 - sh));

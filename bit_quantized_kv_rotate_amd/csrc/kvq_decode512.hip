@@ -189,8 +189,8 @@ __global__ __launch_bounds__(256) void qprep512_kernel(const DecodeParams p) {
     float am = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(x[i]));
-    am = fmaxf(am, __shfl_xor(am, 1, 64));
-    am = fmaxf(am, __shfl_xor(am, 2, 64));
+    am = fmaxf(am, dpp_f32<kDppXor1>(am));
+    am = fmaxf(am, dpp_f32<kDppXor2>(am));
     const int byte = max((int)((as_u32(am) >> 23) & 0xFFu) - 2, 0);
     const int e = byte - 127;
     uint64_t bits = 0;

@@ -5,6 +5,8 @@
 // anonymous namespace: each translation unit gets its own copy.
 #pragma once
 
+#include <type_traits>
+
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -167,6 +169,45 @@ inline int flat_ok(int64_t c_total, int64_t s_total) {
   return c_total <= kFlatMaxBytes && s_total <= kFlatMaxBytes;
 }
 
+// DPP source x of every lane (all masks set; the listed patterns never leave
+// the row, so the zero fill never applies)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return as_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u32(x), CTRL, 0xF, 0xF, true));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kDppXor3 = 0x1B;        // quad_perm [3, 2, 1, 0]
+constexpr int kDppMirror = 0x140;     // lane i of a row of 16 reads lane 15 - i (i ^ 15)
+constexpr int kDppHalfMirror = 0x141; // lane i of a half row reads lane 7 - i (i ^ 7)
+
+// The value lane l ^ s holds (s = 1, 2, 4, 8, 16, 32), with no LDS permute:
+// DPP quad permutations and row mirrors below 16 (i ^ 4 = (i ^ 3) ^ 7 and
+// i ^ 8 = (i ^ 7) ^ 15), a VALU lane swap of rows or halves above.
+template <int S>
+__device__ __forceinline__ float lane_xor(float x, int lane) {
+  if constexpr (S == 1) return dpp_f32<kDppXor1>(x);
+  if constexpr (S == 2) return dpp_f32<kDppXor2>(x);
+  if constexpr (S == 4) return dpp_f32<kDppHalfMirror>(dpp_f32<kDppXor3>(x));
+  if constexpr (S == 8) return dpp_f32<kDppMirror>(dpp_f32<kDppHalfMirror>(x));
+  if constexpr (S == 16 || S == 32) {
+    // the swap leaves (own, partner) in the lower lanes and (partner, own)
+    // in the upper ones
+    const auto a = S == 16 ? __builtin_amdgcn_permlane16_swap(as_u32(x), as_u32(x), false, false)
+                           : __builtin_amdgcn_permlane32_swap(as_u32(x), as_u32(x), false, false);
+    return as_f32((lane & S) ? a[0] : a[1]);
+  }
+  return __shfl_xor(x, S, 64);
+}
+
+// max over the 16 lanes of a row (DPP only)
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_f32<kDppXor1>(x));
+  x = fmaxf(x, dpp_f32<kDppXor2>(x));
+  x = fmaxf(x, dpp_f32<0x124>(x));  // row_ror:4
+  return fmaxf(x, dpp_f32<0x128>(x));  // row_ror:8
+}
+
 // Walsh-Hadamard transform of one row of D = 64 C channels held by a wave,
 // lane l holding channels C l .. C l + C - 1: stages h < C inside the lane,
 // stage h >= C between lanes l and l ^ (h / C); fp32 a + b and a - b in the
@@ -185,24 +226,21 @@ __device__ __forceinline__ void wave_fwht(float (&x)[C], int lane, float c) {
       }
     }
   }
-  // (y - x is y + (-x) and x + y is y + x, exactly; lanes 1 and 2 apart
-  // exchange by DPP quad permutations, the rest through the LDS permute
-  // network)
-#pragma unroll
-  for (int hs = 1; hs < 64; hs <<= 1) {
+  // (y - x is y + (-x) and x + y is y + x, exactly)
+  auto stage = [&](auto s_tag) {
+    constexpr int S = decltype(s_tag)::value;
 #pragma unroll
     for (int i = 0; i < C; ++i) {
-      const float sx = (lane & hs) ? -x[i] : x[i];
-      float y;
-      if (hs == 1)
-        y = as_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u32(x[i]), 0xB1, 0xF, 0xF, true));
-      else if (hs == 2)
-        y = as_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u32(x[i]), 0x4E, 0xF, 0xF, true));
-      else
-        y = __shfl_xor(x[i], hs, 64);
-      x[i] = y + sx;
+      const float sx = (lane & S) ? -x[i] : x[i];
+      x[i] = lane_xor<S>(x[i], lane) + sx;
     }
-  }
+  };
+  stage(std::integral_constant<int, 1>{});
+  stage(std::integral_constant<int, 2>{});
+  stage(std::integral_constant<int, 4>{});
+  stage(std::integral_constant<int, 8>{});
+  stage(std::integral_constant<int, 16>{});
+  stage(std::integral_constant<int, 32>{});
 #pragma unroll
   for (int i = 0; i < C; ++i) x[i] = x[i] * c;
 }

@@ -200,6 +200,25 @@ __device__ __forceinline__ float lane_xor(float x, int lane) {
   return __shfl_xor(x, S, 64);
 }
 
+// max and sum over the 64 lanes, by the butterfly of lane_xor (the sum adds
+// in the order of the l ^ 1, l ^ 2, ... l ^ 32 butterfly)
+__device__ __forceinline__ float wave_max(float x, int lane) {
+  x = fmaxf(x, lane_xor<1>(x, lane));
+  x = fmaxf(x, lane_xor<2>(x, lane));
+  x = fmaxf(x, lane_xor<4>(x, lane));
+  x = fmaxf(x, lane_xor<8>(x, lane));
+  x = fmaxf(x, lane_xor<16>(x, lane));
+  return fmaxf(x, lane_xor<32>(x, lane));
+}
+__device__ __forceinline__ float wave_sum(float x, int lane) {
+  x += lane_xor<1>(x, lane);
+  x += lane_xor<2>(x, lane);
+  x += lane_xor<4>(x, lane);
+  x += lane_xor<8>(x, lane);
+  x += lane_xor<16>(x, lane);
+  return x + lane_xor<32>(x, lane);
+}
+
 // max over the 16 lanes of a row (DPP only)
 __device__ __forceinline__ float row16_max(float x) {
   x = fmaxf(x, dpp_f32<kDppXor1>(x));
@@ -334,12 +353,10 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeParams p) {
   const float* po = p.ws_o + row0 * D + C * lane;
   merge_splits<C>(acc, S, [&](int sp) { return po + (size_t)sp * ROWS * D; }, [&] {
     float M = ms;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    M = wave_max(M, lane);
     const float ws = (M != -INFINITY) ? __builtin_amdgcn_exp2f(ms - M) : 0.0f;
     lsum = ws * ls;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) lsum += __shfl_xor(lsum, o, 64);
+    lsum = wave_sum(lsum, lane);
     return ws;
   });
   const float inv = (lsum > 0.0f) ? 1.0f / lsum : 0.0f;

@@ -77,12 +77,10 @@ __global__ __launch_bounds__(256) void shared_merge_kernel(const MergeParams m) 
       [&](int sp) { return sp < S1 ? p1 + (size_t)sp * m.rows_seq * kDS : p2 + (size_t)(sp - S1) * m.rows2 * kDS; },
       [&] {
         float M = ms;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+        M = wave_max(M, lane);
         const float ws = (M != -INFINITY) ? __builtin_amdgcn_exp2f(ms - M) : 0.0f;
         lsum = ws * ls;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) lsum += __shfl_xor(lsum, o, 64);
+        lsum = wave_sum(lsum, lane);
         return ws;
       });
   const float inv = (lsum > 0.0f) ? 1.0f / lsum : 0.0f;

@@ -14,8 +14,9 @@
 //  * scores S^T = K q^T with the FP4 K codes and scale bytes as A and four
 //    FP6 query terms accumulated in the same 16 x 16 tile (16 full rows);
 //  * online softmax per row, P split into bf16 hi + lo;
-//  * PV against hi and lo in two accumulator sets (the wave's 16 rows in the
-//    MFMA rows of each), so each V operand read serves 32 rows x 32 tokens.
+//  * PV against hi and then lo into one accumulator set (the wave's 16 rows
+//    the MFMA rows of both), so each V operand read serves two MFMAs and the
+//    accumulators take 32 VGPRs: at 112 VGPRs two wide blocks fit a CU.
 // One barrier per tile pair; LDS is double-buffered by pair parity.
 #include <atomic>
 
@@ -316,12 +317,9 @@ __global__ __launch_bounds__(64 * WAVES) void extend_kernel(const DecodeParams p
   for (int o = 1; o < 16; o <<= 1) wave_lim = max(wave_lim, __shfl_xor(wave_lim, o, 64));
   wave_lim = __builtin_amdgcn_readfirstlane(wave_lim);
   float m_run = -INFINITY, l_run = 0.0f;
-  f32x4_t O1[8], O2[8];  // the wave's 16 rows: PV of the hi part of P, of the lo part
+  f32x4_t O[8];  // the wave's 16 rows: PV of the hi part of P, then of the lo part
 #pragma unroll
-  for (int n = 0; n < 8; ++n) {
-    O1[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    O2[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int n = 0; n < 8; ++n) O[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   if (stager) {
 #pragma unroll
@@ -416,7 +414,7 @@ __global__ __launch_bounds__(64 * WAVES) void extend_kernel(const DecodeParams p
       m_run = m_new;
       float psum = 0.0f;
       // P of this lane's row as bf16 hi (A1) and lo (A2): the wave's 16 rows
-      // are the MFMA rows of both, so O1 collects hi and O2 lo
+      // are the MFMA rows of both, accumulated into the same O
       uint32_t a1[4], a2[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -428,8 +426,8 @@ __global__ __launch_bounds__(64 * WAVES) void extend_kernel(const DecodeParams p
         a2[e] = pack_bf16x2(p0 - as_f32(u0 & 0xFFFF0000u), p1 - as_f32(u1 & 0xFFFF0000u));
       }
       if (__builtin_expect(__builtin_amdgcn_ballot_w64(grow) != 0, 0)) {
-        // a row max moved: rescale.  Lane (quad, c) of O1 and O2 holds rows
-        // 4 quad + i; lane c holds the factor of row c (in every quad)
+        // a row max moved: rescale.  Lane (quad, c) of O holds rows 4 quad + i;
+        // lane c holds the factor of row c (in every quad)
         const float alpha = __builtin_amdgcn_exp2f(m_old - m_use);
         l_run *= alpha;
 #pragma unroll
@@ -437,8 +435,7 @@ __global__ __launch_bounds__(64 * WAVES) void extend_kernel(const DecodeParams p
           const float al = __shfl(alpha, 4 * quad + i, 64);
 #pragma unroll
           for (int n = 0; n < 8; ++n) {
-            O1[n][i] *= al;
-            O2[n][i] *= al;
+            O[n][i] *= al;
           }
         }
       }
@@ -461,8 +458,8 @@ __global__ __launch_bounds__(64 * WAVES) void extend_kernel(const DecodeParams p
 #pragma unroll
       for (int n = 0; n < 8; ++n) {
         const bf16x8_t C0 = (n + 1 < 8) ? read_b(n + 1) : B0;
-        O1[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B0, O1[n], 0, 0, 0);
-        O2[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, B0, O2[n], 0, 0, 0);
+        O[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A1, B0, O[n], 0, 0, 0);
+        O[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A2, B0, O[n], 0, 0, 0);
         B0 = C0;
       }
     }
@@ -484,7 +481,7 @@ __global__ __launch_bounds__(64 * WAVES) void extend_kernel(const DecodeParams p
     const long long d = part_row(r0 + 4 * quad + i);
     if (d >= 0) {
 #pragma unroll
-      for (int n = 0; n < 8; ++n) p.ws_o[d * kDX + 16 * n + col] = O1[n][i] + O2[n][i];
+      for (int n = 0; n < 8; ++n) p.ws_o[d * kDX + 16 * n + col] = O[n][i];
     }
   }
   if (lane < 16) {

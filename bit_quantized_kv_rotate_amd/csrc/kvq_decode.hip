@@ -64,27 +64,41 @@ struct Ring {
   static constexpr int kN = NT == 3 ? 2 : 1;
 };
 
+// bf16 terms of the query on the conversion score route.  The FP8 cache is
+// not rotated, so outlier channels of q and K put large products into the
+// scores (log2 units beyond 250 on the outlier test inputs), where two bf16
+// terms (residual 2^-18 of each channel) move softmax weights enough to
+// breach 2e-3 on outputs near 50; a third term leaves 2^-27.  The FP4
+// conversion route works on the rotated cache and keeps two.
+template <int FMT>
+struct Bf16QTerms {
+  static constexpr int kN = FMT == KVQ_FMT_FP8_E4M3 ? 3 : 2;
+};
+
+// Workspace image of the query operands: per (sequence, KV head, row tile)
+// kSlots operands of kDwords per lane (FP6 terms: 6 packed dwords + scale +
+// pad; bf16 terms: one bf16x8 = 4 dwords per k-step of 32 channels, four
+// k-steps per set of 16 MFMA columns: hi in columns 0..7 and lo in 8..15,
+// then, with three terms, a second set with the third term in columns 0..7
+// and zeros in 8..15).
+template <int FMT>
+struct QOpsLayout {
+  static constexpr int kSlots = Fmt<FMT>::kNativeQK ? kQMfma : (Bf16QTerms<FMT>::kN == 3 ? 8 : 4);
+  static constexpr int kDwords = Fmt<FMT>::kNativeQK ? 8 : 4;
+};
+
 // Query operands of the score product.
 //  Native FP4 scores: kQTerms FP6 terms for the scaled MFMA (6 packed dwords
-//  + scale).  FP8 cache, and FP4 through the conversion route: bf16 hi + lo
-//  parts for the bf16 MFMA (4 k-steps of 32 channels).
+//  + scale).  FP8 cache, and FP4 through the conversion route: bf16 terms
+//  for the bf16 MFMA.
 template <int FMT, int NT>
 struct QOps {
-  bf16x8_t b[NT][4];
+  bf16x8_t b[NT][QOpsLayout<FMT>::kSlots];
 };
 template <int NT>
 struct QOps<KVQ_FMT_FP4_E2M1, NT> {
   i32x8_t b[NT][kQMfma];
   int sc[NT][kQMfma];
-};
-
-// Workspace image of the query operands: per (sequence, KV head, row tile)
-// kSlots operands of kDwords per lane (FP6 terms: 6 packed dwords + scale +
-// pad; bf16 hi / lo: one bf16x8 = 4 dwords).
-template <int FMT>
-struct QOpsLayout {
-  static constexpr int kSlots = Fmt<FMT>::kNativeQK ? kQMfma : 4;
-  static constexpr int kDwords = Fmt<FMT>::kNativeQK ? 8 : 4;
 };
 
 template <int FMT>
@@ -226,8 +240,8 @@ __device__ __forceinline__ void compute_pair(const DecodeParams& p, const int32_
       uint32_t kb[16];
       dequant_group<FMT>(r[s].k, scale_operand(r[s].ksc), kb);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const u32x4_t a = {kb[4 * ks], kb[4 * ks + 1], kb[4 * ks + 2], kb[4 * ks + 3]};
+      for (int ks = 0; ks < QOpsLayout<FMT>::kSlots; ++ks) {
+        const u32x4_t a = {kb[4 * (ks & 3)], kb[4 * (ks & 3) + 1], kb[4 * (ks & 3) + 2], kb[4 * (ks & 3) + 3]};
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), q.b[t][ks], acc, 0, 0, 0);
       }
     }
@@ -442,17 +456,26 @@ __device__ __forceinline__ void qprep_row(const DecodeParams& p, int gr, int lan
       if (li < 8) dst[li] = (li < 6) ? d : (li == 6 ? (uint32_t)byte : 0u);
     }
   } else {
-    // bf16 hi + lo parts; the operand lane (col, quad) of k-step s holds
-    // channels 32 quad + 8 s .. + 7 of row 8t + (col & 7), hi for col < 8.
+    // bf16 terms, each the previous residual (exact in fp32) rounded; the
+    // operand lane (col, quad) of k-step s holds channels 32 quad + 8 s .. + 7
+    // of row 8t + (col & 7): hi for col < 8, lo for col >= 8, and in the
+    // second set (k-steps 4..7, three terms) the third term for col < 8 and
+    // zero for col >= 8.
     const uint32_t h0 = f32_to_bf16_rne(x0), h1 = f32_to_bf16_rne(x1);
-    const uint32_t l0 = f32_to_bf16_rne(x0 - bf16_to_f32((uint16_t)h0));
-    const uint32_t l1 = f32_to_bf16_rne(x1 - bf16_to_f32((uint16_t)h1));
+    const float r0 = x0 - bf16_to_f32((uint16_t)h0), r1 = x1 - bf16_to_f32((uint16_t)h1);
+    const uint32_t l0 = f32_to_bf16_rne(r0), l1 = f32_to_bf16_rne(r1);
     const int quad = lane >> 4;
     const int s4 = (lane & 15) >> 2;
     const int e = lane & 3;
     uint32_t* dst = base + ((size_t)(t * kS + s4) * 64 + 16 * quad + c7) * kW + e;
     dst[0] = h0 | (h1 << 16);
     dst[8 * kW] = l0 | (l1 << 16);
+    if constexpr (Bf16QTerms<FMT>::kN == 3) {
+      const uint32_t m0 = f32_to_bf16_rne(r0 - bf16_to_f32((uint16_t)l0));
+      const uint32_t m1 = f32_to_bf16_rne(r1 - bf16_to_f32((uint16_t)l1));
+      dst[4 * 64 * kW] = m0 | (m1 << 16);
+      dst[4 * 64 * kW + 8 * kW] = 0u;
+    }
   }
 }
 
@@ -805,11 +828,12 @@ int plan_decode(const CacheGeom& c, int batch, int hq, int n_q, int max_context_
   plan->row_tiles = row_tiles;
   plan->splits = splits;
   plan->tiles_per_split = per;
-  const size_t qops = (size_t)batch * c.hkv * row_tiles * 64 * sizeof(uint32_t) *
-                      ((kfmt == KVQ_FMT_FP4_E2M1) ? QOpsLayout<KVQ_FMT_FP4_E2M1>::kSlots *
-                                                        QOpsLayout<KVQ_FMT_FP4_E2M1>::kDwords
-                                                  : QOpsLayout<KVQ_FMT_FP8_E4M3>::kSlots *
-                                                        QOpsLayout<KVQ_FMT_FP8_E4M3>::kDwords);
+  const int per_lane = (kfmt == KVQ_FMT_FP4_E2M1)
+                           ? QOpsLayout<KVQ_FMT_FP4_E2M1>::kSlots * QOpsLayout<KVQ_FMT_FP4_E2M1>::kDwords
+                       : (kfmt == kFmtFP4Conv)
+                           ? QOpsLayout<kFmtFP4Conv>::kSlots * QOpsLayout<kFmtFP4Conv>::kDwords
+                           : QOpsLayout<KVQ_FMT_FP8_E4M3>::kSlots * QOpsLayout<KVQ_FMT_FP8_E4M3>::kDwords;
+  const size_t qops = (size_t)batch * c.hkv * row_tiles * 64 * sizeof(uint32_t) * per_lane;
   plan->qops_bytes = qops;
   plan->workspace =
       qops + ((splits > 1) ? (size_t)batch * c.hkv * splits * (8 * row_tiles) * (kD + 2) * sizeof(float) : 0);

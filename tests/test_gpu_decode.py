@@ -114,21 +114,26 @@ def test_decode_split_count_invariance(gpu):
     assert_close(ref[0], want[0], "one split")
 
 
-@pytest.mark.parametrize("group,n_q", [(8, 1), (8, 3)])
-def test_decode_ragged_many_splits(gpu, group, n_q):
+@pytest.mark.parametrize("fmt,group,n_q", [("fp4", 8, 1), ("fp4", 8, 3), ("fp4", 16, 1), ("fp8", 8, 1),
+                                         ("fp8", 16, 1), ("fp8", 8, 3)])
+def test_decode_ragged_many_splits(gpu, fmt, group, n_q):
     """Ragged contexts (52 .. 7425 tokens) under forced split counts up to 64:
     the short sequences' splits past the first few are empty (weight zero),
     the longest has 59 live splits, so the merge takes its later splits in
-    rounds of eight nonzero-weight ones, the last round partly filled.  8 rows
-    run the one-wave kernel, 24 the many-row kernel."""
+    rounds of eight nonzero-weight ones, the last round partly filled.  8 and
+    16 rows run the one-wave kernel, 24 rows the many-row kernel (FP4) or
+    three 8-row tiles of the one-wave kernel (FP8).  The FP8 cases carry
+    outlier channels unrotated into the scores (log2-unit scores near 300),
+    which two bf16 query terms did not resolve to 2e-3 (16 rows, sequence 4:
+    2.2e-3); the FP8 query has three."""
     wl = syn.Workload("ragged_splits", batch=6, num_kv_heads=1, num_q_heads=group,
                       head_dim=128, page_size=16, context=0, n_q=n_q, ctx_range=(40, 9000), seed=1)
-    f = Filled(wl, "fp4")
+    f = Filled(wl, fmt)
     assert list(f.plan.context_lens) == [362, 52, 1020, 7425, 1578, 1489]
     q = syn.queries(wl).cuda()
     want = oracle_decode_batch(f, syn.bf16_bits(q))
     ref = None
-    for s in (1, 12, 40, 64):
+    for s in (1, 4, 5, 7, 8, 12, 40, 64):
         got = f.decode(q, flags=kvq.splits_flag(s)).cpu().numpy()
         for b in range(wl.batch):
             assert_close(got[b], want[b], "ragged %d rows, %d splits, seq %d" % (group * n_q, s, b))
@@ -291,7 +296,7 @@ def test_decode_ragged_splits_stale_workspace(gpu, kind):
     f = Filled(wl, "fp4")
     q = syn.queries(wl).cuda()
     want = oracle_decode_batch(f, syn.bf16_bits(q.cpu()))
-    for s in (12, 40, 64) if kind != "shared" else (8, 32):
+    for s in (4, 8, 12, 40, 64) if kind != "shared" else (8, 32):
         flags = kvq.splits_flag(s)
         if kind == "shared":
             groups = f.prefix_groups()

@@ -74,6 +74,9 @@ def parse():
                     help="sample the shader clock (one side-stream wave) during the warmup and "
                          "timed steps, and record clocks and socket power over 2.5 s of "
                          "sustained FP4 steps and FP8 calls (needs bench_clock.so)")
+    ap.add_argument("--settle-ms", type=float, default=150.0,
+                    help="wall time of back-to-back calls before each section's timed calls "
+                         "(the record's step keeps --warmup)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain fp32 elementwise kernel over 2 x 512 MiB "
                          "(reference for the HBM byte counters)")
@@ -187,6 +190,29 @@ def abba(stream, fa, fb, n):
         tb.append((b1 + b2) / 2)
         ratios.append(tb[-1] / ta[-1])
     return statistics.median(ta), statistics.median(tb), statistics.median(ratios)
+
+
+SETTLE_S = 0.15
+
+
+def settle(fn, seconds=None):
+    """Back-to-back calls of fn(i) for `seconds` of wall time, before a
+    section's timed calls.  The device's power controller cuts the shader
+    clock for some tens of milliseconds after the device leaves idle (the
+    section set-up idles it), and the compute-bound section kernels then take
+    up to a fifth longer per call; the section figures are of the settled
+    device.  The record's step keeps the driver's own warmup count."""
+    import torch
+    seconds = SETTLE_S if seconds is None else seconds
+    t0 = time.perf_counter()
+    i = 0
+    while True:
+        for _ in range(8):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return i
 
 
 class ClockSampler:
@@ -318,6 +344,8 @@ def sustained(fn, stream, seconds, sampler=None):
 
 def main():
     args = parse()
+    global SETTLE_S
+    SETTLE_S = args.settle_ms / 1e3
     want = set(s.strip() for s in args.sections.split(",")) if args.sections != "all" else None
     on = lambda s: want is None or s in want
     if args.gpus != 1:
@@ -556,6 +584,7 @@ def main():
         "fp8_comparator": fp8,
         "context_8k": small,
         "append_bulk": append_bulk,
+        "section_settle_ms": args.settle_ms,
         "agentic_mix": mix,
         "fork_prefix": fork,
         "extend_chunk": ext,
@@ -631,7 +660,7 @@ def bench_small(kvq, syn, dev, stream, steps, name="b8_l8k", min_bytes=512e6):
     for i in range(2 * max(r4, r8)):
         d4(i)
         d8(i)
-    torch.cuda.synchronize()
+    settle(lambda i: (d4(i), d8(i)))
     t4, t8, ratio = abba(stream, d4, d8, steps)
     tok = int(plan.context_lens.astype(np.int64).sum()) * H
     kv4, kv8 = tok * (D // 2 + D // 32) * 2, tok * (D + D // 32) * 2
@@ -672,9 +701,8 @@ def bench_mix(kvq, syn, dev, stream, steps, R, name="mtp_mixed_b32", fp8=False):
     B, HQ, NQ, D = wl.batch, wl.num_q_heads, wl.n_q, wl.head_dim
     out = torch.empty((B, NQ, HQ, D), dtype=torch.float32, device=dev)
     ws = torch.empty(kvq.decode_workspace_bytes(c, B, HQ, NQ, maxL, QK_FLAGS), dtype=torch.uint8, device=dev)
-    for i in range(5):
-        kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream, flags=QK_FLAGS)
-    torch.cuda.synchronize()
+    settle(lambda i: kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream,
+                                         flags=QK_FLAGS))
     es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for i, (a, b) in enumerate(es):
         a.record(stream)
@@ -692,10 +720,8 @@ def bench_mix(kvq, syn, dev, stream, steps, R, name="mtp_mixed_b32", fp8=False):
         plan.prefix_pages, shared, [int(x) for x in plan.context_lens], device=dev)
     ws2 = torch.empty(kvq.decode_shared_workspace_bytes(c, B, HQ, NQ, groups), dtype=torch.uint8, device=dev)
     out2 = torch.empty_like(out)
-    for i in range(5):
-        kvq.decode_attn_fp4_shared(cs[i % R], q, bt, cl, groups, out=out2, workspace=ws2, stream=stream,
-                                   max_context_len=maxL)
-    torch.cuda.synchronize()
+    settle(lambda i: kvq.decode_attn_fp4_shared(cs[i % R], q, bt, cl, groups, out=out2, workspace=ws2,
+                                                stream=stream, max_context_len=maxL))
     for i, (a, b) in enumerate(es):
         a.record(stream)
         kvq.decode_attn_fp4_shared(cs[i % R], q, bt, cl, groups, out=out2, workspace=ws2, stream=stream,
@@ -719,9 +745,7 @@ def bench_mix(kvq, syn, dev, stream, steps, R, name="mtp_mixed_b32", fp8=False):
         def d8(i):
             kvq.decode_attn_fp8(c8s[i % R], q, bt, cl, maxL, out=out8, workspace=ws8, stream=stream)
 
-        for i in range(5):
-            d8(i)
-        torch.cuda.synchronize()
+        settle(lambda i: (d4(i), d8(i)))
         t4a, t8a, ratio = abba(stream, d4, d8, steps)
         logical8 = int(plan.context_lens.astype(np.int64).sum()) * (D + D // 32) * 2 * wl.num_kv_heads
         fp8_res = {
@@ -783,9 +807,8 @@ def bench_extend(kvq, syn, dev, stream, steps, R, chunk=1024):
     B, HQ, NQ, D = wl.batch, wl.num_q_heads, wl.n_q, wl.head_dim
     out = torch.empty((B, NQ, HQ, D), dtype=torch.float32, device=dev)
     ws = torch.empty(kvq.decode_workspace_bytes(c, B, HQ, NQ, maxL, QK_FLAGS), dtype=torch.uint8, device=dev)
-    for i in range(3):
-        kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream, flags=QK_FLAGS)
-    torch.cuda.synchronize()
+    settle(lambda i: kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream,
+                                         flags=QK_FLAGS))
     es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for i, (a, b) in enumerate(es):
         a.record(stream)
@@ -829,9 +852,8 @@ def bench_latent(kvq, syn, dev, stream, steps, R, name="mla_b16_l128k"):
     B, HQ, NQ, D = wl.batch, wl.num_q_heads, wl.n_q, wl.head_dim
     out = torch.empty((B, NQ, HQ, D), dtype=torch.float32, device=dev)
     ws = torch.empty(kvq.decode_workspace_bytes(c, B, HQ, NQ, maxL, QK_FLAGS), dtype=torch.uint8, device=dev)
-    for i in range(10):
-        kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream, flags=QK_FLAGS)
-    torch.cuda.synchronize()
+    settle(lambda i: kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream,
+                                         flags=QK_FLAGS))
     es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     for i, (a, b) in enumerate(es):
         a.record(stream)
@@ -856,9 +878,8 @@ def bench_latent(kvq, syn, dev, stream, steps, R, name="mla_b16_l128k"):
     sel_lens = torch_from(np.array([len(x) for x in sels], dtype=np.int32), dev)
     ws_s = torch.empty(kvq.decode_selected_workspace_bytes(c, B, HQ, max_sel), dtype=torch.uint8, device=dev)
     out_s = torch.empty((B, 1, HQ, D), dtype=torch.float32, device=dev)
-    for i in range(10):
-        kvq.decode_attn_fp4_selected(cs[i % R], q, bt, sel_d, sel_lens, out=out_s, workspace=ws_s, stream=stream)
-    torch.cuda.synchronize()
+    settle(lambda i: kvq.decode_attn_fp4_selected(cs[i % R], q, bt, sel_d, sel_lens, out=out_s, workspace=ws_s,
+                                                  stream=stream))
     for i, (a, b) in enumerate(es):
         a.record(stream)
         kvq.decode_attn_fp4_selected(cs[i % R], q, bt, sel_d, sel_lens, out=out_s, workspace=ws_s, stream=stream)

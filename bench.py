@@ -14,7 +14,8 @@ in ABBA order against FP4.
 Prints ONE JSON line.  `value` is KV-cache bytes streamed per second by the
 whole step (GB/s, inputs resident in HBM); `roofline` is that step call
 (query prologue with the append, page-scan and split-merge kernels):
-algorithmic bytes per call over its mean HIP-event duration, against the
+algorithmic bytes per call over its mean duration by one HIP event pair
+around the timed steps on the step's stream, against the
 8 TB/s HBM peak, with the HBM traffic the committed counter summary records
 for these kernel sources; `cpu_baseline` times the CPU oracle on a bounded
 sample.  Further sections time the bulk append of the whole cache, the
@@ -165,20 +166,28 @@ def replicate(kvq, c, n):
     return reps
 
 
+def timed_calls(fn, n, stream):
+    """ms per call of n back-to-back calls fn(0) .. fn(n - 1): one HIP event
+    pair on `stream` around all of them (an event record between calls costs
+    the stream several microseconds of its own)."""
+    import torch
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(n):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
 def abba(stream, fa, fb, n):
     """Paired timing in ABBA order (a, b, b, a), three repeats: returns the
-    median of the paired means of a and b (ms per call, each the median of
-    n HIP-event timed calls) and the median of the paired ratios b / a."""
-    import torch
+    median of the paired means of a and b (ms per call, each the mean of n
+    back-to-back calls under one HIP event pair) and the median of the
+    paired ratios b / a."""
 
     def timed(fn):
-        es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-        for i, (x, y) in enumerate(es):
-            x.record(stream)
-            fn(i)
-            y.record(stream)
-        torch.cuda.synchronize()
-        return statistics.median([x.elapsed_time(y) for x, y in es])
+        return timed_calls(fn, n, stream)
 
     ta, tb, ratios = [], [], []
     for _ in range(3):
@@ -413,18 +422,22 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    # One HIP event pair on the step's stream brackets the K steps: an event
+    # record between consecutive steps costs the stream ~7 us per step on
+    # MI355X (back-to-back b32_l32k steps: 188-190 us of wall time per step
+    # with a pair around each step, 180-182 us without), so per-step events
+    # would time themselves as well as the step.
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
+    ev[0].record(stream)
     for i in range(args.steps):
-        e = ev[i]
-        e[0].record(stream)
         step(i)
-        e[1].record(stream)
+    ev[1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    step_ms = [e[0].elapsed_time(e[1]) for e in ev]
     ms_per_step = wall * 1e3 / args.steps
+    mean_step = ev[0].elapsed_time(ev[1]) / args.steps
 
     # ---------------- bytes
     Ls = plan.context_lens.astype(np.int64)
@@ -441,7 +454,6 @@ def main():
     step_app = n_new * H * n_t * (2 * D + D // 2 + D // 32) + n_new * 4
     dec_alg = kv_fp4 + q_bytes + bt_bytes + out_bytes + step_app
     value = kv_fp4 / (ms_per_step * 1e-3) / 1e9
-    mean_step = statistics.fmean(step_ms)
     achieved = dec_alg / (mean_step * 1e-3) / 1e9
 
     # ---------------- FP4 vs FP8, ABBA (median of three paired-mean ratios)
@@ -572,7 +584,6 @@ def main():
         },
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "kv_bytes_per_step": kv_fp4,
-        "step_ms_events_median": round(statistics.median(step_ms), 4),
         "step_ms_events_mean": round(mean_step, 4),
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -703,13 +714,8 @@ def bench_mix(kvq, syn, dev, stream, steps, R, name="mtp_mixed_b32", fp8=False):
     ws = torch.empty(kvq.decode_workspace_bytes(c, B, HQ, NQ, maxL, QK_FLAGS), dtype=torch.uint8, device=dev)
     settle(lambda i: kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream,
                                          flags=QK_FLAGS))
-    es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i, (a, b) in enumerate(es):
-        a.record(stream)
-        kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream, flags=QK_FLAGS)
-        b.record(stream)
-    torch.cuda.synchronize()
-    t = statistics.fmean([a.elapsed_time(b) for a, b in es])
+    t = timed_calls(lambda i: kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream,
+                                                  flags=QK_FLAGS), steps, stream)
 
     # the same call through the shared-prefix entry point: each prefix's pages
     # read once for all the sequences that share it
@@ -722,13 +728,8 @@ def bench_mix(kvq, syn, dev, stream, steps, R, name="mtp_mixed_b32", fp8=False):
     out2 = torch.empty_like(out)
     settle(lambda i: kvq.decode_attn_fp4_shared(cs[i % R], q, bt, cl, groups, out=out2, workspace=ws2,
                                                 stream=stream, max_context_len=maxL))
-    for i, (a, b) in enumerate(es):
-        a.record(stream)
-        kvq.decode_attn_fp4_shared(cs[i % R], q, bt, cl, groups, out=out2, workspace=ws2, stream=stream,
-                                   max_context_len=maxL)
-        b.record(stream)
-    torch.cuda.synchronize()
-    t2 = statistics.fmean([a.elapsed_time(b) for a, b in es])
+    t2 = timed_calls(lambda i: kvq.decode_attn_fp4_shared(cs[i % R], q, bt, cl, groups, out=out2, workspace=ws2,
+                                                          stream=stream, max_context_len=maxL), steps, stream)
     max_diff = float((out2 - out).abs().max())
 
     # the same plain decode over an FP8 cache of the same inputs, ABBA
@@ -809,13 +810,8 @@ def bench_extend(kvq, syn, dev, stream, steps, R, chunk=1024):
     ws = torch.empty(kvq.decode_workspace_bytes(c, B, HQ, NQ, maxL, QK_FLAGS), dtype=torch.uint8, device=dev)
     settle(lambda i: kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream,
                                          flags=QK_FLAGS))
-    es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i, (a, b) in enumerate(es):
-        a.record(stream)
-        kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream, flags=QK_FLAGS)
-        b.record(stream)
-    torch.cuda.synchronize()
-    t = statistics.fmean([a.elapsed_time(b) for a, b in es])
+    t = timed_calls(lambda i: kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream,
+                                                  flags=QK_FLAGS), steps, stream)
     L = wl.context
     visible = NQ * (L - NQ) + NQ * (NQ + 1) // 2          # (position, token) pairs per query head
     row_tokens = float(visible) * HQ * B
@@ -854,13 +850,8 @@ def bench_latent(kvq, syn, dev, stream, steps, R, name="mla_b16_l128k"):
     ws = torch.empty(kvq.decode_workspace_bytes(c, B, HQ, NQ, maxL, QK_FLAGS), dtype=torch.uint8, device=dev)
     settle(lambda i: kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream,
                                          flags=QK_FLAGS))
-    es = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    for i, (a, b) in enumerate(es):
-        a.record(stream)
-        kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream, flags=QK_FLAGS)
-        b.record(stream)
-    torch.cuda.synchronize()
-    t = statistics.fmean([a.elapsed_time(b) for a, b in es])
+    t = timed_calls(lambda i: kvq.decode_attn_fp4(cs[i % R], q, bt, cl, maxL, out=out, workspace=ws, stream=stream,
+                                                  flags=QK_FLAGS), steps, stream)
     tokens = int(plan.context_lens.astype(np.int64).sum()) * wl.num_kv_heads
     rows = wl.group * NQ
     alg_flops = 4.0 * D * rows * tokens                 # QK^T + PV, single term
@@ -880,12 +871,8 @@ def bench_latent(kvq, syn, dev, stream, steps, R, name="mla_b16_l128k"):
     out_s = torch.empty((B, 1, HQ, D), dtype=torch.float32, device=dev)
     settle(lambda i: kvq.decode_attn_fp4_selected(cs[i % R], q, bt, sel_d, sel_lens, out=out_s, workspace=ws_s,
                                                   stream=stream))
-    for i, (a, b) in enumerate(es):
-        a.record(stream)
-        kvq.decode_attn_fp4_selected(cs[i % R], q, bt, sel_d, sel_lens, out=out_s, workspace=ws_s, stream=stream)
-        b.record(stream)
-    torch.cuda.synchronize()
-    t_sel = statistics.fmean([a.elapsed_time(b) for a, b in es])
+    t_sel = timed_calls(lambda i: kvq.decode_attn_fp4_selected(cs[i % R], q, bt, sel_d, sel_lens, out=out_s,
+                                                               workspace=ws_s, stream=stream), steps, stream)
     n_sel = int(sum(len(x) for x in sels)) * wl.num_kv_heads
     del cs, c
     return {

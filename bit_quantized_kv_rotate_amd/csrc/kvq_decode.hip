@@ -692,6 +692,18 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
 constexpr int kMinTilesPerSplit = 8;     // 128 tokens
 constexpr int kMaxTilesPerSplit = 256;   // 4096 tokens
 constexpr int kMaxWavesPerCU = 8;        // two page-scan waves per SIMD
+// The FP8 comparator moves twice the bytes per tile and is fastest with
+// fewer concurrent page streams: six waves per CU measured best both at
+// 32K (b32_l32k: 6 splits 0.3838 ms, 7 0.3900, 8 0.4032) and at 8K (b8_l8k:
+// 24 splits 0.0383 ms, 32 0.0411), where FP4 is best at eight (b32_l32k 8
+// splits 0.1787 ms against 0.1883 at 6; b8_l8k 32 splits 0.0255 against
+// 0.0259 at 24).
+constexpr int kMaxWavesPerCUFP8 = 6;
+// ... and so with longer splits, up to 16 rows (the shapes measured): at
+// most 384 tiles each (6K tokens), which lets b32_l32k run its 6 splits.
+// At 24 rows the kernel holds one wave per SIMD, the wave cap does not bind,
+// and the FP8 plan keeps the 256-tile cap.
+constexpr int kMaxTilesPerSplitFP8 = 384;
 constexpr int kDefaultWaveSlots = 2048;  // MI355X: 256 CUs x kMaxWavesPerCU
 constexpr int kMaxDevices = 64;
 
@@ -752,7 +764,8 @@ int resident_waves_nt(int dev) {
   // blocks lose HBM bandwidth to row conflicts as concurrent streams grow
   // (three waves per SIMD were a third slower than two on b32_l32k, with
   // the same bytes in flight per wave)
-  const int v = cus * (blocks < kMaxWavesPerCU ? blocks : kMaxWavesPerCU);
+  const int cap = FMT == KVQ_FMT_FP8_E4M3 ? kMaxWavesPerCUFP8 : kMaxWavesPerCU;
+  const int v = cus * (blocks < cap ? blocks : cap);
   if (dev < kMaxDevices) cache[dev].store(v, std::memory_order_relaxed);
   return v;
 }
@@ -813,12 +826,14 @@ int plan_decode(const CacheGeom& c, int batch, int hq, int n_q, int max_context_
     // is known here, and long splits of the longest sequences would then
     // set the time of the whole call.
     int slots = resident_waves(kfmt, row_tiles);
-    if (slots <= 0) slots = kDefaultWaveSlots;
+    if (slots <= 0) slots = kfmt == KVQ_FMT_FP8_E4M3 ? kDefaultWaveSlots / kMaxWavesPerCU * kMaxWavesPerCUFP8
+                                                      : kDefaultWaveSlots;
     const long long units = (long long)batch * c.hkv;
     long long want = units >= slots ? 1 : slots / units;
     const long long by_len = n_tiles / kMinTilesPerSplit;
     if (want > by_len) want = by_len;
-    const long long by_cap = (n_tiles + kMaxTilesPerSplit - 1) / kMaxTilesPerSplit;
+    const int max_per = (kfmt == KVQ_FMT_FP8_E4M3 && row_tiles <= 2) ? kMaxTilesPerSplitFP8 : kMaxTilesPerSplit;
+    const long long by_cap = (n_tiles + max_per - 1) / max_per;
     if (want < by_cap) want = by_cap;
     splits = (int)(want < 1 ? 1 : want);
   }

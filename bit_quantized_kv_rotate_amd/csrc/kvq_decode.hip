@@ -521,7 +521,7 @@ __global__ __launch_bounds__(64) void decode_kernel(const DecodeParams p) {
   // u / 32, so that units 32 apart (at 8 splits, the waves an XCD's 32
   // compute units receive in turn) read different heads' slices of the
   // pages: b32_l32k decode 0.1787-0.1791 against 0.1797-0.1803 ms unrotated
-  // (three ABBA pairs, one box).
+  // (three ABBA pairs on one device).
   const int u = blockIdx.x / p.splits;
   const int b = u / p.hkv;
   const int kvh = (u % p.hkv + u / 32) % p.hkv;

@@ -159,6 +159,22 @@ def test_decode_workspace_checks():
     assert L.kvq_decode_workspace_bytes(ctypes.byref(d), 32, 64, 1, -1, 0) == 0
 
 
+def test_decode_workspace_fp8_three_query_terms_and_plan():
+    """The FP8 comparator's query operands are three bf16 terms in two sets of
+    four k-step operands (8 operands of 4 dwords per lane and 8-row tile), and
+    without a device its plan takes the fallback of six page-scan waves per
+    compute unit (b32_l32k: 6 splits, as forced), where FP4 takes eight."""
+    L = kvq.library()
+    d8 = _desc(fmt=2, rotate=0)
+    one = L.kvq_decode_workspace_bytes(ctypes.byref(d8), 32, 64, 1, 32768, kvq.splits_flag(1))
+    assert one == 32 * d8.num_kv_heads * 1 * 64 * 4 * 8 * 4
+    need8 = L.kvq_decode_workspace_bytes(ctypes.byref(d8), 32, 64, 1, 32768, 0)
+    assert need8 == L.kvq_decode_workspace_bytes(ctypes.byref(d8), 32, 64, 1, 32768, kvq.splits_flag(6))
+    d4 = _desc()
+    need4 = L.kvq_decode_workspace_bytes(ctypes.byref(d4), 32, 64, 1, 32768, 0)
+    assert need4 == L.kvq_decode_workspace_bytes(ctypes.byref(d4), 32, 64, 1, 32768, kvq.splits_flag(8))
+
+
 def test_dequant_argument_errors():
     L = kvq.library()
     d = _desc()

@@ -274,14 +274,15 @@ constexpr float kLazyLog2 = 8.0f;
 // acc += w_s * O_s over the splits s < S (1 <= S <= 64) of one query row, in
 // split order, skipping splits of weight zero (an empty split stores no O):
 // src(s) points at this lane's C channels of split s, and weights() returns
-// ws, whose lane s holds w_s.  The loads of eight splits are issued before
-// any is used (a loop of one load and one wait per split pays a memory round
-// trip per split).  The first eight splits are loaded before weights() runs,
-// so that their loads share a round trip with the (m, l) loads it waits for;
-// of the others only those of nonzero weight are loaded.
-template <int C, typename Src, typename Weights>
+// ws, whose lane s holds w_s.  The loads of K splits are issued before any is
+// used (a loop of one load and one wait per split pays a memory round trip
+// per split).  The first K splits are loaded before weights() runs, so that
+// their loads share a round trip with the (m, l) loads it waits for; of the
+// others only those of nonzero weight are loaded, K at a time.  The sums are
+// the same for every K: the same fused multiply-adds in split order.
+template <int C, int K = 8, typename Src, typename Weights>
 __device__ __forceinline__ void merge_splits(float (&acc)[C], int S, Src src, Weights weights) {
-  constexpr int K = 8;
+  static_assert(K >= 1 && K <= 32, "splits per round");
   f32x2_t o[K][C / 2];
   int idx[K];
   // the next K splits of the wave-uniform mask todo, in ascending order;
@@ -326,8 +327,8 @@ __device__ __forceinline__ void merge_splits(float (&acc)[C], int S, Src src, We
 // (four per block, ROWS padded rows per (sequence, KV head), or p.rows_pad
 // when ROWS is 0); lane s < S
 // holds split s's (m, l), lane l accumulates channels C l .. C l + C - 1 of
-// the D = 64 C channels over the splits.
-template <int ROWS_T, int C>
+// the D = 64 C channels over the splits, loading K splits per round.
+template <int ROWS_T, int C, int K = 8>
 __global__ __launch_bounds__(256) void merge_kernel(const DecodeParams p) {
   constexpr int D = 64 * C;
   const int ROWS = ROWS_T > 0 ? ROWS_T : p.rows_pad;  // 0: padded row count at run time
@@ -351,7 +352,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const DecodeParams p) {
 #pragma unroll
   for (int i = 0; i < C; ++i) acc[i] = 0.0f;
   const float* po = p.ws_o + row0 * D + C * lane;
-  merge_splits<C>(acc, S, [&](int sp) { return po + (size_t)sp * ROWS * D; }, [&] {
+  merge_splits<C, K>(acc, S, [&](int sp) { return po + (size_t)sp * ROWS * D; }, [&] {
     float M = ms;
     M = wave_max(M, lane);
     const float ws = (M != -INFINITY) ? __builtin_amdgcn_exp2f(ms - M) : 0.0f;

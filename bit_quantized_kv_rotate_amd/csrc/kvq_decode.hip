@@ -730,12 +730,9 @@ hipError_t launch_nt(const DecodeParams& p, int batch, const AppendParams* ap, h
     hipLaunchKernelGGL((decode_kernel<FMT, NT, false>), grid, dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.splits == 1 || p.keep_partials) return e;
-  // more than eight splits (short contexts over many sequences' worth of
-  // waves): all splits' loads in one round rather than rounds of eight
-  if (p.splits > 8)
-    hipLaunchKernelGGL((merge_kernel<8 * NT, 2, 32>), dim3(qblocks), dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL((merge_kernel<8 * NT, 2>), dim3(qblocks), dim3(256), 0, stream, p);
+  // past the first eight splits, the nonzero-weight ones in rounds of 32
+  // rather than of eight (b8_l8k's 32 splits: two memory round trips, not four)
+  hipLaunchKernelGGL((merge_kernel<8 * NT, 2, 32>), dim3(qblocks), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -274,22 +274,25 @@ constexpr float kLazyLog2 = 8.0f;
 // acc += w_s * O_s over the splits s < S (1 <= S <= 64) of one query row, in
 // split order, skipping splits of weight zero (an empty split stores no O):
 // src(s) points at this lane's C channels of split s, and weights() returns
-// ws, whose lane s holds w_s.  The loads of K splits are issued before any is
+// ws, whose lane s holds w_s.  The loads of a round are issued before any is
 // used (a loop of one load and one wait per split pays a memory round trip
-// per split).  The first K splits are loaded before weights() runs, so that
-// their loads share a round trip with the (m, l) loads it waits for; of the
-// others only those of nonzero weight are loaded, K at a time.  The sums are
+// per split).  The first eight splits are loaded before weights() runs, so
+// that their loads share a round trip with the (m, l) loads it waits for; of
+// the others only those of nonzero weight are loaded, K at a time (K = 32 for
+// two channels per lane: up to 56 more splits in two rounds).  The sums are
 // the same for every K: the same fused multiply-adds in split order.
 template <int C, int K = 8, typename Src, typename Weights>
 __device__ __forceinline__ void merge_splits(float (&acc)[C], int S, Src src, Weights weights) {
-  static_assert(K >= 1 && K <= 32, "splits per round");
+  static_assert(K >= 8 && K <= 32, "splits per round");
+  constexpr int K0 = 8;  // the first round, beside the (m, l) loads
   f32x2_t o[K][C / 2];
   int idx[K];
-  // the next K splits of the wave-uniform mask todo, in ascending order;
+  // the next N splits of the wave-uniform mask todo, in ascending order;
   // past its last split, idx = -1 and split idx[0] is loaded again
-  auto load = [&](uint64_t& todo) {
+  auto load = [&](uint64_t& todo, auto n_tag) {
+    constexpr int N = decltype(n_tag)::value;
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
+    for (int k = 0; k < N; ++k) {
       idx[k] = todo ? __builtin_ctzll(todo) : -1;
       todo &= todo - 1;
       const float* ptr = src(idx[k] >= 0 ? idx[k] : idx[0]);
@@ -297,9 +300,10 @@ __device__ __forceinline__ void merge_splits(float (&acc)[C], int S, Src src, We
       for (int i = 0; i < C; i += 2) o[k][i / 2] = *reinterpret_cast<const f32x2_t*>(ptr + i);
     }
   };
-  auto add = [&](float ws) {
+  auto add = [&](float ws, auto n_tag) {
+    constexpr int N = decltype(n_tag)::value;
 #pragma unroll
-    for (int k = 0; k < K; ++k) {
+    for (int k = 0; k < N; ++k) {
       const float wl = as_f32((uint32_t)__builtin_amdgcn_readlane((int)as_u32(ws), idx[k] & 63));
       const float w = idx[k] >= 0 ? wl : 0.0f;
 #pragma unroll
@@ -309,15 +313,17 @@ __device__ __forceinline__ void merge_splits(float (&acc)[C], int S, Src src, We
       }
     }
   };
-  uint64_t todo = S >= K ? (1ull << K) - 1 : (1ull << S) - 1;
-  load(todo);
+  using First = std::integral_constant<int, K0>;
+  using Later = std::integral_constant<int, K>;
+  uint64_t todo = S >= K0 ? (1ull << K0) - 1 : (1ull << S) - 1;
+  load(todo, First{});
   __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the waits in weights()
   const float ws = weights();
-  add(ws);
-  todo = __ballot(ws != 0.0f) & ~((1ull << K) - 1);
+  add(ws, First{});
+  todo = __ballot(ws != 0.0f) & ~((1ull << K0) - 1);
   while (todo) {
-    load(todo);
-    add(ws);
+    load(todo, Later{});
+    add(ws, Later{});
   }
 }
 
@@ -327,7 +333,8 @@ __device__ __forceinline__ void merge_splits(float (&acc)[C], int S, Src src, We
 // (four per block, ROWS padded rows per (sequence, KV head), or p.rows_pad
 // when ROWS is 0); lane s < S
 // holds split s's (m, l), lane l accumulates channels C l .. C l + C - 1 of
-// the D = 64 C channels over the splits, loading K splits per round.
+// the D = 64 C channels over the splits, loading up to K nonzero-weight
+// splits per round after the first eight.
 template <int ROWS_T, int C, int K = 8>
 __global__ __launch_bounds__(256) void merge_kernel(const DecodeParams p) {
   constexpr int D = 64 * C;

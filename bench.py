@@ -89,10 +89,15 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    """sha256 of the decode kernel sources without comments and blank lines
-    (a comment edit keeps the measured traffic valid; a code edit does not)."""
+    """sha256 of the decode kernel sources without comments and blank lines,
+    and of the compiler flags they are built with (a comment edit keeps the
+    measured traffic valid; a code or flag edit does not)."""
     import re
+    sys.path.insert(0, ROOT)
+    from bit_quantized_kv_rotate_amd import _build
     h = hashlib.sha256()
+    flags = [x for x in _build.COMMON if not x.startswith("-I")] + _build.SOURCES["kvq_decode.hip"]
+    h.update(repr(flags).encode() + b"\n")
     for f in KERNEL_SOURCES:
         with open(f) as fh:
             for line in fh:

@@ -171,6 +171,27 @@ def replicate(kvq, c, n):
     return reps
 
 
+def step_bytes(wl, plan, n_new):
+    """Algorithmic bytes of one step call over a workload's cache: the FP4
+    and FP8 KV bytes every decode call streams (codes plus one scale byte per
+    32 channels, K and V, every cached token of every KV head), and the
+    step's whole traffic: FP4 KV + the bf16 queries + each (sequence, KV
+    head)'s block-table entries + the fp32 outputs + the append of n_new
+    tokens (bf16 K and V rows in, FP4 codes and scales out, slot ids)."""
+    import numpy as np
+    D, H, P = wl.head_dim, wl.num_kv_heads, wl.page_size
+    B, HQ, NQ = wl.batch, wl.num_q_heads, wl.n_q
+    Ls = plan.context_lens.astype(np.int64)
+    n_t = 1 if wl.kv_shared else 2
+    kv_fp4 = int(Ls.sum()) * H * (D // 2 + D // 32) * n_t      # 136 B per token and head at d128
+    kv_fp8 = int(Ls.sum()) * H * (D + D // 32) * n_t           # 264
+    q_bytes = B * NQ * HQ * D * 2
+    bt_bytes = int(sum((l + P - 1) // P for l in Ls)) * H * 4
+    out_bytes = B * NQ * HQ * D * 4
+    app = n_new * H * n_t * (2 * D + D // 2 + D // 32) + n_new * 4
+    return kv_fp4, kv_fp8, kv_fp4 + q_bytes + bt_bytes + out_bytes + app
+
+
 def timed_calls(fn, n, stream):
     """ms per call of n back-to-back calls fn(0) .. fn(n - 1): one HIP event
     pair on `stream` around all of them (an event record between calls costs
@@ -445,19 +466,8 @@ def main():
     mean_step = ev[0].elapsed_time(ev[1]) / args.steps
 
     # ---------------- bytes
-    Ls = plan.context_lens.astype(np.int64)
-    n_t = 1 if wl.kv_shared else 2
-    per_tok_fp4 = (D // 2 + D // 32) * n_t     # 136 at d128 (K and V)
-    per_tok_fp8 = (D + D // 32) * n_t          # 264 at d128
-    kv_fp4 = int(Ls.sum()) * H * per_tok_fp4
-    kv_fp8 = int(Ls.sum()) * H * per_tok_fp8
-    q_bytes = B * NQ * HQ * D * 2
-    bt_bytes = int(sum((l + P - 1) // P for l in Ls)) * H * 4   # each (seq, KV head) reads its table
-    out_bytes = B * NQ * HQ * D * 4
-    # the step's append: bf16 K and V rows in, FP4 codes + scales out, slots
     n_new = int(step_slots.numel())
-    step_app = n_new * H * n_t * (2 * D + D // 2 + D // 32) + n_new * 4
-    dec_alg = kv_fp4 + q_bytes + bt_bytes + out_bytes + step_app
+    kv_fp4, kv_fp8, dec_alg = step_bytes(wl, plan, n_new)
     value = kv_fp4 / (ms_per_step * 1e-3) / 1e9
     achieved = dec_alg / (mean_step * 1e-3) / 1e9
 
@@ -506,6 +516,7 @@ def main():
             torch.cuda.synchronize()
             app_ms.append(a.elapsed_time(b))
         app_t = statistics.median(app_ms[2:])
+        n_t = 1 if wl.kv_shared else 2
         app_bytes = L0 * H * n_t * (2 * D + D // 2 + D // 32) + L0 * 4
         append_bulk = {
             "tokens": L0, "ms": round(app_t, 4),
